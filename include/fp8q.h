@@ -1,0 +1,194 @@
+/*
+ * fp8q.h — C ABI of libfp8q.so: per-token-group FP8 quantization of activations
+ * and the block-scaled FP8 GEMMs that consume it, for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute is defined by these sources:
+ *   [PR30924]  prhub report of sglang PR #30924, "[JIT] Trait-driven
+ *              per_token_group_quant: unify the quant kernel family (flat + masked)":
+ *              section "实现拆解" items 1-2 (the trait axes: input/output dtype, group
+ *              size, fp32 or UE8M0 scale, row- or column-major scale layout, fused
+ *              silu_and_mul, flat or masked dispatch with masked_m / expected_m) and
+ *              section "关键源码片段" (the _jit_module trait list and the UE8M0 test
+ *              reference ref_fp8_ue8m0).
+ *   [TF]       TeleFuser page "tf-kernel 安装与使用": the per-token FP8 example, where
+ *              the caller pre-allocates the e4m3 output and the fp32 scale tensor; and
+ *              the silu_and_mul example, where the last dimension splits into two halves.
+ *   [FI]       "FlashInfer GEMM 学习笔记": section 6 (block-scaled FP8 / MXFP8 with
+ *              block size 32, 2D non-swizzled scales) and section 7 (DeepGEMM's grouped
+ *              masked FP8 "NT" groupwise GEMM driven by expected_m + masked_m).
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or synchronises; it only validates arguments and enqueues kernels.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call is
+ *     asynchronous on that stream.
+ *   - Sizes and strides are signed 64-bit and counted in ELEMENTS of the tensor they
+ *     describe (bytes for e4m3/UE8M0 tensors). The innermost (K) dimension of x, q, a
+ *     and b is always contiguous.
+ *   - e4m3 tensors are passed as uint8_t bytes in the OCP E4M3FN encoding (bias 7,
+ *     no infinities, 0x7F/0xFF are NaN, largest finite 448 = 0x7E).
+ *   - UE8M0 scale bytes encode 2^(byte-127); 0xFF is never produced.
+ *   - Return value: FP8Q_OK (0) or one of the positive status codes below. On error
+ *     nothing is enqueued and no output byte is written. fp8q_last_error() returns a
+ *     thread-local description of the last failure on the calling thread.
+ *   - A call with a zero-sized problem (E, M, N or K equal to 0) returns FP8Q_OK and
+ *     enqueues nothing.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified (but in-bounds) output.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FP8Q_OK 0
+#define FP8Q_EINVAL 1       /* null pointer with non-zero size, bad shape, stride or layout */
+#define FP8Q_EUNSUPPORTED 2 /* dtype, group size, scale format or mode outside the supported set */
+#define FP8Q_EALIGN 3       /* pointer or row stride not aligned as required */
+#define FP8Q_EDEVICE 4      /* current device is not gfx950, or no device */
+#define FP8Q_ELAUNCH 5      /* the HIP runtime reported an error at launch */
+
+/* activation dtypes (input of the quant calls) */
+#define FP8Q_DTYPE_BF16 0
+#define FP8Q_DTYPE_F16 1
+#define FP8Q_DTYPE_F32 2
+
+/* scale formats */
+#define FP8Q_SCALE_F32 0   /* one IEEE float per group: s = amax / 448 */
+#define FP8Q_SCALE_UE8M0 1 /* one byte per group: s = 2^(byte-127), the smallest power of two >= amax/448 */
+
+/* GEMM scaling modes */
+#define FP8Q_GEMM_BLOCK128 0 /* a: 1x128 scales per (row, K block); b: 128x128 scales per (N block, K block) */
+#define FP8Q_GEMM_MX32 1     /* a and b: one E8M0 byte per (row, 32-wide K block), applied by scaled MFMA */
+
+/*
+ * fp8q_group_quant — per-token-group FP8 (e4m3fn) quantization  [PR30924 items 1-2, ref_fp8_ue8m0]
+ *
+ * x is viewed as [E][M][K] (flat calls use E = 1): element (e, m, k) is at
+ * x + e*x_se + m*x_sm + k, with dtype `in_dtype`. Each row is cut into K/G groups of
+ * G = group_size consecutive elements. For every group of every processed row:
+ *   amax = max(max |x_i|, 1e-10f)                                  (fp32)
+ *   FP8Q_SCALE_F32:   s = amax / 448 (IEEE fp32 division), stored as float;
+ *                     multiplier inv = 1 / s (IEEE fp32 division)
+ *   FP8Q_SCALE_UE8M0: r = amax / 448 (fp32); byte = biased_exponent(r) + (mantissa(r) != 0),
+ *                     stored as uint8; multiplier inv = 2^(127 - (byte - 127)), exact
+ *   q_i = e4m3_round_nearest_even( clamp(x_i * inv, -448, 448) )
+ * q (uint8 e4m3 bytes) element (e, m, k) is at q + e*q_se + m*q_sm + k.
+ * The scale of group g of row (e, m) is at s + e*s_se + m*s_sm + g*s_sg, counted in
+ * scale elements (4-byte floats or single bytes). The layout is read from the strides:
+ * s_sg == 1 means row-major [M][K/G], s_sm == 1 means column-major [K/G][M]; any other
+ * combination is FP8Q_EINVAL.
+ *
+ * Dispatch:
+ *   masked_m == NULL: flat — every row m < M of every e < E is processed.
+ *   masked_m != NULL: masked (the EP-MoE layout) — masked_m is a DEVICE int32[E];
+ *     expert e processes rows m < clamp(masked_m[e], 0, M) only. Rows at or beyond
+ *     that bound are never read or written (q and s keep their previous contents).
+ *     expected_m >= 0 is a host-side hint of the typical rows per expert used to size
+ *     the launch; it never changes the result (0 = no hint).
+ *
+ * Requirements (else the status in brackets):
+ *   in_dtype in {BF16, F16, F32} and group_size in {32, 64, 128}       [EUNSUPPORTED]
+ *   K % group_size == 0, E, M, K >= 0, strides non-negative             [EINVAL]
+ *   x and q 16-byte aligned; x_sm, x_se (in bytes) and q_sm, q_se
+ *   multiples of 16 bytes; F32 scales 4-byte aligned                    [EALIGN]
+ *   E <= 4096 when masked                                                [EUNSUPPORTED]
+ */
+int fp8q_group_quant(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K,
+                     int64_t x_se, int64_t x_sm,
+                     uint8_t* q, int64_t q_se, int64_t q_sm,
+                     void* s, int scale_fmt, int64_t s_se, int64_t s_sm, int64_t s_sg,
+                     int group_size, const int32_t* masked_m, int64_t expected_m,
+                     void* stream);
+
+/*
+ * fp8q_silu_mul_group_quant — fused silu_and_mul followed by group quantization
+ * [PR30924 item 1 (fuse_silu_and_mul trait), item 4 (silu_and_mul_masked_post_quant_fwd);
+ *  TF silu_and_mul example (last dimension split in two halves)]
+ *
+ * Same arguments and outputs as fp8q_group_quant, except that x is [E][M][2K]: the
+ * gate is columns [0, K) and the up projection is columns [K, 2K) of each row, and
+ * the value that is quantized is, in fp32,
+ *   y_j = ( g_j / (1 + exp(-g_j)) ) * u_j
+ * where exp is the fixed fp32 sequence below (so that every conforming implementation
+ * produces the same bits), not a vendor math library:
+ *   t = clamp(-g, -87, 88); n = rint(t * log2(e)); r = fma(-n, ln2_hi, t); r = fma(-n, ln2_lo, r);
+ *   p = Horner of sum_{k=0..7} r^k / k! with fma; exp = p * 2^n (2^n built from its bits).
+ * All constants are the fp32 values nearest to log2(e), ln 2 (hi part) and its remainder,
+ * and 1/k!. y is not rounded to a narrower type before quantization.
+ */
+int fp8q_silu_mul_group_quant(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K,
+                              int64_t x_se, int64_t x_sm,
+                              uint8_t* q, int64_t q_se, int64_t q_sm,
+                              void* s, int scale_fmt, int64_t s_se, int64_t s_sm, int64_t s_sg,
+                              int group_size, const int32_t* masked_m, int64_t expected_m,
+                              void* stream);
+
+/*
+ * fp8q_gemm_blockscaled — Y = dequant(A) * dequant(B)^T, bf16 output  [FI sections 6-7]
+ *
+ * A is [M][K] e4m3 (row m at a + m*lda), B is [N][K] e4m3 (row n at b + n*ldb): both
+ * operands are K-major ("NT"). Y is [M][N] bf16 (element (m, n) at y + m*ldy + n, passed
+ * as uint16_t bits).
+ *   mode FP8Q_GEMM_BLOCK128:
+ *     sa: one scale per (m, kb), kb = k/128, at sa + m*sa_sm + kb*sa_sk; sa_fmt F32 or UE8M0.
+ *     sb: one scale per (nb, kb), nb = n/128, at sb + nb*sb_sn + kb*sb_sk; sb_fmt F32 or UE8M0.
+ *     Y[m][n] = bf16_rne( sum_kb sa(m,kb) * sb(n/128,kb) * sum_{k in kb} dec(A[m][k]) * dec(B[n][k]) )
+ *   mode FP8Q_GEMM_MX32:
+ *     sa: one E8M0 byte per (m, k/32) at sa + m*sa_sm + (k/32)*sa_sk; sb likewise per (n, k/32).
+ *     sa_fmt and sb_fmt must be FP8Q_SCALE_UE8M0.
+ *     Y[m][n] = bf16_rne( sum_k 2^(sa-127) dec(A[m][k]) * 2^(sb-127) dec(B[n][k]) )
+ * Accumulation is fp32; the result is rounded to bf16 once, at the end.
+ *
+ * Requirements: M, N, K >= 0, K % 128 == 0 [EINVAL]; a, b 16-byte aligned with lda, ldb
+ * multiples of 16; y 4-byte aligned with ldy even [EALIGN]; lda, ldb >= K, ldy >= N [EINVAL].
+ */
+int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda,
+                          const void* sa, int sa_fmt, int64_t sa_sm, int64_t sa_sk,
+                          const uint8_t* b, int64_t ldb,
+                          const void* sb, int sb_fmt, int64_t sb_sn, int64_t sb_sk,
+                          uint16_t* y, int64_t ldy,
+                          int64_t M, int64_t N, int64_t K, int mode, void* stream);
+
+/*
+ * fp8q_grouped_gemm_masked — per-expert BLOCK128 GEMM over the masked EP-MoE layout
+ * [FI section 7: DeepGEMM grouped masked, expected_m + masked_m; PR30924 item 2]
+ *
+ * For every expert e < E: A_e = a + e*a_se ([cap][K], row stride lda),
+ * sa_e = sa + e*sa_se (indexed like fp8q_gemm_blockscaled's sa), B_e = b + e*b_se
+ * ([N][K], row stride ldb), sb_e = sb + e*sb_se, Y_e = y + e*y_se ([cap][N], row
+ * stride ldy). Rows m < clamp(masked_m[e], 0, cap) of Y_e receive the BLOCK128 product
+ * of A_e and B_e; rows at or beyond that bound are never written. masked_m is a
+ * DEVICE int32[E]; expected_m is a host-side launch hint only (result-invariant).
+ * Requirements as for fp8q_gemm_blockscaled, plus E <= 4096 [EUNSUPPORTED].
+ */
+int fp8q_grouped_gemm_masked(const uint8_t* a, int64_t a_se, int64_t lda,
+                             const void* sa, int sa_fmt, int64_t sa_se, int64_t sa_sm, int64_t sa_sk,
+                             const uint8_t* b, int64_t b_se, int64_t ldb,
+                             const void* sb, int sb_fmt, int64_t sb_se, int64_t sb_sn, int64_t sb_sk,
+                             uint16_t* y, int64_t y_se, int64_t ldy,
+                             const int32_t* masked_m, int64_t expected_m,
+                             int64_t E, int64_t cap, int64_t N, int64_t K, void* stream);
+
+/* Human-readable name of a status code. Never returns NULL. */
+const char* fp8q_status_string(int status);
+
+/* Description of the last failure on this thread ("" if none). Never returns NULL. */
+const char* fp8q_last_error(void);
+
+/*
+ * fp8q_device_check — FP8Q_OK if HIP device `device` exists and is a gfx950 (CDNA4)
+ * part, else FP8Q_EDEVICE. The compute calls perform the same check on the current
+ * device the first time they see it.
+ */
+int fp8q_device_check(int device);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,210 @@
+"""CPU oracle for per-token-group FP8 quantization and block-scaled FP8 GEMM.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchmark's
+CPU-baseline leg, never by the product path. It shares no code with the HIP library.
+
+The arithmetic lives in plain C (fp8q_oracle.c, built by build.py with IEEE semantics);
+this module only marshals numpy arrays into it. Function-level citations are in the C
+source; the arguments mirror the C ABI declared in include/fp8q.h, with host arrays in
+place of device pointers.
+
+Parity status of each function (what pins it is in tests/test_oracle_*.py):
+  e4m3_decode, e4m3_encode  pinned: all 256 codes and a 2^24-value sweep vs torch's cast,
+                            hand-derived golden codes
+  ue8m0_byte                pinned: exact rational ceil-power-of-two over every bf16 amax
+  exp_spec, silu_mul        pinned: accuracy vs math.exp (<= 2 ulp), special values
+  group_quant               pinned: golden group, dequant-error bound, layout/mask invariants
+  gemm                      pinned: exact Fraction arithmetic, torch float64 dequant-matmul,
+                            one-hot operands
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "libfp8q_oracle.so")
+
+BF16, F16, F32 = 0, 1, 2
+SCALE_F32, SCALE_UE8M0 = 0, 1
+GEMM_BLOCK128, GEMM_MX32 = 0, 1
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.ora_group_quant.restype = ctypes.c_int
+    lib.ora_group_quant.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64,
+                                    _P, ctypes.c_int, _I64, _I64, _I64, ctypes.c_int, _P, ctypes.c_int,
+                                    _P, _P, _I64]
+    lib.ora_gemm.restype = ctypes.c_int
+    lib.ora_gemm.argtypes = [_P, _I64, _P, ctypes.c_int, _I64, _I64, _P, _I64, _P, ctypes.c_int,
+                             _I64, _I64, _I64, _I64, _I64, ctypes.c_int, _P, _P, _I64, _P, _P]
+    for name in ("ora_e4m3_decode_array", "ora_e4m3_encode_array", "ora_ue8m0_byte_array",
+                 "ora_exp_spec_array"):
+        getattr(lib, name).restype = None
+        getattr(lib, name).argtypes = [_P, _P, _I64]
+    lib.ora_silu_mul_array.restype = None
+    lib.ora_silu_mul_array.argtypes = [_P, _P, _P, _I64]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------- codecs
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().ora_e4m3_decode_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """Nearest e4m3 code (ties to even) of fp32 values already within [-448, 448]."""
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().ora_e4m3_encode_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def ue8m0_byte(amax) -> np.ndarray:
+    v = np.ascontiguousarray(amax, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().ora_ue8m0_byte_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def exp_spec(t) -> np.ndarray:
+    v = np.ascontiguousarray(t, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.float32)
+    _load().ora_exp_spec_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def silu_mul(g, u) -> np.ndarray:
+    gv = np.ascontiguousarray(g, dtype=np.float32)
+    uv = np.ascontiguousarray(u, dtype=np.float32)
+    assert gv.shape == uv.shape
+    out = np.empty(gv.shape, dtype=np.float32)
+    _load().ora_silu_mul_array(_ptr(gv), _ptr(uv), _ptr(out), gv.size)
+    return out
+
+
+# --------------------------------------------------------------------------- quant
+def group_quant_raw(x: np.ndarray, in_dtype: int, E: int, M: int, K: int, x_se: int, x_sm: int,
+                    q: np.ndarray, q_se: int, q_sm: int, s: np.ndarray, scale_fmt: int,
+                    s_se: int, s_sm: int, s_sg: int, group_size: int,
+                    masked_m: np.ndarray | None = None, silu: bool = False,
+                    rows: tuple[np.ndarray, np.ndarray] | None = None) -> None:
+    """Same arguments as fp8q_group_quant (strides in elements), on host arrays.
+    `rows` = (e_indices, m_indices) restricts the work to those rows."""
+    mm = None if masked_m is None else np.ascontiguousarray(masked_m, dtype=np.int32)
+    re = rm = None
+    n_rows = 0
+    if rows is not None:
+        re = np.ascontiguousarray(rows[0], dtype=np.int64)
+        rm = np.ascontiguousarray(rows[1], dtype=np.int64)
+        n_rows = re.size
+    rc = _load().ora_group_quant(_ptr(x), in_dtype, E, M, K, x_se, x_sm, _ptr(q), q_se, q_sm,
+                                 _ptr(s), scale_fmt, s_se, s_sm, s_sg, group_size, _ptr(mm),
+                                 int(silu), _ptr(re), _ptr(rm), n_rows)
+    if rc != 0:
+        raise ValueError("oracle group_quant: unsupported arguments")
+
+
+def group_quant(x: np.ndarray, group_size: int, scale_fmt: int, layout: str = "row",
+                in_dtype: int = BF16, silu: bool = False, masked_m: np.ndarray | None = None,
+                rows: tuple[np.ndarray, np.ndarray] | None = None,
+                fill: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Quantizes x ([M, K] or [E, M, K]; with silu the last dim is 2K) into freshly
+    allocated outputs: q [.., M, K] uint8 and scales [.., M, K/G] (layout "row") or
+    [.., K/G, M] (layout "col"), float32 or uint8. Untouched entries hold `fill`."""
+    x3 = x if x.ndim == 3 else x[None]
+    E, M, W = x3.shape
+    K = W // 2 if silu else W
+    ng = K // group_size
+    x3 = np.ascontiguousarray(x3)
+    q = np.full((E, M, K), fill, dtype=np.uint8)
+    width = 4 if scale_fmt == SCALE_F32 else 1
+    if layout == "row":
+        s = np.full((E, M, ng * width), fill, dtype=np.uint8)
+        s_sm, s_sg = ng, 1
+    else:
+        s = np.full((E, ng, M * width), fill, dtype=np.uint8)
+        s_sm, s_sg = 1, M
+    if scale_fmt == SCALE_F32:
+        s = s.view(np.float32)
+    group_quant_raw(x3, in_dtype, E, M, K, M * W, W, q, M * K, K, s, scale_fmt, M * ng, s_sm, s_sg,
+                    group_size, masked_m, silu, rows)
+    if x.ndim == 2:
+        return q[0], s[0]
+    return q, s
+
+
+# --------------------------------------------------------------------------- gemm
+def gemm_raw(a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, M, N, K, mode,
+             at: tuple[np.ndarray, np.ndarray] | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Same arguments as fp8q_gemm_blockscaled (without y), on host arrays. Returns
+    (Y*, S): the fp64 dequantize-then-multiply result and the sum of |terms|, either for
+    all [M, N] elements or for the (m, n) pairs in `at`."""
+    if at is not None:
+        ms = np.ascontiguousarray(at[0], dtype=np.int64)
+        ns = np.ascontiguousarray(at[1], dtype=np.int64)
+        y = np.empty(ms.size, dtype=np.float64)
+        s = np.empty(ms.size, dtype=np.float64)
+        cnt = ms.size
+    else:
+        ms = ns = None
+        y = np.empty((M, N), dtype=np.float64)
+        s = np.empty((M, N), dtype=np.float64)
+        cnt = 0
+    rc = _load().ora_gemm(_ptr(a), lda, _ptr(sa), sa_fmt, sa_sm, sa_sk, _ptr(b), ldb, _ptr(sb),
+                          sb_fmt, sb_sn, sb_sk, M, N, K, mode, _ptr(ms), _ptr(ns), cnt,
+                          _ptr(y), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle gemm: unsupported arguments")
+    return y, s
+
+
+def gemm_block128(a: np.ndarray, sa: np.ndarray, b: np.ndarray, sb: np.ndarray, sa_fmt: int,
+                  sa_layout: str = "row", sb_fmt: int = SCALE_F32,
+                  at: tuple[np.ndarray, np.ndarray] | None = None):
+    """a [M, K] codes; sa [M, K/128] ("row") or [K/128, M] ("col"); b [N, K] codes;
+    sb [ceil(N/128), K/128]."""
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    sa = np.ascontiguousarray(sa)
+    sb = np.ascontiguousarray(sb)
+    M, K = a.shape
+    N = b.shape[0]
+    kb = K // 128
+    sa_sm, sa_sk = (kb, 1) if sa_layout == "row" else (1, M)
+    return gemm_raw(a, K, sa, sa_fmt, sa_sm, sa_sk, b, K, sb, sb_fmt, kb, 1, M, N, K,
+                    GEMM_BLOCK128, at)
+
+
+def gemm_mx32(a: np.ndarray, ea: np.ndarray, b: np.ndarray, eb: np.ndarray,
+              at: tuple[np.ndarray, np.ndarray] | None = None):
+    """a [M, K], b [N, K] codes; ea [M, K/32], eb [N, K/32] E8M0 bytes (row-major)."""
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    ea = np.ascontiguousarray(ea)
+    eb = np.ascontiguousarray(eb)
+    M, K = a.shape
+    N = b.shape[0]
+    return gemm_raw(a, K, ea, SCALE_UE8M0, K // 32, 1, b, K, eb, SCALE_UE8M0, K // 32, 1, M, N, K,
+                    GEMM_MX32, at)
