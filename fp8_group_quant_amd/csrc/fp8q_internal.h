@@ -1,0 +1,59 @@
+// fp8q_internal.h — internal declarations shared by the HIP translation units of libfp8q.
+// Not part of the public ABI (that is include/fp8q.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "fp8q.h"
+
+namespace fp8q {
+
+// ------------------------------------------------------------------ host-side status
+void set_error(const std::string& msg);  // thread-local detail for fp8q_last_error()
+int fail(int status, const std::string& msg);
+
+// Validates the current device once per device (gfx950 only).
+int check_current_device();
+
+// ------------------------------------------------------------------ quant launcher
+struct QuantParams {
+  const void* x;
+  uint8_t* q;
+  void* s;
+  const int32_t* masked_m;  // device, or nullptr (flat)
+  int64_t E, M, K;          // K = quantized width
+  int64_t x_se, x_sm;       // input strides (elements)
+  int64_t q_se, q_sm;       // output strides (bytes)
+  int64_t s_se, s_sm, s_sg; // scale strides (scale elements)
+  int64_t nseg;             // segments per row
+  int32_t chunks_per_seg;   // 512-element chunks per segment (1..8)
+  int32_t chunks_per_row;   // ceil(K / 512)
+};
+
+int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu,
+                       QuantParams p, int64_t expected_m, hipStream_t stream);
+
+// ------------------------------------------------------------------ GEMM launchers
+struct GemmParams {
+  const uint8_t* a;
+  const void* sa;
+  const uint8_t* b;
+  const void* sb;
+  uint16_t* y;
+  const int32_t* masked_m;  // grouped masked only
+  int64_t M, N, K;          // M = capacity per expert when grouped
+  int64_t E;                // experts (1 for the dense GEMM)
+  int64_t lda, ldb, ldy;
+  int64_t a_se, b_se, y_se;
+  int64_t sa_sm, sa_sk, sa_se;
+  int64_t sb_sn, sb_sk, sb_se;
+  int sa_fmt, sb_fmt;
+};
+
+int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t stream);
+int launch_gemm_mx32(const GemmParams& p, hipStream_t stream);
+
+}  // namespace fp8q

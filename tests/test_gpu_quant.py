@@ -1,0 +1,353 @@
+"""GPU parity of the group-quant calls against the CPU oracle: every FP8 byte and every
+scale byte must be identical (bit-exact), untouched rows must keep their sentinel bytes,
+and the result must not depend on expected_m. Calls go through the C ABI via the binding.
+
+Sizes: full oracle comparison at sizes that span several chunks and a ragged tail; at the
+named workloads' full sizes, a sample of rows (first, last and seeded-random rows of every
+expert) is compared, and the whole output is checked for properties that hold everywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+FILL = 0xA5
+
+
+def fq():
+    import fp8_group_quant_amd
+    return fp8_group_quant_amd
+
+
+def _to_dev(x: np.ndarray, in_dtype: int) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    if in_dtype == oracle.BF16:
+        return t.view(torch.bfloat16)
+    if in_dtype == oracle.F16:
+        return t.view(torch.float16)
+    return t
+
+
+def _gpu_quant(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, expected_m=0, stream=None):
+    """Runs the GPU quant on x ([M, W] or [E, M, W]); returns (q, scale storage) as numpy in
+    the oracle's storage layout ([.., M, ng] row-major or [.., ng, M] column-major)."""
+    f = fq()
+    x = _to_dev(x_np, in_dtype)
+    x3 = x if x.dim() == 3 else x[None]
+    E, M, W = x3.shape
+    K = W // 2 if silu else W
+    ng = K // G
+    q = torch.full((E, M, K), FILL, dtype=torch.uint8, device="cuda")
+    width = 4 if fmt == oracle.SCALE_F32 else 1
+    shape = (E, M, ng * width) if layout == "row" else (E, ng, M * width)
+    s_store = torch.full(shape, FILL, dtype=torch.uint8, device="cuda")
+    s_typed = s_store.view(torch.float32) if fmt == oracle.SCALE_F32 else s_store
+    s_view = s_typed if layout == "row" else s_typed.transpose(1, 2)
+    mm = None if masked_m is None else torch.from_numpy(np.asarray(masked_m, dtype=np.int32)).cuda()
+    fn = f.fp8q_silu_mul_group_quant if silu else f.fp8q_group_quant
+    xin, qin, sin = (x3, q, s_view) if x.dim() == 3 else (x3[0], q[0], s_view[0])
+    fn(xin, qin, sin, G, masked_m=mm, expected_m=expected_m, stream=stream)
+    torch.cuda.synchronize()
+    qn = q.cpu().numpy()
+    sn = s_typed.cpu().numpy()
+    if x.dim() == 2:
+        return qn[0], sn[0]
+    return qn, sn
+
+
+def _oracle(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, rows=None):
+    return oracle.group_quant(x_np, G, fmt, layout, in_dtype=in_dtype, silu=silu, masked_m=masked_m,
+                              rows=rows, fill=FILL)
+
+
+def _assert_same(a, b, what):
+    if not np.array_equal(a, b):
+        bad = np.argwhere(a != b)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} mismatching entries, first at {i}: gpu={a[i]!r} oracle={b[i]!r}")
+
+
+def _full_case(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, expected_m=0):
+    qg, sg = _gpu_quant(x_np, in_dtype, G, fmt, layout, silu, masked_m, expected_m)
+    qo, so = _oracle(x_np, in_dtype, G, fmt, layout, silu, masked_m)
+    _assert_same(qg, qo, "q")
+    _assert_same(sg.view(np.uint8), so.view(np.uint8), "scales")
+
+
+# ----------------------------------------------------------------------------- small / full
+def test_tiny_workload_full():
+    w = synth.TINY
+    x = synth.quant_input(w)
+    _full_case(x, oracle.BF16, w.G, oracle.SCALE_F32, "row")
+
+
+@pytest.mark.parametrize("M", [1, 16, 128])
+def test_dense_small_m_full(M):
+    w = synth.dense(M)
+    _full_case(synth.quant_input(w), oracle.BF16, w.G, oracle.SCALE_UE8M0, "col")
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("fmt", [oracle.SCALE_F32, oracle.SCALE_UE8M0])
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_group_sizes_formats_layouts(G, fmt, layout):
+    # 37 rows, 1536 columns = 3 chunks of 512; outliers make groups differ widely
+    x = synth.activations_bf16(21, 37, 1536, outlier_p=0.02)
+    _full_case(x, oracle.BF16, G, fmt, layout)
+
+
+@pytest.mark.parametrize("in_dtype", [oracle.F16, oracle.F32])
+def test_input_dtypes(in_dtype):
+    xb = synth.activations_bf16(22, 29, 1024, outlier_p=0.01)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    x = xf.astype(np.float16).view(np.uint16) if in_dtype == oracle.F16 else xf
+    for fmt in (oracle.SCALE_F32, oracle.SCALE_UE8M0):
+        _full_case(x, in_dtype, 128, fmt, "row")
+
+
+@pytest.mark.parametrize("K", [32, 96, 512, 608, 7296])
+def test_ragged_widths(K):
+    G = 32 if K % 128 else 128
+    x = synth.activations_bf16(23, 5, K)
+    _full_case(x, oracle.BF16, G, oracle.SCALE_UE8M0, "col")
+    _full_case(x, oracle.BF16, G, oracle.SCALE_F32, "row")
+
+
+def test_silu_small_full():
+    x = synth.activations_bf16(24, 300, 2 * 2048)
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_F32, "row", silu=True)
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "col", silu=True)
+
+
+def test_silu_large_magnitudes():
+    # gates far into both tails of silu, and inputs whose products land near the clamp
+    xb = synth.activations_bf16(25, 64, 2 * 512)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32).copy()
+    xf[:, :512] *= 40.0
+    x = synth.f64_to_bf16_bits(xf.astype(np.float64))
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_F32, "row", silu=True)
+    _full_case(x, oracle.BF16, 64, oracle.SCALE_UE8M0, "row", silu=True)
+
+
+def test_strided_rows():
+    # rows of x and q taken from wider buffers (row stride > K)
+    f = fq()
+    xb = synth.activations_bf16(26, 17, 1024)
+    x = torch.from_numpy(xb).cuda().view(torch.bfloat16)[:, :896]
+    q = torch.full((17, 1024), FILL, dtype=torch.uint8, device="cuda")[:, :896]
+    s = torch.full((17, 7), FILL, dtype=torch.uint8, device="cuda")
+    f.fp8q_group_quant(x, q, s, 128)
+    torch.cuda.synchronize()
+    qo, so = _oracle(np.ascontiguousarray(xb[:, :896]), oracle.BF16, 128, oracle.SCALE_UE8M0, "row")
+    _assert_same(q.cpu().numpy(), qo, "q")
+    _assert_same(s.cpu().numpy(), so, "scales")
+    full = q.as_strided((17, 1024), (1024, 1)).cpu().numpy()
+    assert np.all(full[:, 896:] == FILL)
+
+
+def test_every_bf16_value_through_unit_scale():
+    # each group starts with 448, so its UE8M0 byte is 127 and the multiplier is exactly 1:
+    # every finite bf16 value in [-448, 448] reaches the fp8 conversion unchanged
+    bits = np.arange(65536, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    vals = bits[np.isfinite(f) & (np.abs(f) <= 448)].astype(np.uint16)
+    per = 127
+    n = -(-vals.size // per)
+    body = np.zeros(n * per, dtype=np.uint16)
+    body[:vals.size] = vals
+    x = np.concatenate([np.full((n, 1), 0x43E0, dtype=np.uint16), body.reshape(n, per)], axis=1)  # 448
+    qg, sg = _gpu_quant(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "row")
+    assert np.all(sg == 127)
+    qo, so = _oracle(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "row")
+    _assert_same(qg, qo, "q")
+
+
+def test_fp32_sweep_through_unit_scale():
+    # fp32 inputs (F32 path) covering every exponent of the e4m3 range, mid-points included
+    g = np.random.default_rng(5)
+    mant = g.integers(0, 1 << 23, size=1 << 20, dtype=np.uint32)
+    expo = g.integers(100, 136, size=1 << 20, dtype=np.uint32)
+    sign = g.integers(0, 2, size=1 << 20, dtype=np.uint32) << 31
+    v = (sign | (expo << 23) | mant).view(np.float32)
+    v = np.clip(v, -448, 448)
+    pos = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    extra = np.concatenate([mids, np.nextafter(mids, np.float32(1e9)), np.nextafter(mids, np.float32(-1)),
+                            -mids])
+    v = np.concatenate([v, extra]).astype(np.float32)
+    per = 127
+    n = -(-v.size // per)
+    body = np.zeros(n * per, dtype=np.float32)
+    body[:v.size] = v
+    x = np.concatenate([np.full((n, 1), 448.0, dtype=np.float32), body.reshape(n, per)], axis=1)
+    qg, sg = _gpu_quant(x, oracle.F32, 128, oracle.SCALE_UE8M0, "row")
+    assert np.all(sg == 127)
+    qref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()  # library cast
+    _assert_same(qg, qref, "q vs torch cast")
+    qo = oracle.e4m3_encode(x[:2048])
+    _assert_same(qg[:2048], qo, "q vs oracle encoder")
+
+
+# ----------------------------------------------------------------------------- masked
+def _masked_input(E, M, K, seed):
+    return np.stack([synth.activations_bf16(seed, M, K, tensor_id=(synth.T_X << 12) | e) for e in range(E)])
+
+
+@pytest.mark.parametrize("layout", ["col", "row"])
+def test_masked_small_full(layout):
+    E, M, K = 6, 40, 1024
+    x = _masked_input(E, M, K, 31)
+    mm = np.array([0, 1, 40, 39, 17, 3], dtype=np.int32)
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_UE8M0, layout, masked_m=mm)
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_F32, layout, masked_m=mm)
+
+
+def test_masked_counts_are_clamped():
+    E, M, K = 4, 8, 256
+    x = _masked_input(E, M, K, 32)
+    mm = np.array([-5, 100, 0, 8], dtype=np.int32)
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "col", masked_m=mm)
+
+
+def test_masked_result_independent_of_expected_m():
+    E, M, K = 8, 64, 512
+    x = _masked_input(E, M, K, 33)
+    mm = synth.masked_rows(33, E, M)
+    ref = None
+    for em in (0, 1, 7, 64, 1000):
+        q, s = _gpu_quant(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "col", masked_m=mm, expected_m=em)
+        if ref is None:
+            ref = (q, s)
+        else:
+            _assert_same(q, ref[0], f"q expected_m={em}")
+            _assert_same(s, ref[1], f"s expected_m={em}")
+
+
+def test_masked_silu_full():
+    E, M, K = 5, 24, 512
+    x = _masked_input(E, M, 2 * K, 34)
+    mm = np.array([24, 0, 5, 23, 1], dtype=np.int32)
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "col", silu=True, masked_m=mm)
+
+
+def _sample_rows(valid_rows_per_expert, g, per_expert=3):
+    re, rm = [], []
+    for e, r in enumerate(valid_rows_per_expert):
+        if r <= 0:
+            continue
+        pick = {0, r - 1} | set(g.integers(0, r, size=per_expert).tolist())
+        for m in sorted(pick):
+            re.append(e)
+            rm.append(m)
+    return np.array(re, dtype=np.int64), np.array(rm, dtype=np.int64)
+
+
+def _compare_rows(qg, sg, qo, so, re, rm, layout):
+    for e, m in zip(re, rm):
+        _assert_same(qg[e, m], qo[e, m], f"q row ({e},{m})")
+        if layout == "row":
+            _assert_same(sg[e, m].view(np.uint8), so[e, m].view(np.uint8), f"s row ({e},{m})")
+        else:
+            _assert_same(sg[e, :, m], so[e, :, m], f"s row ({e},{m})")
+
+
+@pytest.mark.parametrize("forced", [False, True])
+def test_masked_moe_workload_sampled(forced):
+    w = synth.MASKED
+    x = np.stack([synth.quant_input(w, e) for e in range(w.E)])
+    mm = synth.masked_rows(w.seed, w.E, w.M)
+    if forced:
+        mm[:4] = [0, 1, 511, 512]
+    qg, sg = _gpu_quant(x, oracle.BF16, w.G, oracle.SCALE_UE8M0, "col", masked_m=mm, expected_m=256)
+    re, rm = _sample_rows(mm, np.random.default_rng(7))
+    qo, so = _oracle(x, oracle.BF16, w.G, oracle.SCALE_UE8M0, "col", masked_m=mm, rows=(re, rm))
+    _compare_rows(qg, sg, qo, so, re, rm, "col")
+    for e in range(w.E):
+        assert np.all(qg[e, mm[e]:] == FILL), f"expert {e}: rows past masked_m were written"
+        assert np.all(sg[e, :, mm[e]:] == FILL), f"expert {e}: scales past masked_m were written"
+    assert not np.any((qg[0, :mm[0]] & 0x7F) == 0x7F)
+
+
+# ----------------------------------------------------------------------------- full-size flat
+def test_dense_m4096_sampled():
+    w = synth.dense(4096)
+    x = synth.quant_input(w)
+    qg, sg = _gpu_quant(x, oracle.BF16, w.G, oracle.SCALE_UE8M0, "col")
+    g = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, 4095], g.integers(0, 4096, size=61)]))
+    qo, so = _oracle(x, oracle.BF16, w.G, oracle.SCALE_UE8M0, "col", rows=(np.zeros_like(rows), rows))
+    for m in rows:
+        _assert_same(qg[m], qo[m], f"q row {m}")
+        _assert_same(sg[:, m], so[:, m], f"s row {m}")
+    # everywhere: no NaN code, and each group's largest code is in the top binade
+    assert not np.any((qg & 0x7F) == 0x7F)
+    top = (qg & 0x7F).reshape(4096, 56, 128).max(-1)
+    assert np.all(top >= 0x70)  # |code value| >= 128 > 448/4
+    assert sg.min() >= 85 and sg.max() <= 247
+
+
+def test_silu_workload_sampled():
+    w = synth.SILU
+    x = synth.quant_input(w)
+    qg, sg = _gpu_quant(x, oracle.BF16, w.G, oracle.SCALE_F32, "row", silu=True)
+    g = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, w.M - 1], g.integers(0, w.M, size=40)]))
+    qo, so = _oracle(x, oracle.BF16, w.G, oracle.SCALE_F32, "row", silu=True,
+                     rows=(np.zeros_like(rows), rows))
+    for m in rows:
+        _assert_same(qg[m], qo[m], f"q row {m}")
+        _assert_same(sg[m].view(np.uint8), so[m].view(np.uint8), f"s row {m}")
+    assert not np.any((qg & 0x7F) == 0x7F)
+
+
+# ----------------------------------------------------------------------------- API behaviour
+def test_empty_problems_are_noops():
+    f = fq()
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((0, 256), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((0, 2), dtype=torch.uint8, device="cuda")
+    f.fp8q_group_quant(x, q, s, 128)
+    x3 = torch.zeros((0, 4, 256), dtype=torch.bfloat16, device="cuda")
+    f.fp8q_group_quant(x3, torch.zeros((0, 4, 256), dtype=torch.uint8, device="cuda"),
+                       torch.zeros((0, 4, 2), dtype=torch.uint8, device="cuda"), 128,
+                       masked_m=torch.zeros(0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_invalid_arguments_write_nothing():
+    f = fq()
+    x = torch.ones((4, 256), dtype=torch.bfloat16, device="cuda")
+    q = torch.full((4, 256), FILL, dtype=torch.uint8, device="cuda")
+    s = torch.full((4, 2), FILL, dtype=torch.uint8, device="cuda")
+    with pytest.raises(f.Fp8qError) as ei:
+        f.fp8q_group_quant(x, q, s, 96)
+    assert ei.value.status == f.EUNSUPPORTED
+    with pytest.raises(f.Fp8qError) as ei:
+        f.fp8q_group_quant(x[:, 1:129], q[:, :128], s[:, :1], 128)  # misaligned x
+    assert ei.value.status == f.EALIGN
+    bad = torch.full((4, 4), FILL, dtype=torch.uint8, device="cuda")[:, ::2]  # strides (4, 2)
+    with pytest.raises(f.Fp8qError) as ei:
+        f.fp8q_group_quant(x, q, bad, 128)
+    assert ei.value.status == f.EINVAL
+    torch.cuda.synchronize()
+    assert torch.all(q == FILL) and torch.all(s == FILL)
+
+
+def test_runs_on_the_callers_stream():
+    x = synth.activations_bf16(27, 64, 2048)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        qg, sg = _gpu_quant(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "col", stream=st)
+    qo, so = _oracle(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "col")
+    _assert_same(qg, qo, "q")
+    _assert_same(sg, so, "s")
+
+
+def test_device_check():
+    f = fq()
+    assert f.fp8q_device_check(0) == f.OK
+    assert f.fp8q_device_check(1000) == f.EDEVICE
