@@ -1,0 +1,234 @@
+"""Benchmark of the FP8 group-quant -> block-scaled FP8 GEMM path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input resident in HBM:
+per-token-group quantization of bf16 activations (UE8M0 column-major scales) followed by
+the 1x128 x 128x128 block-scaled FP8 GEMM against e4m3 weights, bf16 output. The default
+workload is the dense DeepSeek-V3-like projection at M = 4096 (X [4096, 7168], W [4096,
+7168]); --workload picks another named shape for reporting (extra lines are only printed
+when asked for).
+
+Timing: W untimed warm-up steps, then exactly K steps between two synchronizations,
+measured with HIP events on the stream the kernels run on. The per-kernel roofline figures
+come from two more event-timed loops of K launches of each kernel alone. To defeat the 256 MB
+Infinity Cache and the L2s, the steps rotate over enough independent input/output buffer
+sets that the working set exceeds 1 GB.
+
+The CPU baseline is the plain oracle (single-threaded C), timed on a bounded sample of the
+same workload in the same run and scaled to the metric's unit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-FP8 GEMM TFLOP/s & % MFMA peak; group-quant GB/s & % HBM peak"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _kernel_source_tag(name: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "fp8_group_quant_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _measured_traffic(kernel_file: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        ent = rec[workload][kernel_file]
+        if ent["source_sha256_16"] != _kernel_source_tag(kernel_file):
+            return None
+        return ent["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def quant_bytes(rows: int, K: int, G: int, in_bytes: int, scale_bytes: int, silu: bool) -> int:
+    """Algorithmic bytes of one group-quant launch: read the input once, write codes + scales."""
+    width = 2 * K if silu else K
+    return rows * (width * in_bytes + K + (K // G) * scale_bytes)
+
+
+def build_workload(name: str):
+    import synth
+    if name.startswith("dense"):
+        M = int(name.split("_m")[1]) if "_m" in name else 4096
+        return synth.dense(M)
+    if name == "silu_down":
+        return synth.SILU
+    if name == "tiny":
+        return synth.TINY
+    raise SystemExit(f"unknown workload {name!r}")
+
+
+def run(args) -> dict:
+    import torch
+    import fp8_group_quant_amd as fq
+    import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    fq.load_library()
+    if fq.fp8q_device_check(0) != fq.OK:
+        raise SystemExit("device 0 is not a gfx950: " + fq.fp8q_last_error())
+    w = build_workload(args.workload)
+    M, K, N, G = w.M, w.K, w.N, w.G
+    dev = torch.device("cuda", 0)
+
+    # ---- synthetic inputs, resident in HBM
+    x_host = synth.quant_input(w)
+    w_host, sw_host = synth.weights(w)
+    ue8m0 = w.scale_fmt == "ue8m0"
+    x0 = torch.from_numpy(x_host).to(dev).view(torch.bfloat16)
+    w0 = torch.from_numpy(w_host).to(dev)
+    sw0 = torch.from_numpy(sw_host).to(dev)
+    set_bytes = x0.numel() * 2 + M * K + w0.numel() + M * N * 2
+    nsets = max(2, min(16, -(-(1 << 30) // set_bytes)))  # >= 1 GiB working set
+    sets = []
+    for _ in range(nsets):
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        s = fq.alloc_scales(None, M, K // G, w.scale_fmt, w.layout, dev)
+        sets.append(dict(x=x0.clone(), q=q, s=s, w=w0.clone(), sw=sw0.clone(),
+                         y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        st = sets[i % nsets]
+        if w.silu:
+            fq.fp8q_silu_mul_group_quant(st["x"], st["q"], st["s"], G)
+        else:
+            fq.fp8q_group_quant(st["x"], st["q"], st["s"], G)
+        fq.fp8q_gemm_blockscaled(st["q"], st["s"], st["w"], st["sw"], st["y"], fq.GEMM_BLOCK128)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        """average ms of n back-to-back launches between two events on the kernels' stream"""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def quant_only(i):
+        st = sets[i % nsets]
+        if w.silu:
+            fq.fp8q_silu_mul_group_quant(st["x"], st["q"], st["s"], G)
+        else:
+            fq.fp8q_group_quant(st["x"], st["q"], st["s"], G)
+
+    def gemm_only(i):
+        st = sets[i % nsets]
+        fq.fp8q_gemm_blockscaled(st["q"], st["s"], st["w"], st["sw"], st["y"], fq.GEMM_BLOCK128)
+
+    # the timed steps: exactly args.steps passes of the whole path
+    ms_step = timed(lambda i: step(args.warmup + i), args.steps)
+    # per-kernel averages (each kernel alone, same buffer rotation)
+    quant_ms = timed(quant_only, args.steps)
+    gemm_ms = timed(gemm_only, args.steps)
+
+    flops = 2.0 * M * N * K
+    qbytes = quant_bytes(M, K, G, 2, 1 if ue8m0 else 4, w.silu)
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    quant_gbs = qbytes / (quant_ms * 1e-3) / 1e9
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    traffic = _measured_traffic("gemm.hip", w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp8e4m3 -> fp32 acc -> bf16 (quant: bf16 -> e4m3, fp32 arithmetic)",
+        "data": "synthetic (seeded Philox; shapes and distributions of the named workload, no weights)",
+        "config": {"workload": w.name, "M": M, "K": K, "N": N, "group_size": G,
+                   "act_scale": f"{w.scale_fmt} {w.layout}-major", "weight_scale": "fp32 128x128",
+                   "buffer_sets": nsets, "silu": w.silu},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic},
+        "kernels": {
+            "group_quant": {"avg_ms": round(quant_ms, 5), "algorithmic_bytes": qbytes,
+                            "GB/s": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": _measured_traffic("quant.hip", w.name)},
+            "gemm_blockscaled": {"avg_ms": round(gemm_ms, 5), "flops": flops,
+                                 "TFLOP/s": round(gemm_tflops, 2),
+                                 "frac_mfma": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x_host, w_host, sw_host, args.cpu_rows)
+    return out
+
+
+def cpu_baseline(w, x_host, w_host, sw_host, rows: int) -> dict:
+    """Times the plain oracle on a bounded sample of the same workload: quantization of
+    `rows` activation rows, then the GEMM outputs of those rows against 512 weight rows.
+    The per-row and per-output costs are scaled up to the full step and reported in the
+    metric's unit."""
+    import oracle
+    M, K, N, G = w.M, w.K, w.N, w.G
+    fmt = oracle.SCALE_UE8M0 if w.scale_fmt == "ue8m0" else oracle.SCALE_F32
+    t0 = time.perf_counter()
+    q, s = oracle.group_quant(x_host[:rows], G, fmt, w.layout, silu=w.silu)
+    t1 = time.perf_counter()
+    cols = min(N, 512)
+    ms = np.repeat(np.arange(rows), cols)
+    ns = np.tile(np.arange(cols), rows)
+    oracle.gemm_block128(q, s, w_host, sw_host, fmt, w.layout, at=(ms, ns))
+    t2 = time.perf_counter()
+    t_step = (t1 - t0) / rows * M + (t2 - t1) / (rows * cols) * (M * N)
+    return {"value": round(2.0 * M * N * K / t_step / 1e12, 8), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{rows} rows quantized + {rows}x{cols} GEMM outputs of the same workload "
+                      f"({t2 - t0:.1f} s); step time extrapolated per row / per output = {t_step:.0f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_m4096")
+    ap.add_argument("--cpu-rows", type=int, default=384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no multi-GPU "
+              f"component in this build", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+    print(json.dumps(run(args)), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

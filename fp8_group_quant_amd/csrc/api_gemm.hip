@@ -1,0 +1,139 @@
+// api_gemm.hip — C ABI of the block-scaled GEMM calls: argument validation (host only,
+// before any device call), the device check, then the launch. Semantics: include/fp8q.h.
+#include "fp8q_internal.h"
+
+namespace fp8q {
+namespace {
+
+constexpr int64_t kMaxExperts = 4096;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_fmt(int f) { return f == FP8Q_SCALE_F32 || f == FP8Q_SCALE_UE8M0; }
+
+// Checks shared by the dense and the grouped call. rows = rows of A and Y per expert.
+int check_operands(const std::string& pre, const uint8_t* a, int64_t lda, const void* sa, int sa_fmt,
+                   int64_t sa_sm, int64_t sa_sk, const uint8_t* b, int64_t ldb, const void* sb,
+                   int sb_fmt, int64_t sb_sn, int64_t sb_sk, const uint16_t* y, int64_t ldy,
+                   int64_t rows, int64_t N, int64_t K, int mode) {
+  if (mode != FP8Q_GEMM_BLOCK128 && mode != FP8Q_GEMM_MX32)
+    return fail(FP8Q_EUNSUPPORTED, pre + "mode must be BLOCK128 or MX32");
+  if (!valid_fmt(sa_fmt) || !valid_fmt(sb_fmt))
+    return fail(FP8Q_EUNSUPPORTED, pre + "scale formats must be F32 or UE8M0");
+  if (mode == FP8Q_GEMM_MX32 && (sa_fmt != FP8Q_SCALE_UE8M0 || sb_fmt != FP8Q_SCALE_UE8M0))
+    return fail(FP8Q_EUNSUPPORTED, pre + "MX32 scales must be E8M0 bytes (FP8Q_SCALE_UE8M0)");
+  if (rows < 0 || N < 0 || K < 0) return fail(FP8Q_EINVAL, pre + "negative size");
+  if (K % 128 != 0) return fail(FP8Q_EINVAL, pre + "K must be a multiple of 128");
+  if (lda < 0 || ldb < 0 || ldy < 0 || sa_sm < 0 || sa_sk < 0 || sb_sn < 0 || sb_sk < 0)
+    return fail(FP8Q_EINVAL, pre + "negative stride");
+  if (rows == 0 || N == 0 || K == 0) return FP8Q_OK;
+  if (!a || !b || !y || !sa || !sb) return fail(FP8Q_EINVAL, pre + "null tensor pointer");
+  if ((rows > 1 && lda < K) || (N > 1 && ldb < K)) return fail(FP8Q_EINVAL, pre + "lda and ldb must be >= K");
+  if (rows > 1 && ldy < N) return fail(FP8Q_EINVAL, pre + "ldy must be >= N (rows of y overlap)");
+  if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0)
+    return fail(FP8Q_EALIGN, pre + "a, b and their row strides must be 16-byte aligned");
+  if (!aligned(y, 4) || ldy % 2 != 0) return fail(FP8Q_EALIGN, pre + "y must be 4-byte aligned with an even ldy");
+  if ((sa_fmt == FP8Q_SCALE_F32 && !aligned(sa, 4)) || (sb_fmt == FP8Q_SCALE_F32 && !aligned(sb, 4)))
+    return fail(FP8Q_EALIGN, pre + "fp32 scales must be 4-byte aligned");
+  if (mode == FP8Q_GEMM_MX32 && ((sa_sk == 1 && (!aligned(sa, 4) || sa_sm % 4 != 0)) ||
+                                 (sb_sk == 1 && (!aligned(sb, 4) || sb_sn % 4 != 0))))
+    return fail(FP8Q_EALIGN, pre + "MX32 scales with unit K stride need 4-byte aligned rows");
+  return FP8Q_OK;
+}
+
+}  // namespace
+}  // namespace fp8q
+
+extern "C" {
+
+int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t sa_sm,
+                          int64_t sa_sk, const uint8_t* b, int64_t ldb, const void* sb, int sb_fmt,
+                          int64_t sb_sn, int64_t sb_sk, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                          int64_t K, int mode, void* stream) {
+  using namespace fp8q;
+  set_error("");
+  const std::string pre = "fp8q_gemm_blockscaled: ";
+  int rc = check_operands(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy, M,
+                          N, K, mode);
+  if (rc != FP8Q_OK || M == 0 || N == 0 || K == 0) return rc;
+  rc = check_current_device();
+  if (rc != FP8Q_OK) return rc;
+  GemmParams p{};
+  p.a = a;
+  p.sa = sa;
+  p.b = b;
+  p.sb = sb;
+  p.y = y;
+  p.masked_m = nullptr;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.E = 1;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldy = ldy;
+  p.sa_sm = sa_sm;
+  p.sa_sk = sa_sk;
+  p.sb_sn = sb_sn;
+  p.sb_sk = sb_sk;
+  p.sa_fmt = sa_fmt;
+  p.sb_fmt = sb_fmt;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return mode == FP8Q_GEMM_MX32 ? launch_gemm_mx32(p, s) : launch_gemm_block128(p, 0, s);
+}
+
+int fp8q_grouped_gemm_masked(const uint8_t* a, int64_t a_se, int64_t lda, const void* sa, int sa_fmt,
+                             int64_t sa_se, int64_t sa_sm, int64_t sa_sk, const uint8_t* b, int64_t b_se,
+                             int64_t ldb, const void* sb, int sb_fmt, int64_t sb_se, int64_t sb_sn,
+                             int64_t sb_sk, uint16_t* y, int64_t y_se, int64_t ldy,
+                             const int32_t* masked_m, int64_t expected_m, int64_t E, int64_t cap,
+                             int64_t N, int64_t K, void* stream) {
+  using namespace fp8q;
+  set_error("");
+  const std::string pre = "fp8q_grouped_gemm_masked: ";
+  if (E < 0 || cap < 0) return fail(FP8Q_EINVAL, pre + "negative size");
+  if (E > kMaxExperts) return fail(FP8Q_EUNSUPPORTED, pre + "at most 4096 experts");
+  if (a_se < 0 || b_se < 0 || y_se < 0 || sa_se < 0 || sb_se < 0 || expected_m < 0)
+    return fail(FP8Q_EINVAL, pre + "negative stride or expected_m");
+  int rc = check_operands(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy,
+                          cap, N, K, FP8Q_GEMM_BLOCK128);
+  if (rc != FP8Q_OK) return rc;
+  if (E == 0 || cap == 0 || N == 0 || K == 0) return FP8Q_OK;
+  if (!masked_m) return fail(FP8Q_EINVAL, pre + "masked_m is required");
+  if (E > 1 && y_se < (cap - 1) * ldy + N) return fail(FP8Q_EINVAL, pre + "y experts overlap");
+  if (!aligned(a, 16) || a_se % 16 != 0 || b_se % 16 != 0)
+    return fail(FP8Q_EALIGN, pre + "expert strides of a and b must be multiples of 16 bytes");
+  if (y_se % 2 != 0) return fail(FP8Q_EALIGN, pre + "expert stride of y must be even");
+  const int64_t tiles = E * ((cap + 127) / 128) * ((N + 127) / 128);
+  if (tiles >= (int64_t(1) << 31)) return fail(FP8Q_EUNSUPPORTED, pre + "too many output tiles");
+  rc = check_current_device();
+  if (rc != FP8Q_OK) return rc;
+  GemmParams p{};
+  p.a = a;
+  p.sa = sa;
+  p.b = b;
+  p.sb = sb;
+  p.y = y;
+  p.masked_m = masked_m;
+  p.M = cap;
+  p.N = N;
+  p.K = K;
+  p.E = E;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldy = ldy;
+  p.a_se = a_se;
+  p.b_se = b_se;
+  p.y_se = y_se;
+  p.sa_sm = sa_sm;
+  p.sa_sk = sa_sk;
+  p.sa_se = sa_se;
+  p.sb_sn = sb_sn;
+  p.sb_sk = sb_sk;
+  p.sb_se = sb_se;
+  p.sa_fmt = sa_fmt;
+  p.sb_fmt = sb_fmt;
+  return launch_gemm_block128(p, expected_m, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -79,10 +79,12 @@ def activations_bf16(seed: int, rows: int, cols: int, outlier_p: float = 0.0,
     return f64_to_bf16_bits(_rows_chunked(seed, tensor_id, rows, cols, draw))
 
 
-def weight_codes(seed: int, rows: int, cols: int, tensor_id: int = T_W) -> np.ndarray:
-    """e4m3 bytes [rows, cols] of N(0,1) samples (values directly, no per-block scaling)."""
+def weight_codes(seed: int, rows: int, cols: int, tensor_id: int = T_W, sigma: float = 1.0) -> np.ndarray:
+    """e4m3 bytes [rows, cols] of N(0, sigma^2) samples (values directly, no per-block
+    scaling). sigma = 100 spreads the codes over the e4m3 range the way group-quantized
+    activations do (their group maximum maps to about 448)."""
     return f32_to_e4m3_bytes(_rows_chunked(seed, tensor_id, rows, cols,
-                                           lambda g, s: g.standard_normal(s)))
+                                           lambda g, s: sigma * g.standard_normal(s)))
 
 
 def block_scales(seed: int, rows: int, cols: int, sigma: float = 0.5,
@@ -163,3 +165,16 @@ def mx_operands(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray, np.nda
     ea = e8m0_exponents(w.seed, w.M, w.K // 32, tensor_id=T_EA)
     eb = e8m0_exponents(w.seed, w.N, w.K // 32, tensor_id=T_EB)
     return a, b, ea, eb
+
+
+def gemm_activation(w: Workload, expert: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """GEMM activation operand shaped like the group quantizer's output for workload w:
+    (e4m3 bytes [M, K] of N(0, 100^2) samples, scales [M, K/128] row-major storage). The
+    scales are UE8M0 bytes in 118..122 (2^-9 .. 2^-5) or fp32 2^-7 * lognormal(0, 0.3)."""
+    tid = T_A if expert is None else (T_A << 12) | expert
+    a = weight_codes(w.seed, w.M, w.K, tensor_id=tid, sigma=100.0)
+    if w.scale_fmt == "ue8m0":
+        s = e8m0_exponents(w.seed, w.M, w.K // 128, lo=-9, hi=-5, tensor_id=tid + 1)
+    else:
+        s = (2.0 ** -7 * block_scales(w.seed, w.M, w.K // 128, sigma=0.3, tensor_id=tid + 1)).astype(np.float32)
+    return a, s

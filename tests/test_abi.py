@@ -1,0 +1,106 @@
+"""CPU-side checks of the C ABI boundary (no compute calls): the built library loads and
+exports every function declared in include/fp8q.h, status strings are stable, the device
+check refuses when there is no gfx950, and the binding's stride marshalling reads layouts
+the way the header defines them."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+LIB = os.path.join(ROOT, "fp8_group_quant_amd", "libfp8q.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(fp8q_\w+)\s*\(", text, flags=re.M)))
+
+
+def _lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("fp8q_group_quant", "fp8q_silu_mul_group_quant", "fp8q_gemm_blockscaled",
+              "fp8q_grouped_gemm_masked", "fp8q_status_string", "fp8q_last_error", "fp8q_device_check"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    lib = _lib()
+    lib.fp8q_status_string.restype = ctypes.c_char_p
+    lib.fp8q_status_string.argtypes = [ctypes.c_int]
+    for code, prefix in [(0, b"FP8Q_OK"), (1, b"FP8Q_EINVAL"), (2, b"FP8Q_EUNSUPPORTED"), (3, b"FP8Q_EALIGN"),
+                         (4, b"FP8Q_EDEVICE"), (5, b"FP8Q_ELAUNCH")]:
+        assert lib.fp8q_status_string(code).startswith(prefix)
+    assert lib.fp8q_status_string(99) == b"unknown fp8q status"
+    lib.fp8q_last_error.restype = ctypes.c_char_p
+    assert lib.fp8q_last_error() is not None
+
+
+def test_header_constants_match_binding():
+    import fp8_group_quant_amd as fq
+    text = open(HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define (FP8Q_\w+) (\d+)", text))
+    assert consts["FP8Q_OK"] == fq.OK and consts["FP8Q_EINVAL"] == fq.EINVAL
+    assert consts["FP8Q_EUNSUPPORTED"] == fq.EUNSUPPORTED and consts["FP8Q_EALIGN"] == fq.EALIGN
+    assert consts["FP8Q_EDEVICE"] == fq.EDEVICE and consts["FP8Q_ELAUNCH"] == fq.ELAUNCH
+    assert consts["FP8Q_DTYPE_BF16"] == fq.DTYPE_BF16 and consts["FP8Q_DTYPE_F32"] == fq.DTYPE_F32
+    assert consts["FP8Q_SCALE_F32"] == fq.SCALE_F32 and consts["FP8Q_SCALE_UE8M0"] == fq.SCALE_UE8M0
+    assert consts["FP8Q_GEMM_BLOCK128"] == fq.GEMM_BLOCK128 and consts["FP8Q_GEMM_MX32"] == fq.GEMM_MX32
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the refusal path on a machine without a GPU")
+def test_device_check_refuses_without_gpu():
+    lib = _lib()
+    lib.fp8q_device_check.argtypes = [ctypes.c_int]
+    assert lib.fp8q_device_check(0) == 4  # FP8Q_EDEVICE
+
+
+def test_binding_reads_scale_layout_from_strides():
+    import fp8_group_quant_amd as fq
+    row = fq.alloc_scales(None, 6, 4, "f32", "row", "cpu")
+    col = fq.alloc_scales(None, 6, 4, "ue8m0", "col", "cpu")
+    assert fq._scale_strides(row) == (0, 4, 1)      # s_sg == 1: row-major
+    assert fq._scale_strides(col) == (0, 1, 6)      # s_sm == 1: column-major
+    col3 = fq.alloc_scales(3, 6, 4, "ue8m0", "col", "cpu")
+    assert fq._scale_strides(col3) == (24, 1, 6)
+    x = torch.empty(2, 5, 64, dtype=torch.bfloat16)
+    assert fq._as3(x) == (2, 5, 64, 320, 64)
+    assert fq._as3(x[0]) == (1, 5, 64, 320, 64)
+    with pytest.raises(ValueError):
+        fq._as3(torch.empty(4, 8)[:, ::2])
+
+
+def test_package_has_no_fallback_when_library_missing(tmp_path):
+    import fp8_group_quant_amd as fq
+    saved = fq._lib
+    try:
+        fq._lib = None
+        with pytest.raises(ImportError):
+            fq.load_library(str(tmp_path / "missing.so"))
+    finally:
+        fq._lib = saved
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "fp8_group_quant_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), errors="ignore").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "fp8q_oracle" not in text, f

@@ -1,0 +1,280 @@
+"""GPU parity of the block-scaled FP8 GEMMs against the fp64 CPU oracle computed from the
+same FP8 bytes and scales (both produced by the generator or by the oracle quantizer, never
+by the GPU). Tolerance (tests/gemm_check.py): 2 bf16 ulp per element, with a counted fp32
+accumulation allowance where the exact result cancels, and 2e-3 relative Frobenius error.
+
+Full comparison at sizes the oracle finishes in seconds (several tiles and ragged tails);
+at the named workloads' full sizes, seeded samples of output elements (including tile
+corners) are compared, in the same launch configuration the benchmark uses."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gemm_check import check
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0xA5A5
+SENT_I16 = SENT - 0x10000  # the same 16 bits as a signed value, for torch.full
+
+
+def fq():
+    import fp8_group_quant_amd
+    return fp8_group_quant_amd
+
+
+def _dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _gpu_block(a, sa, b, sb, sa_layout="row", ldy=None):
+    """a [M,K] codes, sa storage ([M,kb] row or [kb,M] col, fp32 or uint8), b [N,K], sb [nb,kb]."""
+    f = fq()
+    M, K = a.shape
+    N = b.shape[0]
+    ldy = ldy or N
+    y = torch.full((M, ldy), SENT_I16, dtype=torch.int16, device="cuda")
+    sa_d = _dev(sa)
+    sa_v = sa_d if sa_layout == "row" else sa_d.t()
+    f.fp8q_gemm_blockscaled(_dev(a), sa_v, _dev(b), _dev(sb), y.view(torch.bfloat16)[:, :N], f.GEMM_BLOCK128)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16)
+
+
+def _fmt(s):
+    return oracle.SCALE_F32 if s.dtype == np.float32 else oracle.SCALE_UE8M0
+
+
+def _sample(M, N, count, seed):
+    g = np.random.default_rng(seed)
+    ms = np.concatenate([[0, M - 1, 0, M - 1, min(127, M - 1), min(128, M - 1)], g.integers(0, M, count)])
+    ns = np.concatenate([[0, N - 1, N - 1, 0, min(128, N - 1), min(127, N - 1)], g.integers(0, N, count)])
+    return ms, ns
+
+
+# ----------------------------------------------------------------------------- BLOCK128 full
+def test_tiny_workload_full():
+    w = synth.TINY
+    x = synth.quant_input(w)
+    q, s = oracle.group_quant(x, 128, oracle.SCALE_F32, "row")  # oracle-quantized activations
+    wq, ws = synth.weights(w)
+    y = _gpu_block(q, s, wq, ws)
+    ys, ss = oracle.gemm_block128(q, s, wq, ws, oracle.SCALE_F32)
+    check(y, ys, ss, w.K, "tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 130, 256), (129, 200, 384), (257, 300, 640),
+                                   (64, 1024, 1024)])
+@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col"])
+@pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
+def test_ragged_shapes_full(M, N, K, sa_kind, sb_kind):
+    w = synth.Workload("t", seed=40 + M, M=M, K=K, N=N, scale_fmt=sa_kind.split("-")[0])
+    a, sa = synth.gemm_activation(w)
+    b, sbf = synth.weights(w)
+    sb = sbf if sb_kind == "f32" else synth.e8m0_exponents(7, sbf.shape[0], sbf.shape[1], tensor_id=77)
+    layout = sa_kind.split("-")[1]
+    sa_store = sa if layout == "row" else np.ascontiguousarray(sa.T)
+    y = _gpu_block(a, sa_store, b, sb, layout)
+    ys, ss = oracle.gemm_block128(a, sa_store, b, sb, _fmt(sa), layout, _fmt(sb))
+    check(y, ys, ss, K, f"{M}x{N}x{K}")
+
+
+def test_padded_output_rows_untouched():
+    w = synth.Workload("t", seed=50, M=70, K=256, N=130, scale_fmt="f32")
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    y = _gpu_block(a, sa, b, sb, "row", ldy=136)
+    ys, ss = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_F32)
+    check(y[:, :130], ys, ss, 256, "padded")
+    assert np.all(y[:, 130:] == SENT)
+
+
+# ----------------------------------------------------------------------------- BLOCK128 workloads
+@pytest.mark.parametrize("M", [1, 16, 128])
+def test_dense_small_m(M):
+    w = synth.dense(M)
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    sa_col = np.ascontiguousarray(sa.T)
+    y = _gpu_block(a, sa_col, b, sb, "col")
+    ns = np.unique(np.concatenate([np.arange(0, w.N, 16), np.arange(127, w.N, 128)]))
+    ms = np.repeat(np.arange(M), ns.size)
+    nn = np.tile(ns, M)
+    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", at=(ms, nn))
+    check(y[ms, nn], ys, ss, w.K, f"dense M={M}")
+
+
+def test_dense_m4096_sampled():
+    w = synth.dense(4096)
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    sa_col = np.ascontiguousarray(sa.T)
+    y = _gpu_block(a, sa_col, b, sb, "col")
+    ms, ns = _sample(w.M, w.N, 4000, 1)
+    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", at=(ms, ns))
+    check(y[ms, ns], ys, ss, w.K, "dense M=4096")
+    assert not np.any(y == SENT)
+
+
+def test_silu_down_projection_sampled():
+    w = synth.SILU
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    y = _gpu_block(a, sa, b, sb, "row")
+    ms, ns = _sample(w.M, w.N, 4000, 2)
+    ys, ss = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_F32, "row", at=(ms, ns))
+    check(y[ms, ns], ys, ss, w.K, "silu down-proj")
+
+
+# ----------------------------------------------------------------------------- masked grouped
+def _gpu_masked(a, sa_col, b, sb, mm, expected_m=0):
+    """a [E,cap,K]; sa_col [E,kb,cap] (UE8M0 column-major storage); b [E,N,K]; sb [E,nb,kb]."""
+    f = fq()
+    E, cap, K = a.shape
+    N = b.shape[1]
+    y = torch.full((E, cap, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_grouped_gemm_masked(_dev(a), _dev(sa_col).transpose(1, 2), _dev(b), _dev(sb), y.view(torch.bfloat16),
+                               _dev(mm.astype(np.int32)), expected_m)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16)
+
+
+@functools.lru_cache(maxsize=2)
+def _masked_operands(E, cap, N, K, seed):
+    w = synth.Workload("m", seed=seed, M=cap, K=K, N=N, E=E, scale_fmt="ue8m0", layout="col", masked=True)
+    a, sa, b, sb = [], [], [], []
+    for e in range(E):
+        ae, se = synth.gemm_activation(w, e)
+        be, sbe = synth.weights(w, e)
+        a.append(ae); sa.append(np.ascontiguousarray(se.T)); b.append(be); sb.append(sbe)
+    return np.stack(a), np.stack(sa), np.stack(b), np.stack(sb)
+
+
+def test_masked_small_full():
+    E, cap, N, K = 5, 200, 256, 512
+    a, sa, b, sb = _masked_operands(E, cap, N, K, 60)
+    mm = np.array([0, 1, 200, 130, 129], dtype=np.int32)
+    y = _gpu_masked(a, sa, b, sb, mm)
+    for e in range(E):
+        r = mm[e]
+        if r > 0:
+            ys, ss = oracle.gemm_block128(a[e, :r], np.ascontiguousarray(sa[e][:, :r]), b[e], sb[e],
+                                          oracle.SCALE_UE8M0, "col")
+            check(y[e, :r], ys, ss, K, f"expert {e}")
+        assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
+
+
+def test_masked_result_independent_of_expected_m():
+    E, cap, N, K = 6, 300, 384, 256
+    a, sa, b, sb = _masked_operands(E, cap, N, K, 61)
+    mm = np.array([300, 0, 17, 255, 256, 1], dtype=np.int32)
+    ref = _gpu_masked(a, sa, b, sb, mm, 0)
+    for em in (1, 64, 300, 5000):
+        assert np.array_equal(_gpu_masked(a, sa, b, sb, mm, em), ref), em
+
+
+def test_masked_counts_are_clamped():
+    E, cap, N, K = 3, 64, 128, 128
+    a, sa, b, sb = _masked_operands(E, cap, N, K, 62)
+    y = _gpu_masked(a, sa, b, sb, np.array([-4, 1000, 5], dtype=np.int32))
+    assert np.all(y[0] == SENT)
+    ys, ss = oracle.gemm_block128(a[1], np.ascontiguousarray(sa[1]), b[1], sb[1], oracle.SCALE_UE8M0, "col")
+    check(y[1], ys, ss, K, "clamped to cap")
+    assert np.all(y[2, 5:] == SENT)
+
+
+@pytest.mark.parametrize("forced", [False, True])
+def test_masked_moe_workload_sampled(forced):
+    w = synth.MASKED
+    a, sa, b, sb = _masked_operands(w.E, w.M, w.N, w.K, w.seed)
+    mm = synth.masked_rows(w.seed, w.E, w.M)
+    if forced:
+        mm[:4] = [0, 1, 511, 512]
+    y = _gpu_masked(a, sa, b, sb, mm, expected_m=256)
+    g = np.random.default_rng(3)
+    ys_all, y_all, s_all = [], [], []
+    for e in range(w.E):
+        r = int(mm[e])
+        assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
+        if r == 0:
+            continue
+        ms = np.concatenate([[0, r - 1], g.integers(0, r, 158)])
+        ns = np.concatenate([[0, w.N - 1], g.integers(0, w.N, 158)])
+        ys, ss = oracle.gemm_block128(a[e, :r], np.ascontiguousarray(sa[e][:, :r]), b[e], sb[e],
+                                      oracle.SCALE_UE8M0, "col", at=(ms, ns))
+        check(y[e][ms, ns], ys, ss, w.K, f"expert {e}")
+        ys_all.append(ys); y_all.append(y[e][ms, ns]); s_all.append(ss)
+    check(np.concatenate(y_all), np.concatenate(ys_all), np.concatenate(s_all), w.K, "all experts")
+
+
+# ----------------------------------------------------------------------------- MX32
+def _gpu_mx(a, ea, b, eb, sk_stride=False):
+    f = fq()
+    M, K = a.shape
+    N = b.shape[0]
+    y = torch.full((M, N), SENT_I16, dtype=torch.int16, device="cuda")
+    ea_d, eb_d = _dev(ea), _dev(eb)
+    if sk_stride:  # scales stored [K/32, rows] and passed as a transposed view (K stride != 1)
+        ea_d = _dev(np.ascontiguousarray(ea.T)).t()
+        eb_d = _dev(np.ascontiguousarray(eb.T)).t()
+    f.fp8q_gemm_blockscaled(_dev(a), ea_d, _dev(b), eb_d, y.view(torch.bfloat16), f.GEMM_MX32)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (130, 96, 256), (300, 260, 1024)])
+@pytest.mark.parametrize("sk_stride", [False, True])
+def test_mx_full(M, N, K, sk_stride):
+    a = synth.weight_codes(70, M, K, tensor_id=1)
+    b = synth.weight_codes(70, N, K, tensor_id=2)
+    ea = synth.e8m0_exponents(70, M, K // 32, tensor_id=3)
+    eb = synth.e8m0_exponents(70, N, K // 32, tensor_id=4)
+    y = _gpu_mx(a, ea, b, eb, sk_stride)
+    ys, ss = oracle.gemm_mx32(a, ea, b, eb)
+    check(y, ys, ss, K, f"mx {M}x{N}x{K}")
+
+
+def test_mx_workload_sampled():
+    w = synth.MX
+    a, b, ea, eb = synth.mx_operands(w)
+    y = _gpu_mx(a, ea, b, eb)
+    ms, ns = _sample(w.M, w.N, 4000, 4)
+    ys, ss = oracle.gemm_mx32(a, ea, b, eb, at=(ms, ns))
+    check(y[ms, ns], ys, ss, w.K, "mxfp8 8192^3")
+    assert not np.any(y == SENT)
+
+
+# ----------------------------------------------------------------------------- API behaviour
+def test_invalid_arguments_write_nothing():
+    f = fq()
+    a = torch.zeros((16, 256), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((32, 256), dtype=torch.uint8, device="cuda")
+    sa = torch.ones((16, 2), dtype=torch.float32, device="cuda")
+    sb = torch.ones((1, 2), dtype=torch.float32, device="cuda")
+    y = torch.full((16, 32), SENT_I16, dtype=torch.int16, device="cuda")
+    with pytest.raises(f.Fp8qError) as ei:  # MX32 needs E8M0 scales
+        f.fp8q_gemm_blockscaled(a, sa, b, sb, y.view(torch.bfloat16), f.GEMM_MX32)
+    assert ei.value.status == f.EUNSUPPORTED
+    with pytest.raises(f.Fp8qError) as ei:  # K not a multiple of 128
+        f.fp8q_gemm_blockscaled(a[:, :192], sa[:, :1], b[:, :192], sb[:, :1], y.view(torch.bfloat16))
+    assert ei.value.status == f.EINVAL
+    with pytest.raises(f.Fp8qError) as ei:  # misaligned a
+        f.fp8q_gemm_blockscaled(a.view(-1)[8:8 + 15 * 256].view(15, 256), sa[:15], b, sb,
+                                y[:15].view(torch.bfloat16))
+    assert ei.value.status == f.EALIGN
+    torch.cuda.synchronize()
+    assert torch.all(y == SENT_I16)
+
+
+def test_empty_gemm_is_noop():
+    f = fq()
+    y = torch.full((0, 128), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_gemm_blockscaled(torch.zeros((0, 128), dtype=torch.uint8, device="cuda"),
+                            torch.ones((0, 1), dtype=torch.float32, device="cuda"),
+                            torch.zeros((128, 128), dtype=torch.uint8, device="cuda"),
+                            torch.ones((1, 1), dtype=torch.float32, device="cuda"), y.view(torch.bfloat16))
+    torch.cuda.synchronize()
