@@ -260,12 +260,15 @@ __device__ void run_tile(const GemmParams& p, Smem<C>& sm, const Tile& t) {
           asm volatile("" : "+v"(acc[i][j]));  // keeps the subtile order (register pressure)
         }
         xf = xn;
-        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       const float sbv = sm.sb[st][(wn * C::WTN) / 128];
       const float* psa = sm.sa[st] + (wm * 16 + (lane & 15)) * C::SM;
+      // software-pipelined fold: the MFMAs of subtile i are issued before the fold of
+      // subtile i-1, so each fold reads results that are already complete
       v8i xf = frag(ta, wm * C::WTM, lane);
+      v4f prev[C::SN];
+      float s_prev = 0.f;
 #pragma unroll
       for (int i = 0; i < C::SM; i++) {
         const v8i xn = i + 1 < C::SM ? frag(ta, wm * C::WTM + (i + 1) * 16, lane) : xf;
@@ -276,16 +279,26 @@ __device__ void run_tile(const GemmParams& p, Smem<C>& sm, const Tile& t) {
           const v4f z = {0.f, 0.f, 0.f, 0.f};
           pr[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
         }
+        if (i > 0) {
 #pragma unroll
-        for (int j = 0; j < C::SN; j++) {
+          for (int j = 0; j < C::SN; j++) {
 #pragma unroll
-          for (int r = 0; r < 4; r++) acc[i][j][r] = fmaf(pr[j][r], s, acc[i][j][r]);
-          // pins the fold here: without it the folds sink below all MFMAs of the step and
-          // every MFMA result stays live at once
-          asm volatile("" : "+v"(acc[i][j]));
+            for (int r = 0; r < 4; r++) acc[i - 1][j][r] = fmaf(prev[j][r], s_prev, acc[i - 1][j][r]);
+            // keeps the folds in subtile order: otherwise they sink below every MFMA of the
+            // step and all MFMA results stay live at once (register spills)
+            asm volatile("" : "+v"(acc[i - 1][j]));
+          }
         }
+#pragma unroll
+        for (int j = 0; j < C::SN; j++) prev[j] = pr[j];
+        s_prev = s;
         xf = xn;
-        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < C::SN; j++) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[C::SM - 1][j][r] = fmaf(prev[j][r], s_prev, acc[C::SM - 1][j][r]);
+        asm volatile("" : "+v"(acc[C::SM - 1][j]));
       }
     }
     if (more) ss.store(sm, st ^ 1);
