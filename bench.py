@@ -211,6 +211,114 @@ def cpu_baseline(w, x_host, w_host, sw_host, rows: int) -> dict:
                       f"({t2 - t0:.1f} s); step time extrapolated per row / per output = {t_step:.0f} s"}
 
 
+def _timed(fn, n):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def _nsets(set_bytes: int, cap: int = 8) -> int:
+    return max(1, min(cap, -(-(1 << 30) // max(set_bytes, 1))))
+
+
+def suite(steps: int, warmup: int) -> list:
+    """Per-kernel figures for every named workload (quant GB/s, GEMM TFLOP/s and HBM GB/s),
+    each timed over `steps` launches rotating over >= 1 GiB of buffers where memory allows."""
+    import torch
+    import fp8_group_quant_amd as fq
+    import synth
+    dev = torch.device("cuda", 0)
+    fq.load_library()
+    lines = []
+
+    def report(name, kind, ms, flops=None, nbytes=None, extra=None):
+        rec = {"workload": name, "kernel": kind, "us": round(ms * 1e3, 2)}
+        if flops:
+            t = flops / (ms * 1e-3) / 1e12
+            rec.update({"TFLOP/s": round(t, 1), "frac_mfma": round(t / PEAK_FP8_TFLOPS, 4)})
+        if nbytes:
+            g = nbytes / (ms * 1e-3) / 1e9
+            rec.update({"GB/s": round(g, 1), "frac_hbm": round(g / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes})
+        if extra:
+            rec.update(extra)
+        lines.append(rec)
+        print(json.dumps(rec), flush=True)
+
+    def run(fn, n_sets):
+        for i in range(warmup):
+            fn(i)
+        return _timed(fn, steps)
+
+    # flat workloads: quant then block-scaled GEMM
+    for w in (synth.TINY, synth.dense(1), synth.dense(16), synth.dense(128), synth.dense(4096), synth.SILU):
+        M, K, N, G = w.M, w.K, w.N, w.G
+        x = torch.from_numpy(synth.quant_input(w)).to(dev).view(torch.bfloat16)
+        wq, ws = synth.weights(w)
+        wd, wsd = torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)
+        set_bytes = x.numel() * 2 + M * K + wd.numel() + M * N * 2
+        ns = _nsets(set_bytes)
+        sets = [dict(x=x.clone(), q=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                     s=fq.alloc_scales(None, M, K // G, w.scale_fmt, w.layout, dev), w=wd.clone(), sw=wsd.clone(),
+                     y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(ns)]
+        qf = fq.fp8q_silu_mul_group_quant if w.silu else fq.fp8q_group_quant
+        ms = run(lambda i: qf(sets[i % ns]["x"], sets[i % ns]["q"], sets[i % ns]["s"], G), ns)
+        report(w.name, "silu_mul_group_quant" if w.silu else "group_quant", ms,
+               nbytes=quant_bytes(M, K, G, 2, 1 if w.scale_fmt == "ue8m0" else 4, w.silu))
+        ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["q"], sets[i % ns]["s"], sets[i % ns]["w"],
+                                                    sets[i % ns]["sw"], sets[i % ns]["y"]), ns)
+        sbytes = M * (K // 128) * (1 if w.scale_fmt == "ue8m0" else 4) + ws.nbytes
+        report(w.name, "gemm_blockscaled", ms, flops=2.0 * M * N * K, nbytes=M * K + N * K + sbytes + M * N * 2)
+        del sets
+        torch.cuda.empty_cache()
+
+    # masked MoE: masked quant then masked grouped GEMM
+    w = synth.MASKED
+    E, cap, K, N, G = w.E, w.M, w.K, w.N, w.G
+    mm = synth.masked_rows(w.seed, E, cap)
+    rows = int(mm.sum())
+    x = torch.from_numpy(np.stack([synth.quant_input(w, e) for e in range(E)])).to(dev).view(torch.bfloat16)
+    mmd = torch.from_numpy(mm).to(dev)
+    q = torch.empty((E, cap, K), dtype=torch.uint8, device=dev)
+    sq = fq.alloc_scales(E, cap, K // G, "ue8m0", "col", dev)
+    ms = run(lambda i: fq.fp8q_group_quant(x, q, sq, G, masked_m=mmd, expected_m=cap // 2), 1)
+    report(w.name, "group_quant_masked", ms, nbytes=quant_bytes(rows, K, G, 2, 1, False), extra={"sum_masked_m": rows})
+    del x
+    wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+    for e in range(E):
+        a, b = synth.weights(w, e)
+        wq[e].copy_(torch.from_numpy(a))
+        ws[e].copy_(torch.from_numpy(b))
+    y = torch.empty((E, cap, N), dtype=torch.bfloat16, device=dev)
+    ms = run(lambda i: fq.fp8q_grouped_gemm_masked(q, sq, wq, ws, y, mmd, cap // 2), 1)
+    active = int((mm > 0).sum())
+    report(w.name, "grouped_gemm_masked", ms, flops=2.0 * rows * N * K,
+           nbytes=rows * K + active * N * K + rows * (K // 128) + active * ws[0].numel() * 4 + rows * N * 2,
+           extra={"sum_masked_m": rows})
+    del wq, q, y
+    torch.cuda.empty_cache()
+
+    # MXFP8
+    w = synth.MX
+    a, b, ea, eb = synth.mx_operands(w)
+    ad, bd, ead, ebd = (torch.from_numpy(t).to(dev) for t in (a, b, ea, eb))
+    ns = _nsets(a.nbytes + b.nbytes + w.M * w.N * 2, 4)
+    sets = [dict(a=ad.clone(), b=bd.clone(), ea=ead.clone(), eb=ebd.clone(),
+                 y=torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)) for _ in range(ns)]
+    ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
+                                                sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32), ns)
+    report(w.name, "gemm_mx32", ms, flops=2.0 * w.M * w.N * w.K,
+           nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2)
+    return lines
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +327,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="dense_m4096")
     ap.add_argument("--cpu-rows", type=int, default=384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", action="store_true",
+                    help="print per-kernel lines for every named workload instead of the step line")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no multi-GPU "
@@ -226,6 +336,9 @@ def main(argv=None) -> int:
         return 2
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+    if args.suite:
+        suite(args.steps, args.warmup)
+        return 0
     print(json.dumps(run(args)), flush=True)
     return 0
 

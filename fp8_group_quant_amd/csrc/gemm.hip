@@ -59,19 +59,23 @@ struct TileCfg {
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n range must stay inside one 128-block");
 };
 
-using Large = TileCfg<256, 256, 2, 4, 4>;
+using Large = TileCfg<256, 128, 4, 2, 4>;
 
-// LDS: two stages of both operand tiles and of the per-step scales. Scales are stored in
-// the order the lanes read them: BLOCK128 sa as [wave row][lane%16][subtile] floats;
-// MX32 E8M0 bytes as [wave row][lane%16][K block][subtile].
+// One LDS stage: both operand tiles of one K step and the step's scales. Scales are
+// stored in the order the lanes read them: BLOCK128 sa as [wave row][lane%16][subtile]
+// floats; MX32 E8M0 bytes as [wave row][lane%16][K block][subtile]. The kernel declares
+// the two stages as separate __shared__ objects and each K step receives them through
+// __restrict__ pointers, so the compiler can see that the direct-to-LDS loads into one
+// stage never alias the fragment reads of the other (otherwise it waits for them before
+// every read).
 template <class C>
-struct Smem {
-  alignas(16) uint8_t a[2][C::BM * BK];
-  alignas(16) uint8_t b[2][C::BN * BK];
-  alignas(16) float sa[2][C::BM];
-  float sb[2][C::BN / 128 > 0 ? C::BN / 128 : 1];
-  alignas(16) uint8_t ea[2][C::BM * 4];
-  alignas(16) uint8_t eb[2][C::BN * 4];
+struct Stage {
+  alignas(16) uint8_t a[C::BM * BK];
+  alignas(16) uint8_t b[C::BN * BK];
+  alignas(16) float sa[C::BM];
+  float sb[C::BN / 128 > 0 ? C::BN / 128 : 1];
+  alignas(16) uint8_t ea[C::BM * 4];
+  alignas(16) uint8_t eb[C::BN * 4];
 };
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
@@ -99,24 +103,44 @@ struct Tile {
   int64_t rows;  // valid rows of A for this expert (M, or clamped masked_m[e])
 };
 
-// Direct global -> LDS copy of one K step of a BM/BN-row operand tile. Wave w, load i
-// fills row block rb = w*kLoads + i (8 rows, 1 KB): lane l writes LDS slot l of the block,
-// which holds physical chunk l%8 of row rb*8 + l/8, i.e. logical chunk (l%8) ^ swz(row).
-template <int kLoads>
-__device__ __forceinline__ void load_stage(uint8_t* lds, const uint8_t* g, int64_t ld, int64_t r0,
-                                           int64_t rmax, int kb, int wave, int lane) {
+// Global -> register staging of one K step of both operand tiles. Chunk i (16 bytes) of
+// a tile is row i/8, logical chunk i%8; consecutive threads read consecutive chunks of a
+// row (one 128-byte line per 8 threads). The chunk is stored to LDS at its swizzled slot.
+template <class C>
+struct TileRegs {
+  static constexpr int kChA = C::BM * 8 / C::kThreads, kChB = C::BN * 8 / C::kThreads;
+  static_assert(kChA * C::kThreads == C::BM * 8 && kChB * C::kThreads == C::BN * 8, "chunk split");
+  u32x4 a[kChA], b[kChB];
+
+  __device__ __forceinline__ void load(const uint8_t* A, int64_t lda, int64_t m0, int64_t rmax,
+                                       const uint8_t* B, int64_t ldb, int64_t n0, int64_t nmax, int kb) {
+    const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < kLoads; i++) {
-    const int rb = wave * kLoads + i;
-    const int row = rb * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);
-    const int64_t grow = min(r0 + row, rmax);
-    const uint8_t* src = g + grow * ld + kb * BK + chunk * 16;
-    // (address-space conversions need C-style casts)
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(lds + rb * 1024), 16, 0, 0);
+    for (int j = 0; j < kChA; j++) {
+      const int i = tid + C::kThreads * j, r = i >> 3, c = i & 7;
+      a[j] = *reinterpret_cast<const u32x4*>(A + min(m0 + r, rmax) * lda + kb * BK + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kChB; j++) {
+      const int i = tid + C::kThreads * j, r = i >> 3, c = i & 7;
+      b[j] = *reinterpret_cast<const u32x4*>(B + min(n0 + r, nmax) * ldb + kb * BK + c * 16);
+    }
   }
-}
+
+  __device__ __forceinline__ void store(uint8_t* ta, uint8_t* tb) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kChA; j++) {
+      const int i = tid + C::kThreads * j, r = i >> 3, c = i & 7;
+      *reinterpret_cast<u32x4*>(ta + r * BK + ((c ^ swz(r)) << 4)) = a[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kChB; j++) {
+      const int i = tid + C::kThreads * j, r = i >> 3, c = i & 7;
+      *reinterpret_cast<u32x4*>(tb + r * BK + ((c ^ swz(r)) << 4)) = b[j];
+    }
+  }
+};
 
 // MFMA operand fragment of 16 rows starting at row r (lane l: row r + l%16, K runs at
 // 16*(l/16) and 64 + 16*(l/16)).
@@ -133,9 +157,22 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int r, int lane) {
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// float value of a raw scale word: fp32 bits, or a UE8M0 byte b -> 2^(b-127)
+template <int FMT>
+__device__ __forceinline__ float scale_value(uint32_t raw) {
+  if constexpr (FMT == FP8Q_SCALE_F32) {
+    return __uint_as_float(raw);
+  } else {
+    if (raw == 0u) return __uint_as_float(0x00400000u);  // 2^-127 (subnormal)
+    if (raw == 255u) return __uint_as_float(0x7FC00000u);
+    return __uint_as_float(raw << 23);
+  }
+}
+
 // Scale staging for one K step: thread t < BM fetches the scale(s) of tile row t of A;
 // thread BM + u fetches those of B (MX32: row u of the tile; BLOCK128: N block u). The
-// value is held in one register from the top of a step to its end, then stored to LDS.
+// raw word is held in one register from the top of a step to its end (no use before
+// then, so the load never stalls the step), then converted and stored to LDS.
 template <class C, bool MX, int SA_FMT, int SB_FMT>
 struct ScaleStage {
   uint32_t v;
@@ -143,7 +180,8 @@ struct ScaleStage {
   __device__ __forceinline__ void load(const GemmParams& p, const void* SA, const void* SB, int64_t m0,
                                        int64_t n0, int64_t rmax, int kb) {
     const int tid = threadIdx.x;
-    v = 0;
+    // (threads that fetch no scale leave v untouched: store() never reads it for them, and
+    // writing it would wait for the load still landing in it)
     if constexpr (MX) {
       const uint8_t* s8;
       int64_t off, sk;
@@ -159,19 +197,26 @@ struct ScaleStage {
         return;
       }
       const int64_t k0 = static_cast<int64_t>(4 * kb) * sk;
-      v = static_cast<uint32_t>(s8[off + k0]) | (static_cast<uint32_t>(s8[off + k0 + sk]) << 8) |
-          (static_cast<uint32_t>(s8[off + k0 + 2 * sk]) << 16) | (static_cast<uint32_t>(s8[off + k0 + 3 * sk]) << 24);
+      if (sk == 1 && ((reinterpret_cast<uintptr_t>(s8) + off + k0) & 3) == 0) {
+        v = *reinterpret_cast<const uint32_t*>(s8 + off + k0);  // the 4 bytes of K blocks 4kb..4kb+3
+      } else {
+        v = static_cast<uint32_t>(s8[off + k0]) | (static_cast<uint32_t>(s8[off + k0 + sk]) << 8) |
+            (static_cast<uint32_t>(s8[off + k0 + 2 * sk]) << 16) |
+            (static_cast<uint32_t>(s8[off + k0 + 3 * sk]) << 24);
+      }
     } else {
       if (tid < C::BM) {
-        v = __float_as_uint(scale_at<SA_FMT>(SA, min(m0 + tid, rmax) * p.sa_sm + kb * p.sa_sk));
+        const int64_t idx = min(m0 + tid, rmax) * p.sa_sm + kb * p.sa_sk;
+        v = SA_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(SA)[idx] : static_cast<const uint8_t*>(SA)[idx];
       } else if (tid < C::BM + C::BN / 128) {
         const int64_t nb = min(n0 / 128 + (tid - C::BM), (p.N - 1) / 128);
-        v = __float_as_uint(scale_at<SB_FMT>(SB, nb * p.sb_sn + kb * p.sb_sk));
+        const int64_t idx = nb * p.sb_sn + kb * p.sb_sk;
+        v = SB_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(SB)[idx] : static_cast<const uint8_t*>(SB)[idx];
       }
     }
   }
 
-  __device__ __forceinline__ void store(Smem<C>& sm, int st) const {
+  __device__ __forceinline__ void store(Stage<C>& sg) const {
     const int tid = threadIdx.x;
     if constexpr (MX) {
       if (tid < C::BM + C::BN) {
@@ -179,99 +224,88 @@ struct ScaleStage {
         const int r = is_a ? tid : tid - C::BM;
         const int wt = is_a ? C::WTM : C::WTN, nsub = wt / 16;
         const int w = r / wt, i = (r % wt) / 16, l16 = r % 16;
-        uint8_t* dst = is_a ? sm.ea[st] : sm.eb[st];
+        uint8_t* dst = is_a ? sg.ea : sg.eb;
 #pragma unroll
         for (int b = 0; b < 4; b++) dst[((w * 16 + l16) * 4 + b) * nsub + i] = static_cast<uint8_t>(v >> (8 * b));
       }
     } else {
       if (tid < C::BM) {
         const int w = tid / C::WTM, i = (tid % C::WTM) / 16, l16 = tid % 16;
-        sm.sa[st][(w * 16 + l16) * C::SM + i] = __uint_as_float(v);
+        sg.sa[(w * 16 + l16) * C::SM + i] = scale_value<SA_FMT>(v);
       } else if (tid < C::BM + C::BN / 128) {
-        sm.sb[st][tid - C::BM] = __uint_as_float(v);
+        sg.sb[tid - C::BM] = scale_value<SB_FMT>(v);
       }
     }
   }
 };
 
-// Computes one BM x BN output tile and stores it.
+// Per-tile loop state shared by the K steps.
 template <class C, bool MX, int SA_FMT, int SB_FMT>
-__device__ void run_tile(const GemmParams& p, Smem<C>& sm, const Tile& t) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
-  const uint8_t* A = p.a + t.e * p.a_se;
-  const uint8_t* B = p.b + t.e * p.b_se;
-  const int sa_w = (MX || SA_FMT == FP8Q_SCALE_UE8M0) ? 1 : 4;
-  const int sb_w = (MX || SB_FMT == FP8Q_SCALE_UE8M0) ? 1 : 4;
-  const void* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * sa_w;
-  const void* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * sb_w;
-  const int64_t m0 = t.tm * C::BM, n0 = t.tn * C::BN;
-  const int64_t rmax = t.rows - 1, nmax = p.N - 1;
-  const int nkb = static_cast<int>(p.K / BK);
-
+struct TileRun {
+  const GemmParams& p;
+  const uint8_t* A;
+  const uint8_t* B;
+  const void* SA;
+  const void* SB;
+  int64_t m0, n0, rmax, nmax;
+  int nkb, wave, lane, wm, wn;
+  // two register sets: set q holds the tiles and scales of a step two steps ahead
+  ScaleStage<C, MX, SA_FMT, SB_FMT> ss[2];
+  TileRegs<C> tr[2];
   v4f acc[C::SM][C::SN];
-#pragma unroll
-  for (int i = 0; i < C::SM; i++)
-#pragma unroll
-    for (int j = 0; j < C::SN; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  ScaleStage<C, MX, SA_FMT, SB_FMT> ss;
-  load_stage<C::kLoadsA>(sm.a[0], A, p.lda, m0, rmax, 0, wave, lane);
-  load_stage<C::kLoadsB>(sm.b[0], B, p.ldb, n0, nmax, 0, wave, lane);
-  ss.load(p, SA, SB, m0, n0, rmax, 0);
-  ss.store(sm, 0);
+  __device__ __forceinline__ void issue(int q, int kb) {
+    tr[q].load(A, p.lda, m0, rmax, B, p.ldb, n0, nmax, kb);
+    ss[q].load(p, SA, SB, m0, n0, rmax, kb);
+  }
 
-  for (int kb = 0; kb < nkb; kb++) {
-    const int st = kb & 1;
-    wait_vm();         // this thread's loads of stage kb have landed
-    __syncthreads();   // ... everyone's; and nobody still reads stage st^1
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      load_stage<C::kLoadsA>(sm.a[st ^ 1], A, p.lda, m0, rmax, kb + 1, wave, lane);
-      load_stage<C::kLoadsB>(sm.b[st ^ 1], B, p.ldb, n0, nmax, kb + 1, wave, lane);
-      ss.load(p, SA, SB, m0, n0, rmax, kb + 1);
-    }
-    const uint8_t* ta = sm.a[st];
-    const uint8_t* tb = sm.b[st];
+  __device__ __forceinline__ void commit(int q, Stage<C>& nx) {
+    tr[q].store(nx.a, nx.b);
+    ss[q].store(nx);
+  }
+
+  // One K step (parity Q = kb % 2): compute from stage cu = stage Q; fetch step kb + 2 into
+  // register set Q; write register set 1-Q (step kb + 1, fetched one step earlier) into
+  // stage nx. Q is a compile-time constant so every register set and stage is fixed.
+  template <int Q>
+  __device__ __forceinline__ void step(Stage<C>& cu, Stage<C>& nx, int kb) {
+    // every thread's stage-kb writes are in LDS, and nobody reads stage nx any more
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(Q, min(kb + 2, nkb - 1));  // the index is clamped so every step issues the same loads
+
     v8i wf[C::SN];
 #pragma unroll
-    for (int j = 0; j < C::SN; j++) wf[j] = frag(tb, wn * C::WTN + j * 16, lane);
+    for (int j = 0; j < C::SN; j++) wf[j] = frag(cu.b, wn * C::WTN + j * 16, lane);
     if constexpr (MX) {
       // this lane's E8M0 bytes: A rows (subtile i) and B rows (subtile j), K block 4kb + lane/16
       uint32_t ea_w[(C::SM + 3) / 4], eb_w[(C::SN + 3) / 4];
-      const uint8_t* pea = sm.ea[st] + ((wm * 16 + (lane & 15)) * 4 + (lane >> 4)) * C::SM;
-      const uint8_t* peb = sm.eb[st] + ((wn * 16 + (lane & 15)) * 4 + (lane >> 4)) * C::SN;
+      const uint8_t* pea = cu.ea + ((wm * 16 + (lane & 15)) * 4 + (lane >> 4)) * C::SM;
+      const uint8_t* peb = cu.eb + ((wn * 16 + (lane & 15)) * 4 + (lane >> 4)) * C::SN;
 #pragma unroll
       for (int q = 0; q < (C::SM + 3) / 4; q++) ea_w[q] = reinterpret_cast<const uint32_t*>(pea)[q];
 #pragma unroll
       for (int q = 0; q < (C::SN + 3) / 4; q++) eb_w[q] = reinterpret_cast<const uint32_t*>(peb)[q];
-      // one m subtile at a time: its fragment is read one subtile ahead, and the scheduling
-      // barrier keeps later subtiles' loads and MFMAs from being hoisted (register pressure)
-      v8i xf = frag(ta, wm * C::WTM, lane);
+      v8i xf = frag(cu.a, wm * C::WTM, lane);
 #pragma unroll
       for (int i = 0; i < C::SM; i++) {
-        const v8i xn = i + 1 < C::SM ? frag(ta, wm * C::WTM + (i + 1) * 16, lane) : xf;
+        const v8i xn = i + 1 < C::SM ? frag(cu.a, wm * C::WTM + (i + 1) * 16, lane) : xf;
         const int sa_i = static_cast<int>(ea_w[i / 4] >> (8 * (i % 4)));
 #pragma unroll
         for (int j = 0; j < C::SN; j++) {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wf[j], xf, acc[i][j], 0, 0, 0, static_cast<int>(eb_w[j / 4] >> (8 * (j % 4))), 0, sa_i);
-          asm volatile("" : "+v"(acc[i][j]));  // keeps the subtile order (register pressure)
         }
         xf = xn;
       }
     } else {
-      const float sbv = sm.sb[st][(wn * C::WTN) / 128];
-      const float* psa = sm.sa[st] + (wm * 16 + (lane & 15)) * C::SM;
-      // software-pipelined fold: the MFMAs of subtile i are issued before the fold of
-      // subtile i-1, so each fold reads results that are already complete
-      v8i xf = frag(ta, wm * C::WTM, lane);
-      v4f prev[C::SN];
-      float s_prev = 0.f;
+      const float sbv = cu.sb[(wn * C::WTN) / 128];
+      const float* psa = cu.sa + (wm * 16 + (lane & 15)) * C::SM;
+      v8i xf = frag(cu.a, wm * C::WTM, lane);
 #pragma unroll
       for (int i = 0; i < C::SM; i++) {
-        const v8i xn = i + 1 < C::SM ? frag(ta, wm * C::WTM + (i + 1) * 16, lane) : xf;
+        const v8i xn = i + 1 < C::SM ? frag(cu.a, wm * C::WTM + (i + 1) * 16, lane) : xf;
         const float s = psa[i] * sbv;
         v4f pr[C::SN];
 #pragma unroll
@@ -279,31 +313,55 @@ __device__ void run_tile(const GemmParams& p, Smem<C>& sm, const Tile& t) {
           const v4f z = {0.f, 0.f, 0.f, 0.f};
           pr[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
         }
-        if (i > 0) {
 #pragma unroll
-          for (int j = 0; j < C::SN; j++) {
+        for (int j = 0; j < C::SN; j++) {
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[i - 1][j][r] = fmaf(prev[j][r], s_prev, acc[i - 1][j][r]);
-            // keeps the folds in subtile order: otherwise they sink below every MFMA of the
-            // step and all MFMA results stay live at once (register spills)
-            asm volatile("" : "+v"(acc[i - 1][j]));
-          }
+          for (int r = 0; r < 4; r++) acc[i][j][r] = fmaf(pr[j][r], s, acc[i][j][r]);
         }
-#pragma unroll
-        for (int j = 0; j < C::SN; j++) prev[j] = pr[j];
-        s_prev = s;
         xf = xn;
       }
-#pragma unroll
-      for (int j = 0; j < C::SN; j++) {
-#pragma unroll
-        for (int r = 0; r < 4; r++) acc[C::SM - 1][j][r] = fmaf(prev[j][r], s_prev, acc[C::SM - 1][j][r]);
-        asm volatile("" : "+v"(acc[C::SM - 1][j]));
-      }
     }
-    if (more) ss.store(sm, st ^ 1);
+    if (kb + 1 < nkb) commit(1 - Q, nx);  // waits for set 1-Q only, not the loads just issued
+  }
+};
+
+// Computes one BM x BN output tile and stores it.
+template <class C, bool MX, int SA_FMT, int SB_FMT>
+__device__ void run_tile(const GemmParams& p, Stage<C>& s0, Stage<C>& s1, const Tile& t) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sa_w = (MX || SA_FMT == FP8Q_SCALE_UE8M0) ? 1 : 4;
+  const int sb_w = (MX || SB_FMT == FP8Q_SCALE_UE8M0) ? 1 : 4;
+  TileRun<C, MX, SA_FMT, SB_FMT> r{p};
+  r.A = p.a + t.e * p.a_se;
+  r.B = p.b + t.e * p.b_se;
+  r.SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * sa_w;
+  r.SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * sb_w;
+  r.m0 = t.tm * C::BM;
+  r.n0 = t.tn * C::BN;
+  r.rmax = t.rows - 1;
+  r.nmax = p.N - 1;
+  r.nkb = static_cast<int>(p.K / BK);
+  r.wave = wave;
+  r.lane = lane;
+  r.wm = wave % C::WAVES_M;
+  r.wn = wave / C::WAVES_M;
+#pragma unroll
+  for (int i = 0; i < C::SM; i++)
+#pragma unroll
+    for (int j = 0; j < C::SN; j++) r.acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  r.issue(0, 0);
+  r.commit(0, s0);
+  r.issue(1, min(1, r.nkb - 1));
+  for (int kb = 0; kb < r.nkb; kb += 2) {
+    r.template step<0>(s0, s1, kb);
+    if (kb + 1 < r.nkb) r.template step<1>(s1, s0, kb + 1);
   }
   __syncthreads();  // the next tile's first loads overwrite stage 0
+  const int64_t m0 = r.m0, n0 = r.n0;
+  const int wm = r.wm, wn = r.wn;
+  v4f (&acc)[C::SM][C::SN] = r.acc;
 
   // epilogue: lane holds Y[m][n..n+3], m = m0+wm*WTM+i*16+lane%16, n = n0+wn*WTN+j*16+4*(lane/16)
   uint16_t* Y = p.y + t.e * p.y_se;
@@ -331,7 +389,8 @@ __device__ void run_tile(const GemmParams& p, Smem<C>& sm, const Tile& t) {
 
 template <class C, bool MX, int SA_FMT, int SB_FMT>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
-  __shared__ Smem<C> sm;
+  __shared__ Stage<C> stage0;
+  __shared__ Stage<C> stage1;
   __shared__ int32_t part[C::kThreads];
   extern __shared__ int32_t pref[];  // masked only, E + 1 entries: exclusive prefix of tiles
   const int tid = threadIdx.x;
@@ -404,7 +463,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
       tile.tn = (t % in_group) / gm;
       tile.rows = p.M;
     }
-    run_tile<C, MX, SA_FMT, SB_FMT>(p, sm, tile);
+    run_tile<C, MX, SA_FMT, SB_FMT>(p, stage0, stage1, tile);
   }
 }
 
