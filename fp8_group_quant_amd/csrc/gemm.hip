@@ -467,6 +467,128 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   }
 }
 
+
+// ------------------------------------------------------------------ skinny GEMM (small M)
+// For M <= 128 the product is bound by streaming B (the weights) from HBM, and 256x128
+// tiles would leave most CUs idle. Here each workgroup owns 16 rows of B (one MFMA n
+// slice) against all M rows of A; its four waves split the K blocks four ways (block kb
+// goes to wave kb % 4) and each lane loads its MFMA fragments straight from global memory,
+// U blocks ahead, with no LDS staging. The four partial sums are added through LDS at the
+// end. BLOCK128 only.
+constexpr int kSkinnyThreads = 256;
+constexpr int64_t kSkinnyMaxM = 128;  // at most 8 m subtiles
+
+template <int SM>
+struct SkinnyCfg {
+  static constexpr int U = SM == 1 ? 8 : (SM == 2 ? 6 : (SM <= 4 ? 3 : 2));  // K blocks in flight per wave
+};
+
+__device__ __forceinline__ v8i frag_global(const uint8_t* row, int kb, int lane) {
+  const uint8_t* p = row + kb * BK + (lane >> 4) * 16;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 64);
+  v8i v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
+template <int SM, int SA_FMT, int SB_FMT>
+__global__ __launch_bounds__(kSkinnyThreads) void gemm_skinny_kernel(GemmParams p) {
+  constexpr int U = SkinnyCfg<SM>::U;
+  __shared__ v4f red[4][SM][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int nkb = static_cast<int>(p.K / BK);
+  const uint8_t* wrow = p.b + min(n0 + (lane & 15), p.N - 1) * p.ldb;
+  const uint8_t* xrow[SM];
+  int64_t mrow[SM];
+#pragma unroll
+  for (int i = 0; i < SM; i++) {
+    mrow[i] = min(static_cast<int64_t>(i * 16 + (lane & 15)), p.M - 1);
+    xrow[i] = p.a + mrow[i] * p.lda;
+  }
+  const int64_t nb = n0 / 128;
+  v4f acc[SM];
+#pragma unroll
+  for (int i = 0; i < SM; i++) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb0 = wave; kb0 < nkb; kb0 += 4 * U) {
+    v8i wf[U], xf[U][SM];
+    uint32_t sa_raw[U][SM], sb_raw[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int kb = min(kb0 + 4 * u, nkb - 1);  // clamped: blocks past the end are loaded, not used
+      wf[u] = frag_global(wrow, kb, lane);
+#pragma unroll
+      for (int i = 0; i < SM; i++) {
+        xf[u][i] = frag_global(xrow[i], kb, lane);
+        const int64_t si = mrow[i] * p.sa_sm + kb * p.sa_sk;
+        sa_raw[u][i] = SA_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(p.sa)[si]
+                                                : static_cast<const uint8_t*>(p.sa)[si];
+      }
+      const int64_t bi = nb * p.sb_sn + kb * p.sb_sk;
+      sb_raw[u] = SB_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(p.sb)[bi]
+                                           : static_cast<const uint8_t*>(p.sb)[bi];
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (kb0 + 4 * u < nkb) {
+        const float sbv = scale_value<SB_FMT>(sb_raw[u]);
+#pragma unroll
+        for (int i = 0; i < SM; i++) {
+          const v4f z = {0.f, 0.f, 0.f, 0.f};
+          const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[u], xf[u][i], z, 0, 0, 0, 0, 0, 0);
+          const float sv = scale_value<SA_FMT>(sa_raw[u][i]) * sbv;
+#pragma unroll
+          for (int r = 0; r < 4; r++) acc[i][r] = fmaf(pr[r], sv, acc[i][r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SM; i++) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < SM; i++) {
+      v4f t = red[0][i][lane];
+#pragma unroll
+      for (int w = 1; w < 4; w++) {
+        const v4f o = red[w][i][lane];
+        t[0] += o[0]; t[1] += o[1]; t[2] += o[2]; t[3] += o[3];
+      }
+      const int64_t m = i * 16 + (lane & 15);
+      if (m >= p.M) continue;
+      uint16_t* yrow = p.y + m * p.ldy;
+      const int64_t n = n0 + 4 * (lane >> 4);
+      const uint32_t h0 = bf16_rne(t[0]), h1 = bf16_rne(t[1]), h2 = bf16_rne(t[2]), h3 = bf16_rne(t[3]);
+      if (n + 3 < p.N) {
+        *reinterpret_cast<uint32_t*>(yrow + n) = h0 | (h1 << 16);
+        *reinterpret_cast<uint32_t*>(yrow + n + 2) = h2 | (h3 << 16);
+      } else {
+        if (n < p.N) yrow[n] = static_cast<uint16_t>(h0);
+        if (n + 1 < p.N) yrow[n + 1] = static_cast<uint16_t>(h1);
+        if (n + 2 < p.N) yrow[n + 2] = static_cast<uint16_t>(h2);
+      }
+    }
+  }
+}
+
+template <int SM, int SA_FMT, int SB_FMT>
+void launch_skinny(const GemmParams& p, hipStream_t s) {
+  const int grid = static_cast<int>((p.N + 15) / 16);
+  hipLaunchKernelGGL((gemm_skinny_kernel<SM, SA_FMT, SB_FMT>), dim3(grid), dim3(kSkinnyThreads), 0, s, p);
+}
+
+template <int SA_FMT, int SB_FMT>
+void launch_skinny_m(const GemmParams& p, hipStream_t s) {
+  if (p.M <= 16) launch_skinny<1, SA_FMT, SB_FMT>(p, s);
+  else if (p.M <= 32) launch_skinny<2, SA_FMT, SB_FMT>(p, s);
+  else if (p.M <= 64) launch_skinny<4, SA_FMT, SB_FMT>(p, s);
+  else launch_skinny<8, SA_FMT, SB_FMT>(p, s);
+}
+
 template <class C, bool MX, int SA_FMT, int SB_FMT>
 void launch(const GemmParams& p, int grid, hipStream_t s) {
   const size_t lds = p.masked_m ? static_cast<size_t>(p.E + 1) * sizeof(int32_t) : 0;
@@ -499,6 +621,13 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   }
   const int grid = grid_for(tiles);
   const bool a8 = p.sa_fmt == FP8Q_SCALE_UE8M0, b8 = p.sb_fmt == FP8Q_SCALE_UE8M0;
+  if (!p.masked_m && p.M <= kSkinnyMaxM) {
+    if (a8 && b8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, stream);
+    else if (a8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, stream);
+    else if (b8) launch_skinny_m<FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, stream);
+    else launch_skinny_m<FP8Q_SCALE_F32, FP8Q_SCALE_F32>(p, stream);
+    return finish("block-scaled GEMM launch");
+  }
   if (a8 && b8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid, stream);
   else if (a8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, grid, stream);
   else if (b8) launch<C, false, FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, grid, stream);
