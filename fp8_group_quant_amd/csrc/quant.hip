@@ -9,12 +9,12 @@
 // example; the PR's fuse_silu_and_mul trait).
 //
 // Mapping to CDNA4:
-//   - one wavefront (64 lanes) streams a segment of one row; each lane owns 8
-//     consecutive elements of every 512-element chunk, so every load is a 16-byte
-//     (bf16/f16) or 2x16-byte (f32) vector load and the wave reads 1 KB contiguous per
-//     chunk. All chunk loads of a segment are issued before any arithmetic.
-//   - a group of G elements lives in G/8 adjacent lanes; its amax is a 2-4 step DPP
-//     butterfly (quad_perm, row_half_mirror, row_mirror) inside one 16-lane DPP row.
+//   - one wavefront (64 lanes) streams a segment of one row; each lane owns 16
+//     consecutive elements (32 bytes of bf16) of every 1024-element chunk: two adjacent
+//     16-byte loads in, one 16-byte store of e4m3 codes out (the pages' "32B/lane"
+//     tiling). All chunk loads of a segment are issued before any arithmetic.
+//   - a group of G elements lives in G/16 adjacent lanes; its amax is a 1-3 step DPP
+//     butterfly (quad_perm, row_half_mirror) inside one 8-lane half row.
 //   - fp32 -> e4m3fn uses the hardware v_cvt_pk_fp8_f32 (round to nearest even), after
 //     the explicit clamp to +-448, so saturation never depends on the instruction.
 //   - masked (EP-MoE) dispatch: each block turns masked_m into a prefix sum in LDS and
@@ -33,8 +33,9 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = 64 * kWavesPerBlock;
-constexpr int kChunk = 512;     // elements per wave-wide chunk: 64 lanes x 8
-constexpr int kMaxChunks = 8;   // chunks per segment (unrolled)
+constexpr int kPerLane = 16;    // consecutive elements owned by one lane per chunk (32 B of bf16)
+constexpr int kChunk = 64 * kPerLane;  // elements per wave-wide chunk
+constexpr int kMaxChunks = 1;   // chunks per wave item (one: see launch_group_quant)
 constexpr float kFmax = 448.0f;
 constexpr float kEps = 0x1.b7cdfep-34f;  // 1e-10f, the amax floor
 
@@ -45,14 +46,13 @@ __device__ __forceinline__ float dpp(float v) {
                                                     0xF, 0xF, false));
 }
 
-// Max over the LANES (4, 8 or 16) adjacent lanes holding one group; every lane of the
+// Max over the LANES (2, 4 or 8) adjacent lanes holding one group; every lane of the
 // group receives the result. All 64 lanes must be active.
 template <int LANES>
 __device__ __forceinline__ float group_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));                    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp<0x4E>(v));                    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0xB1>(v));                              // quad_perm [1,0,3,2]
+  if constexpr (LANES >= 4) v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
   if constexpr (LANES >= 8) v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
-  if constexpr (LANES >= 16) v = fmaxf(v, dpp<0x140>(v));  // row_mirror
   return v;
 }
 
@@ -60,36 +60,38 @@ __device__ __forceinline__ float group_max(float v) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Raw storage of 8 consecutive input elements of one lane.
+// Raw storage of the 16 consecutive input elements of one lane (32 or 64 bytes).
 template <int DT>
-struct Raw8;
+struct Raw16;
 template <>
-struct Raw8<FP8Q_DTYPE_BF16> { u32x4 w; };
+struct Raw16<FP8Q_DTYPE_BF16> { u32x4 w[2]; };
 template <>
-struct Raw8<FP8Q_DTYPE_F16> { u32x4 w; };
+struct Raw16<FP8Q_DTYPE_F16> { u32x4 w[2]; };
 template <>
-struct Raw8<FP8Q_DTYPE_F32> { f32x4 lo, hi; };
+struct Raw16<FP8Q_DTYPE_F32> { f32x4 w[4]; };
 
-// Inputs are streamed once: non-temporal 16-byte loads.
+// Inputs are streamed once: non-temporal 16-byte loads of adjacent addresses.
 template <int DT>
-__device__ __forceinline__ void load_raw(const void* base, int64_t idx, Raw8<DT>& r) {
+__device__ __forceinline__ void load_raw(const void* base, int64_t idx, Raw16<DT>& r) {
   if constexpr (DT == FP8Q_DTYPE_F32) {
     const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
-    r.lo = __builtin_nontemporal_load(p);
-    r.hi = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+    for (int h = 0; h < 4; h++) r.w[h] = __builtin_nontemporal_load(p + h);
   } else {
     const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx);
-    r.w = __builtin_nontemporal_load(p);
+    r.w[0] = __builtin_nontemporal_load(p);
+    r.w[1] = __builtin_nontemporal_load(p + 1);
   }
 }
 
 template <int DT>
-__device__ __forceinline__ void zero_raw(Raw8<DT>& r) {
+__device__ __forceinline__ void zero_raw(Raw16<DT>& r) {
   if constexpr (DT == FP8Q_DTYPE_F32) {
-    r.lo = f32x4{0.f, 0.f, 0.f, 0.f};
-    r.hi = r.lo;
+#pragma unroll
+    for (int h = 0; h < 4; h++) r.w[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   } else {
-    r.w = u32x4{0u, 0u, 0u, 0u};
+    r.w[0] = u32x4{0u, 0u, 0u, 0u};
+    r.w[1] = r.w[0];
   }
 }
 
@@ -103,16 +105,27 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
 }
 
 template <int DT>
-__device__ __forceinline__ void widen(const Raw8<DT>& r, float (&v)[8]) {
+__device__ __forceinline__ void widen(const Raw16<DT>& r, float (&v)[16]) {
   if constexpr (DT == FP8Q_DTYPE_F32) {
-    v[0] = r.lo.x; v[1] = r.lo.y; v[2] = r.lo.z; v[3] = r.lo.w;
-    v[4] = r.hi.x; v[5] = r.hi.y; v[6] = r.hi.z; v[7] = r.hi.w;
-  } else if constexpr (DT == FP8Q_DTYPE_BF16) {
-    v[0] = bf16_lo(r.w.x); v[1] = bf16_hi(r.w.x); v[2] = bf16_lo(r.w.y); v[3] = bf16_hi(r.w.y);
-    v[4] = bf16_lo(r.w.z); v[5] = bf16_hi(r.w.z); v[6] = bf16_lo(r.w.w); v[7] = bf16_hi(r.w.w);
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      v[4 * h] = r.w[h].x; v[4 * h + 1] = r.w[h].y; v[4 * h + 2] = r.w[h].z; v[4 * h + 3] = r.w[h].w;
+    }
   } else {
-    v[0] = f16_lo(r.w.x); v[1] = f16_hi(r.w.x); v[2] = f16_lo(r.w.y); v[3] = f16_hi(r.w.y);
-    v[4] = f16_lo(r.w.z); v[5] = f16_hi(r.w.z); v[6] = f16_lo(r.w.w); v[7] = f16_hi(r.w.w);
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint32_t w = r.w[h][q];
+        if constexpr (DT == FP8Q_DTYPE_BF16) {
+          v[8 * h + 2 * q] = bf16_lo(w);
+          v[8 * h + 2 * q + 1] = bf16_hi(w);
+        } else {
+          v[8 * h + 2 * q] = f16_lo(w);
+          v[8 * h + 2 * q + 1] = f16_hi(w);
+        }
+      }
+    }
   }
 }
 
@@ -170,7 +183,7 @@ __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -kFma
 template <int DT, int G, int FMT, bool SILU>
 __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
   extern __shared__ int32_t lds_pref[];  // masked only: E+1 exclusive prefix + 256 partials
-  constexpr int LANES = G / 8;
+  constexpr int LANES = G / kPerLane;
   const int lane = threadIdx.x & 63;
   const bool masked = p.masked_m != nullptr;
 
@@ -236,14 +249,14 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
     const int nc = min(p.chunks_per_seg, p.chunks_per_row - c0);  // wave-uniform
 
     // issue every load of the segment first
-    Raw8<DT> ra[kMaxChunks];
-    Raw8<DT> rb[SILU ? kMaxChunks : 1];
+    Raw16<DT> ra[kMaxChunks];
+    Raw16<DT> rb[SILU ? kMaxChunks : 1];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; c++) {
       zero_raw<DT>(ra[c]);
       if constexpr (SILU) zero_raw<DT>(rb[c]);
       if (c < nc) {
-        const int64_t k = static_cast<int64_t>(c0 + c) * kChunk + lane * 8;
+        const int64_t k = static_cast<int64_t>(c0 + c) * kChunk + lane * kPerLane;
         if (k < p.K) {
           load_raw<DT>(p.x, xrow + k, ra[c]);
           if constexpr (SILU) load_raw<DT>(p.x, xrow + p.K + k, rb[c]);
@@ -253,28 +266,29 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
 #pragma unroll
     for (int c = 0; c < kMaxChunks; c++) {
       if (c < nc) {
-        const int64_t k = static_cast<int64_t>(c0 + c) * kChunk + lane * 8;
-        float v[8];
+        const int64_t k = static_cast<int64_t>(c0 + c) * kChunk + lane * kPerLane;
+        float v[16];
         widen<DT>(ra[c], v);
         if constexpr (SILU) {
-          float u[8];
+          float u[16];
           widen<DT>(rb[c], u);
 #pragma unroll
-          for (int j = 0; j < 8; j++) v[j] = silu_mul(v[j], u[j]);
+          for (int j = 0; j < 16; j++) v[j] = silu_mul(v[j], u[j]);
         }
         float amax = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(v[j]));
+        for (int j = 0; j < 16; j++) amax = fmaxf(amax, fabsf(v[j]));
         amax = group_max<LANES>(amax);  // all lanes active here
         amax = fmaxf(amax, kEps);
         uint32_t sbits;
         const float inv = group_multiplier<FMT>(amax, sbits);
         if (k < p.K) {
-          const uint32_t w0 = cvt4(clamp448(v[0] * inv), clamp448(v[1] * inv),
-                                   clamp448(v[2] * inv), clamp448(v[3] * inv));
-          const uint32_t w1 = cvt4(clamp448(v[4] * inv), clamp448(v[5] * inv),
-                                   clamp448(v[6] * inv), clamp448(v[7] * inv));
-          *reinterpret_cast<uint2*>(qrow + k) = make_uint2(w0, w1);
+          u32x4 w;
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            w[q] = cvt4(clamp448(v[4 * q] * inv), clamp448(v[4 * q + 1] * inv), clamp448(v[4 * q + 2] * inv),
+                        clamp448(v[4 * q + 3] * inv));
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(qrow + k));
           if ((lane & (LANES - 1)) == 0) {
             const int64_t sidx = srow + (k / G) * p.s_sg;
             if constexpr (FMT == FP8Q_SCALE_UE8M0)
@@ -314,28 +328,23 @@ void launch_g(int g, int fmt, bool silu, const QuantParams& p, int grid, size_t 
 
 }  // namespace
 
-// Picks the segment length (chunks per wave item) and the grid, then launches.
-// Rows are cut into segments of U chunks (U <= 8) with no partial segment when
-// possible; U shrinks when there are too few rows to give every wave slot work.
+// Picks the segment length and the grid, then launches. Measured on MI355X: one chunk per
+// wave item and one wave per item (as many waves as the problem has chunks) streams best;
+// the hardware's own wave scheduling keeps HBM busier than longer per-wave segments.
 int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, QuantParams p,
                        int64_t expected_m, hipStream_t stream) {
   const int chunks = static_cast<int>((p.K + kChunk - 1) / kChunk);
   int64_t rows_est = p.E * p.M;
   if (p.masked_m) rows_est = p.E * (expected_m > 0 ? std::min<int64_t>(expected_m, p.M) : p.M);
   if (rows_est < 1) rows_est = 1;
-  constexpr int64_t kTargetItems = 8192;  // wave slots on 256 CUs at 32 waves each
-  int U = 1;
-  for (int u = kMaxChunks; u >= 1; u--) {
-    if (chunks % u != 0 && u < chunks) continue;  // avoid partial segments
-    if (rows_est * ((chunks + u - 1) / u) >= kTargetItems || u == 1) { U = u; break; }
-  }
-  if (U > chunks) U = chunks;
-  p.chunks_per_seg = U;
+  p.chunks_per_seg = 1;
   p.chunks_per_row = chunks;
-  p.nseg = (chunks + U - 1) / U;
+  p.nseg = chunks;
   const int64_t items = rows_est * p.nseg;
   int64_t grid = (items + kWavesPerBlock - 1) / kWavesPerBlock;
-  grid = std::max<int64_t>(1, std::min<int64_t>(grid, 2048));
+  // masked launches rebuild the expert prefix sum in every block: cap the grid there so each
+  // wave walks several rows instead
+  grid = std::max<int64_t>(1, std::min<int64_t>(grid, p.masked_m ? 2048 : 65535));
   const size_t lds = p.masked_m ? static_cast<size_t>(p.E + 1 + kThreads) * sizeof(int32_t) : 0;
   switch (in_dtype) {
     case FP8Q_DTYPE_BF16: launch_g<FP8Q_DTYPE_BF16>(group_size, scale_fmt, silu, p, (int)grid, lds, stream); break;
