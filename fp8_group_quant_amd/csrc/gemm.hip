@@ -20,12 +20,17 @@
 //   - K layout inside a lane (measured on gfx950): lane l of a 16x16x128 operand holds row
 //     l%16 and two 16-byte runs of K, at 16*(l/16) and 64 + 16*(l/16); the E8M0 scale for
 //     (row i, 32-wide block b) comes from lane i + 16*b.
-//   - 256x256 output tiles, 8 wavefronts of 128(m) x 64(n), K step 128. Operand tiles move
-//     global -> LDS with global_load_lds_dwordx4 (no register staging), two LDS stages, the
-//     loads of step k+1 in flight while step k computes, one barrier per step. LDS rows are
+//   - 256x128 output tiles, 8 wavefronts of 64(m) x 64(n), K step 128. Operand tiles and
+//     scales move global -> registers -> LDS: each step's loads are issued two steps
+//     ahead into one of two register sets and written to one of two LDS stages after the
+//     step that last read it, with one barrier per step. (Direct global -> LDS loads
+//     were slower here: the compiler waits for every such load before any later LDS read,
+//     which serialises the next step's loads with the current step's MFMAs.) LDS rows are
 //     128 bytes with the 16-byte chunk index XOR-swizzled by (row/2)%8, which keeps the
 //     16 rows read by one fragment load on distinct banks without padding.
-//   - per-step scales are read straight from global memory into registers one step ahead.
+//   - BLOCK128 fold pipeline: the MFMAs of subtile row i are interleaved with the fold of
+//     row i-1 (the last row's fold moves into the next step), so no fold waits on the
+//     MFMA it consumes and the fold's VALU work co-issues with the matrix core.
 //   - persistent workgroups (one per CU); the tile list is split into 8 contiguous ranges,
 //     one per XCD (workgroup w runs on XCD w % 8), and dense tiles are ordered in groups of
 //     4 m-tiles so one XCD's tiles share operand rows in its L2. Masked grouped launches
@@ -63,11 +68,7 @@ using Large = TileCfg<256, 128, 4, 2, 4>;
 
 // One LDS stage: both operand tiles of one K step and the step's scales. Scales are
 // stored in the order the lanes read them: BLOCK128 sa as [wave row][lane%16][subtile]
-// floats; MX32 E8M0 bytes as [wave row][lane%16][K block][subtile]. The kernel declares
-// the two stages as separate __shared__ objects and each K step receives them through
-// __restrict__ pointers, so the compiler can see that the direct-to-LDS loads into one
-// stage never alias the fragment reads of the other (otherwise it waits for them before
-// every read).
+// floats; MX32 E8M0 bytes as [wave row][lane%16][K block][subtile].
 template <class C>
 struct Stage {
   alignas(16) uint8_t a[C::BM * BK];
@@ -163,9 +164,10 @@ __device__ __forceinline__ float scale_value(uint32_t raw) {
   if constexpr (FMT == FP8Q_SCALE_F32) {
     return __uint_as_float(raw);
   } else {
-    if (raw == 0u) return __uint_as_float(0x00400000u);  // 2^-127 (subnormal)
-    if (raw == 255u) return __uint_as_float(0x7FC00000u);
-    return __uint_as_float(raw << 23);
+    uint32_t bits = raw << 23;
+    bits = raw == 0u ? 0x00400000u : bits;    // 2^-127 (subnormal)
+    bits = raw == 255u ? 0x7FC00000u : bits;  // NaN
+    return __uint_as_float(bits);
   }
 }
 
@@ -253,6 +255,10 @@ struct TileRun {
   ScaleStage<C, MX, SA_FMT, SB_FMT> ss[2];
   TileRegs<C> tr[2];
   v4f acc[C::SM][C::SN];
+  // BLOCK128 fold pipeline: products of the two most recent subtile rows (row i in pr[i%2])
+  // and the factor of the last row of the previous step, whose fold is still pending.
+  v4f pr[2][C::SN];
+  float pend_s;
 
   __device__ __forceinline__ void issue(int q, int kb) {
     tr[q].load(A, p.lda, m0, rmax, B, p.ldb, n0, nmax, kb);
@@ -300,26 +306,31 @@ struct TileRun {
         xf = xn;
       }
     } else {
+      // Row i's MFMAs are interleaved with the fold of row i-1 (for i = 0, the previous
+      // step's last row), so no fold waits on the MFMA just issued.
+      static_assert(C::SM % 2 == 0, "row parity must repeat across steps");
       const float sbv = cu.sb[(wn * C::WTN) / 128];
       const float* psa = cu.sa + (wm * 16 + (lane & 15)) * C::SM;
+      float srow[C::SM];
+#pragma unroll
+      for (int i = 0; i < C::SM; i++) srow[i] = psa[i];
       v8i xf = frag(cu.a, wm * C::WTM, lane);
 #pragma unroll
       for (int i = 0; i < C::SM; i++) {
         const v8i xn = i + 1 < C::SM ? frag(cu.a, wm * C::WTM + (i + 1) * 16, lane) : xf;
-        const float s = psa[i] * sbv;
-        v4f pr[C::SN];
+        const int ip = i == 0 ? C::SM - 1 : i - 1;
+        const float sp = i == 0 ? pend_s : srow[i - 1] * sbv;
 #pragma unroll
         for (int j = 0; j < C::SN; j++) {
           const v4f z = {0.f, 0.f, 0.f, 0.f};
-          pr[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
-        }
+          pr[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < C::SN; j++) {
-#pragma unroll
-          for (int r = 0; r < 4; r++) acc[i][j][r] = fmaf(pr[j][r], s, acc[i][j][r]);
+          for (int r = 0; r < 4; r++) acc[ip][j][r] = fmaf(pr[(i + 1) & 1][j][r], sp, acc[ip][j][r]);
+          __builtin_amdgcn_sched_barrier(0);
         }
         xf = xn;
       }
+      pend_s = srow[C::SM - 1] * sbv;
     }
     if (kb + 1 < nkb) commit(1 - Q, nx);  // waits for set 1-Q only, not the loads just issued
   }
@@ -350,6 +361,9 @@ __device__ void run_tile(const GemmParams& p, Stage<C>& s0, Stage<C>& s1, const 
   for (int i = 0; i < C::SM; i++)
 #pragma unroll
     for (int j = 0; j < C::SN; j++) r.acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < C::SN; j++) r.pr[1][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  r.pend_s = 0.f;
 
   r.issue(0, 0);
   r.commit(0, s0);
@@ -357,6 +371,13 @@ __device__ void run_tile(const GemmParams& p, Stage<C>& s0, Stage<C>& s1, const 
   for (int kb = 0; kb < r.nkb; kb += 2) {
     r.template step<0>(s0, s1, kb);
     if (kb + 1 < r.nkb) r.template step<1>(s1, s0, kb + 1);
+  }
+  if constexpr (!MX) {  // the last row's fold is still pending
+#pragma unroll
+    for (int j = 0; j < C::SN; j++)
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        r.acc[C::SM - 1][j][q] = fmaf(r.pr[(C::SM - 1) & 1][j][q], r.pend_s, r.acc[C::SM - 1][j][q]);
   }
   __syncthreads();  // the next tile's first loads overwrite stage 0
   const int64_t m0 = r.m0, n0 = r.n0;
