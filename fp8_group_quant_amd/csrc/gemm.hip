@@ -20,14 +20,15 @@
 //   - K layout inside a lane (measured on gfx950): lane l of a 16x16x128 operand holds row
 //     l%16 and two 16-byte runs of K, at 16*(l/16) and 64 + 16*(l/16); the E8M0 scale for
 //     (row i, 32-wide block b) comes from lane i + 16*b.
-//   - 256x128 output tiles, 8 wavefronts of 64(m) x 64(n), K step 128. Operand tiles and
-//     scales move global -> registers -> LDS: each step's loads are issued two steps
-//     ahead into one of two register sets and written to one of two LDS stages after the
-//     step that last read it, with one barrier per step. (Direct global -> LDS loads
-//     were slower here: the compiler waits for every such load before any later LDS read,
-//     which serialises the next step's loads with the current step's MFMAs.) LDS rows are
-//     128 bytes with the 16-byte chunk index XOR-swizzled by (row/2)%8, which keeps the
-//     16 rows read by one fragment load on distinct banks without padding.
+//   - 256x128 output tiles, 8 wavefronts of 64(m) x 64(n), K step 128. LDS rows are 128
+//     bytes with the 16-byte chunk index XOR-swizzled by (row/2)%8, which keeps the 16
+//     rows read by one fragment load on distinct banks without padding.
+//   - Two ways to fill LDS. The main kernel loads operand tiles and scales straight into
+//     LDS (global_load_lds) through three stages with one barrier per step, so loads have
+//     two steps to land and the next step's first operands are read during the current
+//     step's last row (see "direct-to-LDS pipeline" below). Scale layouts it cannot move
+//     in aligned 4-byte pieces go to a register-staged kernel: loads issued two steps
+//     ahead into one of two register sets, written to one of two LDS stages.
 //   - BLOCK128 fold pipeline: the MFMAs of subtile row i are interleaved with the fold of
 //     row i-1 (the last row's fold moves into the next step), so no fold waits on the
 //     MFMA it consumes and the fold's VALU work co-issues with the matrix core.
@@ -408,86 +409,424 @@ __device__ void run_tile(const GemmParams& p, Stage<C>& s0, Stage<C>& s1, const 
   }
 }
 
+// Tile list of a launch. Dense: ceil(M/BM) x ceil(N/BN) tiles in grouped order (GROUP_M
+// m tiles share each sweep over n, so operand rows are reused from L2). Masked: the
+// valid tiles of each expert, found through an exclusive prefix of tile counts over the
+// experts that every workgroup builds in LDS (part: kThreads ints of scratch, pref: E + 1).
+template <class C>
+__device__ int64_t build_tile_list(const GemmParams& p, int32_t* part, int32_t* pref) {
+  const int tid = threadIdx.x;
+  const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
+  if (!p.masked_m) return ((p.M + C::BM - 1) / C::BM) * tiles_n;
+  const int E = static_cast<int>(p.E);
+  const int per = (E + C::kThreads - 1) / C::kThreads;
+  const int beg = min(tid * per, E), end = min(beg + per, E);
+  int32_t local = 0;
+  for (int i = beg; i < end; i++) {
+    int64_t r = p.masked_m[i];
+    r = r < 0 ? 0 : (r > p.M ? p.M : r);
+    local += static_cast<int32_t>(((r + C::BM - 1) / C::BM) * tiles_n);
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < C::kThreads; off <<= 1) {
+    const int32_t add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - local;
+  for (int i = beg; i < end; i++) {
+    pref[i] = run;
+    int64_t r = p.masked_m[i];
+    r = r < 0 ? 0 : (r > p.M ? p.M : r);
+    run += static_cast<int32_t>(((r + C::BM - 1) / C::BM) * tiles_n);
+  }
+  if (tid == C::kThreads - 1) pref[E] = part[C::kThreads - 1];
+  __syncthreads();
+  return pref[E];
+}
+
+template <class C>
+__device__ Tile tile_at(const GemmParams& p, const int32_t* pref, int64_t t) {
+  const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
+  Tile tile;
+  if (p.masked_m) {
+    int lo = 0, hi = static_cast<int>(p.E);  // pref[lo] <= t < pref[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pref[mid] <= t) lo = mid; else hi = mid;
+    }
+    int64_t r = p.masked_m[lo];
+    r = r < 0 ? 0 : (r > p.M ? p.M : r);
+    const int64_t tm_e = (r + C::BM - 1) / C::BM;
+    const int64_t local = t - pref[lo];
+    tile.e = lo;
+    tile.tm = local % tm_e;  // m tiles of one (expert, n tile) are adjacent
+    tile.tn = local / tm_e;
+    tile.rows = r;
+  } else {
+    const int64_t tiles_m = (p.M + C::BM - 1) / C::BM;
+    const int64_t in_group = C::GROUP_M * tiles_n;
+    const int64_t first_m = (t / in_group) * C::GROUP_M;
+    const int64_t gm = min(tiles_m - first_m, static_cast<int64_t>(C::GROUP_M));
+    tile.e = 0;
+    tile.tm = first_m + (t % in_group) % gm;
+    tile.tn = (t % in_group) / gm;
+    tile.rows = p.M;
+  }
+  return tile;
+}
+
+// XCD-contiguous split of the tile list: workgroup w runs on XCD w % 8 (the grid is a
+// multiple of 8), and each XCD takes one contiguous eighth of the list.
+struct TileRange {
+  int64_t beg, end, stride;
+  __device__ TileRange(int64_t T) {
+    const int64_t xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nslots = gridDim.x / kXcds;
+    beg = (xcd * T) / kXcds + slot;
+    end = ((xcd + 1) * T) / kXcds;
+    stride = nslots;
+  }
+};
+
 template <class C, bool MX, int SA_FMT, int SB_FMT>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   __shared__ Stage<C> stage0;
   __shared__ Stage<C> stage1;
   __shared__ int32_t part[C::kThreads];
-  extern __shared__ int32_t pref[];  // masked only, E + 1 entries: exclusive prefix of tiles
-  const int tid = threadIdx.x;
-  const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
-  const bool masked = p.masked_m != nullptr;
+  extern __shared__ int32_t pref[];  // masked only, E + 1 entries
+  const TileRange tr(build_tile_list<C>(p, part, pref));
+  for (int64_t t = tr.beg; t < tr.end; t += tr.stride)
+    run_tile<C, MX, SA_FMT, SB_FMT>(p, stage0, stage1, tile_at<C>(p, pref, t));
+}
 
-  int64_t T;
-  if (masked) {
-    const int E = static_cast<int>(p.E);
-    const int per = (E + C::kThreads - 1) / C::kThreads;
-    const int beg = min(tid * per, E), end = min(beg + per, E);
-    int32_t local = 0;
-    for (int i = beg; i < end; i++) {
-      int64_t r = p.masked_m[i];
-      r = r < 0 ? 0 : (r > p.M ? p.M : r);
-      local += static_cast<int32_t>(((r + C::BM - 1) / C::BM) * tiles_n);
-    }
-    part[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < C::kThreads; off <<= 1) {
-      const int32_t add = tid >= off ? part[tid - off] : 0;
-      __syncthreads();
-      part[tid] += add;
-      __syncthreads();
-    }
-    int32_t run = part[tid] - local;
-    for (int i = beg; i < end; i++) {
-      pref[i] = run;
-      int64_t r = p.masked_m[i];
-      r = r < 0 ? 0 : (r > p.M ? p.M : r);
-      run += static_cast<int32_t>(((r + C::BM - 1) / C::BM) * tiles_n);
-    }
-    if (tid == C::kThreads - 1) pref[E] = part[C::kThreads - 1];
-    __syncthreads();
-    T = pref[E];
-  } else {
-    T = ((p.M + C::BM - 1) / C::BM) * tiles_n;
+// ------------------------------------------------------------------ direct-to-LDS pipeline
+// The same 256x128 tiles and 8 wavefronts of 64x64, but operand tiles and scales travel
+// global -> LDS with global_load_lds (no register staging), through three LDS stages:
+// while step kb computes from stage kb%3, stage (kb+1)%3 holds step kb+1 and stage
+// (kb+2)%3 is being filled. The one barrier of a step sits before its last subtile row:
+// by then every wavefront has read what it needs of stage kb%3 and has seen its own loads
+// of step kb+1 land, so after the barrier step kb+3 is loaded into stage kb%3 and the
+// first operands of step kb+1 are read into registers while the last row's MFMAs run.
+// A load therefore has two steps to land.
+//
+// The loads are written as inline assembly so that the compiler, which cannot tell LDS
+// stages apart, does not wait for them before unrelated LDS reads; the waits are explicit
+// (s_waitcnt vmcnt) and the K loop contains no other vector-memory instruction, so the
+// counts are exact. M0 holds the LDS destination of each load; nothing else in these
+// kernels uses M0.
+//
+// Scales reach LDS the same way, which limits this path to scale layouts that can be
+// moved in aligned 4-byte pieces: fp32 activation scales (any strides), UE8M0 activation
+// scales stored column-major ([K/128][M], M a multiple of 4), fp32 weight-block scales,
+// and MX32 E8M0 bytes stored [rows][K/32] with rows a multiple of 4 bytes apart. Other
+// layouts use the register-staged kernel above.
+enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2 };
+
+constexpr int kDmaStage = 256 * BK + 128 * BK + 1792;  // A tile, B tile, scales (+ a spare word per lane)
+constexpr int kDmaScOff = 256 * BK + 128 * BK;
+constexpr int kDmaStages = 3;
+constexpr int kDmaMaxPrefix = 2048;  // masked launches: at most this many experts
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)p));
+}
+
+// lane l: LDS [lds + 16 l, +16) <- global [base + voff, +16)
+__device__ __forceinline__ void dma16(uint32_t lds, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+// lane l: LDS [lds + 4 l, +4) <- global [base + voff, +4)
+__device__ __forceinline__ void dma4(uint32_t lds, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Per-tile state of the direct-to-LDS loop (C = Large: 256x128, 8 waves of 64x64).
+template <int SCM>
+struct DmaRun {
+  using C = Large;
+  static constexpr bool MX = SCM == kScMx;
+  static constexpr int SM = C::SM, SN = C::SN;
+  static_assert(SM == 4 && SN == 4, "this loop is written for 4x4 subtiles per wave");
+
+  const GemmParams& p;
+  uint8_t* smem;       // three stages
+  uint32_t smem_lds;   // LDS address of smem
+  int nkb, lane, wave, wm, wn;
+  // per-step global bases (uniform) and per-lane offsets of this wave's loads
+  const uint8_t* a_base;  // A + m0*lda (step kb adds kb*128)
+  const uint8_t* b_base;  // B + n0*ldb
+  uint32_t a_off[4], b_off[2];
+  // This wave's scale load: every wave issues one per step (those without a scale to
+  // move load 4 bytes of A into a spare area), so each step's group is exactly 7 loads.
+  const uint8_t* s_base;
+  uint32_t s_off;
+  int64_t s_step;         // bytes per K step
+  uint32_t s_lds;         // offset of its destination inside a stage
+  // operands of the current step
+  v8i wf[SN];
+  v8i x0, x1;
+  float sa[SM], sb;
+  uint32_t ea[SM], eb[SN];
+  v4f acc[SM][SN];
+  v4f pr[2][SN];
+  float pend_s;
+
+  // Loads of step kb into stage st: the wave's scale load, then 4 A and 2 B blocks.
+  static constexpr int kGroup = 7;
+  __device__ __forceinline__ void issue(int st, int kb) {
+    const uint32_t base = smem_lds + st * kDmaStage;
+    dma4(base + s_lds, s_base + kb * s_step, s_off);
+    const uint8_t* ap = a_base + kb * BK;
+#pragma unroll
+    for (int q = 0; q < 4; q++) dma16(base + (wave * 4 + q) * 1024, ap, a_off[q]);
+    const uint8_t* bp = b_base + kb * BK;
+#pragma unroll
+    for (int q = 0; q < 2; q++) dma16(base + 256 * BK + (wave * 2 + q) * 1024, bp, b_off[q]);
   }
 
-  // XCD-contiguous split of the tile list: workgroup w runs on XCD w % 8.
-  const int64_t G = gridDim.x;  // a multiple of 8
-  const int64_t xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nslots = G / kXcds;
-  const int64_t t_beg = (xcd * T) / kXcds, t_end = ((xcd + 1) * T) / kXcds;
-  const int64_t tiles_m = (p.M + C::BM - 1) / C::BM;
+  __device__ __forceinline__ const uint8_t* stage(int st) const { return smem + st * kDmaStage; }
 
-  for (int64_t t = t_beg + slot; t < t_end; t += nslots) {
-    Tile tile;
-    if (masked) {
-      int lo = 0, hi = static_cast<int>(p.E);  // pref[lo] <= t < pref[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pref[mid] <= t) lo = mid; else hi = mid;
-      }
-      int64_t r = p.masked_m[lo];
-      r = r < 0 ? 0 : (r > p.M ? p.M : r);
-      const int64_t tm_e = (r + C::BM - 1) / C::BM;
-      const int64_t local = t - pref[lo];
-      tile.e = lo;
-      tile.tm = local % tm_e;  // m tiles of one (expert, n tile) are adjacent
-      tile.tn = local / tm_e;
-      tile.rows = r;
+  __device__ __forceinline__ void load_scales(int st) {
+    const uint8_t* sc = stage(st) + kDmaScOff;
+    if constexpr (MX) {
+#pragma unroll
+      for (int i = 0; i < SM; i++) ea[i] = sc[4 * (wm * 64 + i * 16 + (lane & 15)) + (lane >> 4)];
+#pragma unroll
+      for (int j = 0; j < SN; j++) eb[j] = sc[1024 + 4 * (wn * 64 + j * 16 + (lane & 15)) + (lane >> 4)];
     } else {
-      // grouped order: GROUP_M m tiles share each sweep over n, so rows are reused from L2
-      const int64_t in_group = C::GROUP_M * tiles_n;
-      const int64_t g = t / in_group;
-      const int64_t first_m = g * C::GROUP_M;
-      const int64_t gm = min(tiles_m - first_m, static_cast<int64_t>(C::GROUP_M));
-      tile.e = 0;
-      tile.tm = first_m + (t % in_group) % gm;
-      tile.tn = (t % in_group) / gm;
-      tile.rows = p.M;
+#pragma unroll
+      for (int i = 0; i < SM; i++) {
+        const int row = wm * 64 + i * 16 + (lane & 15);
+        if constexpr (SCM == kScF32Row)
+          sa[i] = reinterpret_cast<const float*>(sc)[row];
+        else
+          sa[i] = scale_value<FP8Q_SCALE_UE8M0>(sc[row]);
+      }
+      sb = reinterpret_cast<const float*>(sc + 1024)[0];
     }
-    run_tile<C, MX, SA_FMT, SB_FMT>(p, stage0, stage1, tile);
+  }
+
+  // First operands of the step held in stage st.
+  __device__ __forceinline__ void load_ops(int st) {
+    const uint8_t* s = stage(st);
+#pragma unroll
+    for (int j = 0; j < SN; j++) wf[j] = frag(s + 256 * BK, wn * 64 + j * 16, lane);
+    x0 = frag(s, wm * 64, lane);
+    x1 = frag(s, wm * 64 + 16, lane);
+    load_scales(st);
+  }
+
+  // Subtile row i: its MFMAs interleaved with the fold of row i-1 (for i = 0, the
+  // previous step's last row). With NXT >= 0, weight fragment j of the next step is read
+  // from stage NXT right after the last MFMA that uses the current one.
+  template <int NXT>
+  __device__ __forceinline__ void row(int i, const v8i& xf, float sp) {
+    const int ip = i == 0 ? SM - 1 : i - 1;
+#pragma unroll
+    for (int j = 0; j < SN; j++) {
+      if constexpr (MX) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 0, 0, 0,
+                                                                     static_cast<int>(eb[j]), 0,
+                                                                     static_cast<int>(ea[i]));
+      } else {
+        const v4f z = {0.f, 0.f, 0.f, 0.f};
+        pr[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[ip][j][r] = fmaf(pr[(i + 1) & 1][j][r], sp, acc[ip][j][r]);
+      }
+      if constexpr (NXT >= 0) wf[j] = frag(stage(NXT) + 256 * BK, wn * 64 + j * 16, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // K step kb computed from stage S.
+  template <int S>
+  __device__ __forceinline__ void step(int kb) {
+    constexpr int NX = (S + 1) % kDmaStages;
+    const uint8_t* cu = stage(S);
+    float srow[SM], sbv = 0.f;
+    if constexpr (!MX) {
+#pragma unroll
+      for (int i = 0; i < SM; i++) srow[i] = sa[i];
+      sbv = sb;
+    }
+    v8i x2 = frag(cu, wm * 64 + 32, lane);
+    row<-1>(0, x0, pend_s);
+    v8i x3 = frag(cu, wm * 64 + 48, lane);
+    row<-1>(1, x1, srow[0] * sbv);
+    row<-1>(2, x2, srow[1] * sbv);
+    // Every load of step kb+1 by this wave has landed (only step kb+2's group, issued
+    // later, may still be in flight), and its reads of stage S are done.
+    wait_vmcnt<kGroup>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // Past the end the step index is clamped: the stage it fills is never read again,
+    // and every step keeps the same load count and no branch.
+    issue(S, min(kb + 3, nkb - 1));
+    row<NX>(3, x3, srow[2] * sbv);
+    x0 = frag(stage(NX), wm * 64, lane);
+    x1 = frag(stage(NX), wm * 64 + 16, lane);
+    load_scales(NX);
+    if constexpr (!MX) pend_s = srow[3] * sbv;
+  }
+};
+
+template <int SCM>
+__device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) {
+  using C = Large;
+  DmaRun<SCM> r{p};
+  r.smem = smem;
+  r.smem_lds = lds_addr(smem);
+  r.lane = threadIdx.x & 63;
+  r.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  r.wm = r.wave % C::WAVES_M;
+  r.wn = r.wave / C::WAVES_M;
+  r.nkb = static_cast<int>(p.K / BK);
+  const int lane = r.lane, wave = r.wave;
+  const int64_t m0 = t.tm * C::BM, n0 = t.tn * C::BN;
+  const int64_t rmax = t.rows - 1, nmax = p.N - 1;
+  const uint8_t* A = p.a + t.e * p.a_se;
+  const uint8_t* B = p.b + t.e * p.b_se;
+  r.a_base = A + m0 * p.lda;
+  r.b_base = B + n0 * p.ldb;
+  // lane l of a 1 KB block: tile row blk*8 + l/8, LDS chunk l%8 = logical chunk ^ swz(row)
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int row = (wave * 4 + q) * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
+    r.a_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.lda + c * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int row = (wave * 2 + q) * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
+    r.b_off[q] = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.ldb + c * 16);
+  }
+  // this wave's scale load (default: 4 bytes of A into the spare area)
+  r.s_base = r.a_base;
+  r.s_off = 0;
+  r.s_step = 0;
+  r.s_lds = kDmaScOff + 1536;
+  if constexpr (SCM == kScF32Row) {
+    const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
+    if (wave < 4) {  // 4 bytes of tile row wave*64 + lane
+      const int row = wave * 64 + lane;
+      r.s_base = SA + m0 * p.sa_sm * 4;
+      r.s_off = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
+      r.s_step = p.sa_sk * 4;
+      r.s_lds = kDmaScOff + wave * 256;
+    }
+  } else if constexpr (SCM == kScE8Col) {
+    const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se;
+    if (wave == 0) {  // the 4 bytes of tile rows 4*lane .. 4*lane + 3 (clamped to the last full word)
+      r.s_base = SA + m0;
+      r.s_off = static_cast<uint32_t>(min(m0 + 4 * lane, p.M - 4) - m0);
+      r.s_step = p.sa_sk;
+      r.s_lds = kDmaScOff;
+    }
+  } else {
+    const uint8_t* SA = static_cast<const uint8_t*>(p.sa);
+    const uint8_t* SB = static_cast<const uint8_t*>(p.sb);
+    if (wave < 4) {  // E8M0 word (K blocks 4kb..4kb+3) of A row wave*64 + lane
+      const int row = wave * 64 + lane;
+      r.s_base = SA + m0 * p.sa_sm;
+      r.s_off = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm);
+      r.s_step = 4;
+      r.s_lds = kDmaScOff + wave * 256;
+    } else if (wave < 6) {  // and of B row (wave-4)*64 + lane
+      const int row = (wave - 4) * 64 + lane;
+      r.s_base = SB + n0 * p.sb_sn;
+      r.s_off = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.sb_sn);
+      r.s_step = 4;
+      r.s_lds = kDmaScOff + 1024 + (wave - 4) * 256;
+    }
+  }
+  if constexpr (SCM != kScMx) {
+    // the weight-block scale, one fp32 word per step (every lane loads it; the word
+    // lands 64 times in [1024, 1280) of the scale area)
+    if (wave == (SCM == kScF32Row ? 4 : 1)) {
+      const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
+      r.s_base = SB + (n0 / 128) * p.sb_sn * 4;
+      r.s_off = 0;
+      r.s_step = p.sb_sk * 4;
+      r.s_lds = kDmaScOff + 1024;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::SM; i++)
+#pragma unroll
+    for (int j = 0; j < C::SN; j++) r.acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < C::SN; j++) r.pr[1][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  r.pend_s = 0.f;
+
+  const int nkb = r.nkb;
+  r.issue(0, 0);
+  r.issue(1, min(1, nkb - 1));
+  r.issue(2, min(2, nkb - 1));
+  wait_vmcnt<2 * DmaRun<SCM>::kGroup>();  // step 0 has landed; steps 1 and 2 may be in flight
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  r.load_ops(0);
+  for (int kb = 0; kb < nkb; kb += 3) {
+    r.template step<0>(kb);
+    if (kb + 1 < nkb) r.template step<1>(kb + 1);
+    if (kb + 2 < nkb) r.template step<2>(kb + 2);
+  }
+  if constexpr (SCM != kScMx) {  // the last row's fold is still pending
+#pragma unroll
+    for (int j = 0; j < C::SN; j++)
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        r.acc[C::SM - 1][j][q] = fmaf(r.pr[(C::SM - 1) & 1][j][q], r.pend_s, r.acc[C::SM - 1][j][q]);
+  }
+  // no load is in flight and nobody reads a stage any more before the next tile's loads
+  wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // epilogue: lane holds Y[m][n..n+3], m = m0+wm*64+i*16+lane%16, n = n0+wn*64+j*16+4*(lane/16)
+  uint16_t* Y = p.y + t.e * p.y_se;
+  const int wm = r.wm, wn = r.wn;
+#pragma unroll
+  for (int i = 0; i < C::SM; i++) {
+    const int64_t m = m0 + wm * C::WTM + i * 16 + (lane & 15);
+    if (m >= t.rows) continue;
+    uint16_t* yrow = Y + m * p.ldy;
+#pragma unroll
+    for (int j = 0; j < C::SN; j++) {
+      const int64_t n = n0 + wn * C::WTN + j * 16 + 4 * (lane >> 4);
+      const uint32_t h0 = bf16_rne(r.acc[i][j][0]), h1 = bf16_rne(r.acc[i][j][1]);
+      const uint32_t h2 = bf16_rne(r.acc[i][j][2]), h3 = bf16_rne(r.acc[i][j][3]);
+      if (n + 3 < p.N) {
+        *reinterpret_cast<uint32_t*>(yrow + n) = h0 | (h1 << 16);
+        *reinterpret_cast<uint32_t*>(yrow + n + 2) = h2 | (h3 << 16);
+      } else {
+        if (n < p.N) yrow[n] = static_cast<uint16_t>(h0);
+        if (n + 1 < p.N) yrow[n + 1] = static_cast<uint16_t>(h1);
+        if (n + 2 < p.N) yrow[n + 2] = static_cast<uint16_t>(h2);
+      }
+    }
   }
 }
 
+template <int SCM>
+__global__ __launch_bounds__(Large::kThreads, 1) void gemm_dma_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kDmaStages * kDmaStage];
+  __shared__ int32_t pref[kDmaMaxPrefix + 1];  // masked only, E + 1 entries
+  int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch, used before any load
+  const TileRange tr(build_tile_list<Large>(p, part, pref));
+  for (int64_t t = tr.beg; t < tr.end; t += tr.stride) run_tile_dma<SCM>(p, smem, tile_at<Large>(p, pref, t));
+}
 
 // ------------------------------------------------------------------ skinny GEMM (small M)
 // For M <= 128 the product is bound by streaming B (the weights) from HBM, and 256x128
@@ -628,6 +967,30 @@ int finish(const char* what) {
   return FP8Q_OK;
 }
 
+// Whether the direct-to-LDS kernel can move this problem's scales (see its description),
+// and with which scale mode; -1 selects the register-staged kernel.
+bool u32_ok(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+int dma_mode(const GemmParams& p, bool mx) {
+  if (p.lda >= (int64_t(1) << 24) || p.ldb >= (int64_t(1) << 24)) return -1;
+  if (p.masked_m && p.E > kDmaMaxPrefix) return -1;
+  if (mx) {
+    const bool ok = p.sa_sk == 1 && p.sb_sk == 1 && p.sa_sm % 4 == 0 && p.sb_sn % 4 == 0 && u32_ok(p.sa) &&
+                    u32_ok(p.sb) && p.sa_sm < (int64_t(1) << 24) && p.sb_sn < (int64_t(1) << 24);
+    return ok ? kScMx : -1;
+  }
+  if (p.sb_fmt != FP8Q_SCALE_F32) return -1;
+  if (p.sa_fmt == FP8Q_SCALE_F32) return p.sa_sm < (int64_t(1) << 22) ? kScF32Row : -1;
+  const bool col = p.sa_sm == 1 && p.sa_sk % 4 == 0 && p.M % 4 == 0 && u32_ok(p.sa) &&
+                   (p.masked_m == nullptr || p.sa_se % 4 == 0);
+  return col ? kScE8Col : -1;
+}
+
+template <int SCM>
+void launch_dma(const GemmParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_dma_kernel<SCM>), dim3(grid), dim3(Large::kThreads), 0, s, p);
+}
+
 }  // namespace
 
 int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t stream) {
@@ -649,7 +1012,10 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
     else launch_skinny_m<FP8Q_SCALE_F32, FP8Q_SCALE_F32>(p, stream);
     return finish("block-scaled GEMM launch");
   }
-  if (a8 && b8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid, stream);
+  const int dm = dma_mode(p, false);
+  if (dm == kScF32Row) launch_dma<kScF32Row>(p, grid, stream);
+  else if (dm == kScE8Col) launch_dma<kScE8Col>(p, grid, stream);
+  else if (a8 && b8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid, stream);
   else if (a8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, grid, stream);
   else if (b8) launch<C, false, FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, grid, stream);
   else launch<C, false, FP8Q_SCALE_F32, FP8Q_SCALE_F32>(p, grid, stream);
@@ -659,7 +1025,8 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
 int launch_gemm_mx32(const GemmParams& p, hipStream_t stream) {
   using C = Large;
   const int64_t tiles = ((p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN);
-  launch<C, true, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid_for(tiles), stream);
+  if (dma_mode(p, true) == kScMx) launch_dma<kScMx>(p, grid_for(tiles), stream);
+  else launch<C, true, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid_for(tiles), stream);
   return finish("MXFP8 GEMM launch");
 }
 

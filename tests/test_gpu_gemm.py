@@ -67,8 +67,12 @@ def test_tiny_workload_full():
     check(y, ys, ss, w.K, "tiny")
 
 
+# M > 128 with M % 4 == 0 reaches the direct-to-LDS kernel for fp32 weight scales (also
+# with UE8M0 column-major activation scales); M % 4 != 0 or UE8M0 weight scales take the
+# register-staged kernel; K = 128 and 256 cover pipelines shorter than their depth.
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 130, 256), (129, 200, 384), (257, 300, 640),
-                                   (64, 1024, 1024)])
+                                   (64, 1024, 1024), (132, 136, 128), (264, 128, 256),
+                                   (260, 300, 640), (516, 136, 384)])
 @pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col"])
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
 def test_ragged_shapes_full(M, N, K, sa_kind, sb_kind):
