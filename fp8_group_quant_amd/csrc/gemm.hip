@@ -629,14 +629,15 @@ struct DmaRun {
   // previous step's last row). With NXT >= 0, weight fragment j of the next step is read
   // from stage NXT right after the last MFMA that uses the current one.
   template <int NXT>
-  __device__ __forceinline__ void row(int i, const v8i& xf, float sp) {
+  __device__ __forceinline__ void row(int i, const v8i& xf, float sp, const uint32_t (&eas)[SM],
+                                      const uint32_t (&ebs)[SN]) {
     const int ip = i == 0 ? SM - 1 : i - 1;
 #pragma unroll
     for (int j = 0; j < SN; j++) {
       if constexpr (MX) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 0, 0, 0,
-                                                                     static_cast<int>(eb[j]), 0,
-                                                                     static_cast<int>(ea[i]));
+                                                                     static_cast<int>(ebs[j]), 0,
+                                                                     static_cast<int>(eas[i]));
       } else {
         const v4f z = {0.f, 0.f, 0.f, 0.f};
         pr[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
@@ -660,10 +661,10 @@ struct DmaRun {
       sbv = sb;
     }
     v8i x2 = frag(cu, wm * 64 + 32, lane);
-    row<-1>(0, x0, pend_s);
+    row<-1>(0, x0, pend_s, ea, eb);
     v8i x3 = frag(cu, wm * 64 + 48, lane);
-    row<-1>(1, x1, srow[0] * sbv);
-    row<-1>(2, x2, srow[1] * sbv);
+    row<-1>(1, x1, srow[0] * sbv, ea, eb);
+    row<-1>(2, x2, srow[1] * sbv, ea, eb);
     // Every load of step kb+1 by this wave has landed (only step kb+2's group, issued
     // later, may still be in flight), and its reads of stage S are done.
     wait_vmcnt<kGroup>();
@@ -673,10 +674,20 @@ struct DmaRun {
     // Past the end the step index is clamped: the stage it fills is never read again,
     // and every step keeps the same load count and no branch.
     issue(S, min(kb + 3, nkb - 1));
-    row<NX>(3, x3, srow[2] * sbv);
+    // the next step's first activation fragments and scales go into registers freed by
+    // rows 0 and 1, so they are in flight during the whole last row
+    uint32_t ea_c[SM], eb_c[SN];
+    if constexpr (MX) {
+#pragma unroll
+      for (int i = 0; i < SM; i++) ea_c[i] = ea[i];
+#pragma unroll
+      for (int j = 0; j < SN; j++) eb_c[j] = eb[j];
+    }
     x0 = frag(stage(NX), wm * 64, lane);
     x1 = frag(stage(NX), wm * 64 + 16, lane);
     load_scales(NX);
+    __builtin_amdgcn_sched_barrier(0);
+    row<NX>(3, x3, srow[2] * sbv, ea_c, eb_c);
     if constexpr (!MX) pend_s = srow[3] * sbv;
   }
 };
