@@ -38,6 +38,8 @@
 //     build the tile list on device from masked_m, so the work scales with the valid rows.
 #include "fp8q_internal.h"
 
+#include <utility>
+
 #pragma clang fp contract(off)
 
 namespace fp8q {
@@ -549,48 +551,59 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Per-tile state of the direct-to-LDS loop (C = Large: 256x128, 8 waves of 64x64).
-template <int SCM>
+// Tile shape of the direct-to-LDS kernel: 256x128 outputs per workgroup, 8 wave tiles of
+// 64(m) x 64(n). (One wavefront per SIMD with 128x64 wave tiles reads 25% less from LDS
+// but measured slower here: no second wavefront covers a stall.)
+using DmaCfg = TileCfg<256, 128, 4, 2, 4>;
+
+// Per-tile state of the direct-to-LDS loop.
+template <class C, int SCM>
 struct DmaRun {
-  using C = Large;
   static constexpr bool MX = SCM == kScMx;
   static constexpr int SM = C::SM, SN = C::SN;
-  static_assert(SM == 4 && SN == 4, "this loop is written for 4x4 subtiles per wave");
+  static_assert(C::BM == 256 && C::BN == 128 && SN == 4 && C::WTN == 64, "256x128 tiles, 64-wide wave tiles");
+  static constexpr int kW = C::kWaves;
+  static constexpr int kLA = (C::BM / 8) / kW, kLB = (C::BN / 8) / kW;  // 1 KB blocks per wave
+  static constexpr int kSc = 8 / kW;                                   // scale jobs per wave
+  // loads per wave and step: tile blocks, then scale jobs
+  static constexpr int kGroup = kLA + kLB + kSc;
+  static constexpr int kPerStep = 4 * SM;  // MFMAs per wave and step
 
   const GemmParams& p;
   uint8_t* smem;       // three stages
   uint32_t smem_lds;   // LDS address of smem
   int nkb, lane, wave, wm, wn;
-  // per-step global bases (uniform) and per-lane offsets of this wave's loads
   const uint8_t* a_base;  // A + m0*lda (step kb adds kb*128)
   const uint8_t* b_base;  // B + n0*ldb
-  uint32_t a_off[4], b_off[2];
-  // This wave's scale load: every wave issues one per step (those without a scale to
-  // move load 4 bytes of A into a spare area), so each step's group is exactly 7 loads.
-  const uint8_t* s_base;
-  uint32_t s_off;
-  int64_t s_step;         // bytes per K step
-  uint32_t s_lds;         // offset of its destination inside a stage
+  uint32_t a_off[kLA], b_off[kLB];
+  // Scale jobs: 8 per step across the workgroup (see run_tile_dma); those without a scale
+  // to move load 4 bytes of A into a spare area, so every wave issues kGroup loads.
+  const uint8_t* s_base[kSc];
+  uint32_t s_off[kSc];
+  int64_t s_step[kSc];
+  uint32_t s_lds[kSc];
   // operands of the current step
   v8i wf[SN];
   v8i x0, x1;
   float sa[SM], sb;
   uint32_t ea[SM], eb[SN];
   v4f acc[SM][SN];
-  v4f pr[2][SN];
+  // BLOCK128 fold pipeline: the product of MFMA g (counted across steps) sits in
+  // pr[g % 3] and is folded two MFMAs later; the last two of a step are folded at the
+  // start of the next one with that step's last-row factor pend_s.
+  v4f pr[3];
   float pend_s;
 
-  // Loads of step kb into stage st: the wave's scale load, then 4 A and 2 B blocks.
-  static constexpr int kGroup = 7;
   __device__ __forceinline__ void issue(int st, int kb) {
     const uint32_t base = smem_lds + st * kDmaStage;
-    dma4(base + s_lds, s_base + kb * s_step, s_off);
     const uint8_t* ap = a_base + kb * BK;
 #pragma unroll
-    for (int q = 0; q < 4; q++) dma16(base + (wave * 4 + q) * 1024, ap, a_off[q]);
+    for (int q = 0; q < kLA; q++) dma16(base + (wave * kLA + q) * 1024, ap, a_off[q]);
     const uint8_t* bp = b_base + kb * BK;
 #pragma unroll
-    for (int q = 0; q < 2; q++) dma16(base + 256 * BK + (wave * 2 + q) * 1024, bp, b_off[q]);
+    for (int q = 0; q < kLB; q++) dma16(base + 256 * BK + (wave * kLB + q) * 1024, bp, b_off[q]);
+#pragma unroll
+    for (int q = 0; q < kSc; q++) dma4(base + kDmaScOff + s_lds[q], s_base[q] + kb * s_step[q], s_off[q]);
   }
 
   __device__ __forceinline__ const uint8_t* stage(int st) const { return smem + st * kDmaStage; }
@@ -599,13 +612,13 @@ struct DmaRun {
     const uint8_t* sc = stage(st) + kDmaScOff;
     if constexpr (MX) {
 #pragma unroll
-      for (int i = 0; i < SM; i++) ea[i] = sc[4 * (wm * 64 + i * 16 + (lane & 15)) + (lane >> 4)];
+      for (int i = 0; i < SM; i++) ea[i] = sc[4 * (wm * C::WTM + i * 16 + (lane & 15)) + (lane >> 4)];
 #pragma unroll
       for (int j = 0; j < SN; j++) eb[j] = sc[1024 + 4 * (wn * 64 + j * 16 + (lane & 15)) + (lane >> 4)];
     } else {
 #pragma unroll
       for (int i = 0; i < SM; i++) {
-        const int row = wm * 64 + i * 16 + (lane & 15);
+        const int row = wm * C::WTM + i * 16 + (lane & 15);
         if constexpr (SCM == kScF32Row)
           sa[i] = reinterpret_cast<const float*>(sc)[row];
         else
@@ -620,51 +633,81 @@ struct DmaRun {
     const uint8_t* s = stage(st);
 #pragma unroll
     for (int j = 0; j < SN; j++) wf[j] = frag(s + 256 * BK, wn * 64 + j * 16, lane);
-    x0 = frag(s, wm * 64, lane);
-    x1 = frag(s, wm * 64 + 16, lane);
+    x0 = frag(s, wm * C::WTM, lane);
+    x1 = frag(s, wm * C::WTM + 16, lane);
     load_scales(st);
   }
 
-  // Subtile row i: its MFMAs interleaved with the fold of row i-1 (for i = 0, the
-  // previous step's last row). With NXT >= 0, weight fragment j of the next step is read
-  // from stage NXT right after the last MFMA that uses the current one.
-  template <int NXT>
-  __device__ __forceinline__ void row(int i, const v8i& xf, float sp, const uint32_t (&eas)[SM],
-                                      const uint32_t (&ebs)[SN]) {
-    const int ip = i == 0 ? SM - 1 : i - 1;
+  // MFMA t = 4i + j of the step computed from stage S, then (BLOCK128) the fold of MFMA
+  // t-2 (for t < 2: the previous step's last two) with factor f[] of its row. With
+  // NXT >= 0, weight fragment j of the next step is read from stage NXT right after it.
+  template <int S, int NXT, int T>
+  __device__ __forceinline__ void mf(const v8i& xf, const float (&f)[SM], const uint32_t (&eas)[SM],
+                                     const uint32_t (&ebs)[SN]) {
+    constexpr int i = T / 4, j = T % 4;
+    if constexpr (MX) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 0, 0, 0,
+                                                                   static_cast<int>(ebs[j]), 0,
+                                                                   static_cast<int>(eas[i]));
+    } else {
+      constexpr int g = kPerStep * S + T;  // MFMA index mod 3 (steps of stage S are kb = S mod 3)
+      constexpr int slot = g % 3, pslot = (g + 1) % 3;
+      constexpr int ip = T >= 2 ? (T - 2) / 4 : SM - 1;
+      constexpr int jp = T >= 2 ? (T - 2) % 4 : T + 2;
+      const float sp = T >= 2 ? f[ip] : pend_s;
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+      pr[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < SN; j++) {
-      if constexpr (MX) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 0, 0, 0,
-                                                                     static_cast<int>(ebs[j]), 0,
-                                                                     static_cast<int>(eas[i]));
-      } else {
-        const v4f z = {0.f, 0.f, 0.f, 0.f};
-        pr[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
+      for (int r = 0; r < 4; r++) acc[ip][jp][r] = fmaf(pr[pslot][r], sp, acc[ip][jp][r]);
+    }
+    if constexpr (NXT >= 0) wf[j] = frag(stage(NXT) + 256 * BK, wn * 64 + j * 16, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <int S, int NXT, int I>
+  __device__ __forceinline__ void row(const v8i& xf, const float (&f)[SM], const uint32_t (&eas)[SM],
+                                     const uint32_t (&ebs)[SN]) {
+    mf<S, NXT, 4 * I + 0>(xf, f, eas, ebs);
+    mf<S, NXT, 4 * I + 1>(xf, f, eas, ebs);
+    mf<S, NXT, 4 * I + 2>(xf, f, eas, ebs);
+    mf<S, NXT, 4 * I + 3>(xf, f, eas, ebs);
+  }
+
+  // rows 0..SM-2 of a step; row I first reads the activation fragment of row I+2
+  template <int S, int... I>
+  __device__ __forceinline__ void rows(v8i (&xs)[SM], const float (&f)[SM], std::integer_sequence<int, I...>) {
+    ((pre<S, I>(xs), row<S, -1, I>(xs[I], f, ea, eb)), ...);
+  }
+  template <int S, int I>
+  __device__ __forceinline__ void pre(v8i (&xs)[SM]) {
+    if constexpr (I + 2 < SM) xs[I + 2] = frag(stage(S), wm * C::WTM + (I + 2) * 16, lane);
+  }
+
+  // the folds still pending after the last step (which used stage S)
+  template <int S>
+  __device__ __forceinline__ void drain() {
 #pragma unroll
-        for (int r = 0; r < 4; r++) acc[ip][j][r] = fmaf(pr[(i + 1) & 1][j][r], sp, acc[ip][j][r]);
-      }
-      if constexpr (NXT >= 0) wf[j] = frag(stage(NXT) + 256 * BK, wn * 64 + j * 16, lane);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 2; q++) {
+      const int slot = (kPerStep * S + kPerStep - 2 + q) % 3;
+#pragma unroll
+      for (int r = 0; r < 4; r++) acc[SM - 1][2 + q][r] = fmaf(pr[slot][r], pend_s, acc[SM - 1][2 + q][r]);
     }
   }
 
-  // K step kb computed from stage S.
+  // K step kb computed from stage S: rows 0..SM-2, the barrier, the loads of step kb+3,
+  // the next step's first operands, the last row.
   template <int S>
   __device__ __forceinline__ void step(int kb) {
     constexpr int NX = (S + 1) % kDmaStages;
-    const uint8_t* cu = stage(S);
-    float srow[SM], sbv = 0.f;
+    float f[SM];
     if constexpr (!MX) {
 #pragma unroll
-      for (int i = 0; i < SM; i++) srow[i] = sa[i];
-      sbv = sb;
+      for (int i = 0; i < SM; i++) f[i] = sa[i] * sb;
     }
-    v8i x2 = frag(cu, wm * 64 + 32, lane);
-    row<-1>(0, x0, pend_s, ea, eb);
-    v8i x3 = frag(cu, wm * 64 + 48, lane);
-    row<-1>(1, x1, srow[0] * sbv, ea, eb);
-    row<-1>(2, x2, srow[1] * sbv, ea, eb);
+    v8i xs[SM];
+    xs[0] = x0;
+    xs[1] = x1;
+    rows<S>(xs, f, std::make_integer_sequence<int, SM - 1>{});
     // Every load of step kb+1 by this wave has landed (only step kb+2's group, issued
     // later, may still be in flight), and its reads of stage S are done.
     wait_vmcnt<kGroup>();
@@ -674,8 +717,6 @@ struct DmaRun {
     // Past the end the step index is clamped: the stage it fills is never read again,
     // and every step keeps the same load count and no branch.
     issue(S, min(kb + 3, nkb - 1));
-    // the next step's first activation fragments and scales go into registers freed by
-    // rows 0 and 1, so they are in flight during the whole last row
     uint32_t ea_c[SM], eb_c[SN];
     if constexpr (MX) {
 #pragma unroll
@@ -683,19 +724,21 @@ struct DmaRun {
 #pragma unroll
       for (int j = 0; j < SN; j++) eb_c[j] = eb[j];
     }
-    x0 = frag(stage(NX), wm * 64, lane);
-    x1 = frag(stage(NX), wm * 64 + 16, lane);
+    // the next step's first activation fragments and scales, into registers freed by
+    // rows 0 and 1, in flight during the whole last row
+    x0 = frag(stage(NX), wm * C::WTM, lane);
+    x1 = frag(stage(NX), wm * C::WTM + 16, lane);
     load_scales(NX);
     __builtin_amdgcn_sched_barrier(0);
-    row<NX>(3, x3, srow[2] * sbv, ea_c, eb_c);
-    if constexpr (!MX) pend_s = srow[3] * sbv;
+    row<S, NX, SM - 1>(xs[SM - 1], f, ea_c, eb_c);
+    if constexpr (!MX) pend_s = f[SM - 1];
   }
 };
 
-template <int SCM>
+template <class C, int SCM>
 __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) {
-  using C = Large;
-  DmaRun<SCM> r{p};
+  using R = DmaRun<C, SCM>;
+  R r{p};
   r.smem = smem;
   r.smem_lds = lds_addr(smem);
   r.lane = threadIdx.x & 63;
@@ -712,78 +755,84 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   r.b_base = B + n0 * p.ldb;
   // lane l of a 1 KB block: tile row blk*8 + l/8, LDS chunk l%8 = logical chunk ^ swz(row)
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int row = (wave * 4 + q) * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
+  for (int q = 0; q < R::kLA; q++) {
+    const int row = (wave * R::kLA + q) * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
     r.a_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.lda + c * 16);
   }
 #pragma unroll
-  for (int q = 0; q < 2; q++) {
-    const int row = (wave * 2 + q) * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
+  for (int q = 0; q < R::kLB; q++) {
+    const int row = (wave * R::kLB + q) * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
     r.b_off[q] = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.ldb + c * 16);
   }
-  // this wave's scale load (default: 4 bytes of A into the spare area)
-  r.s_base = r.a_base;
-  r.s_off = 0;
-  r.s_step = 0;
-  r.s_lds = kDmaScOff + 1536;
-  if constexpr (SCM == kScF32Row) {
-    const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
-    if (wave < 4) {  // 4 bytes of tile row wave*64 + lane
-      const int row = wave * 64 + lane;
-      r.s_base = SA + m0 * p.sa_sm * 4;
-      r.s_off = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
-      r.s_step = p.sa_sk * 4;
-      r.s_lds = kDmaScOff + wave * 256;
+  // Scale job js = q * kW + wave (8 per step). Default: 4 bytes of A into the spare area.
+#pragma unroll
+  for (int q = 0; q < R::kSc; q++) {
+    const int js = q * R::kW + wave;
+    r.s_base[q] = r.a_base;
+    r.s_off[q] = 0;
+    r.s_step[q] = 0;
+    r.s_lds[q] = 1536;
+    if constexpr (SCM == kScF32Row) {
+      if (js < 4) {  // fp32 scale of tile row 64 js + lane
+        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
+        const int row = js * 64 + lane;
+        r.s_base[q] = SA + m0 * p.sa_sm * 4;
+        r.s_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
+        r.s_step[q] = p.sa_sk * 4;
+        r.s_lds[q] = js * 256;
+      }
+    } else if constexpr (SCM == kScE8Col) {
+      if (js == 0) {  // the 4 bytes of tile rows 4*lane .. 4*lane + 3 (clamped to the last full word)
+        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se;
+        r.s_base[q] = SA + m0;
+        r.s_off[q] = static_cast<uint32_t>(min(m0 + 4 * lane, p.M - 4) - m0);
+        r.s_step[q] = p.sa_sk;
+        r.s_lds[q] = 0;
+      }
+    } else {
+      if (js < 4) {  // E8M0 word (K blocks 4kb..4kb+3) of A row 64 js + lane
+        const uint8_t* SA = static_cast<const uint8_t*>(p.sa);
+        const int row = js * 64 + lane;
+        r.s_base[q] = SA + m0 * p.sa_sm;
+        r.s_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm);
+        r.s_step[q] = 4;
+        r.s_lds[q] = js * 256;
+      } else if (js < 6) {  // and of B row 64 (js-4) + lane
+        const uint8_t* SB = static_cast<const uint8_t*>(p.sb);
+        const int row = (js - 4) * 64 + lane;
+        r.s_base[q] = SB + n0 * p.sb_sn;
+        r.s_off[q] = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.sb_sn);
+        r.s_step[q] = 4;
+        r.s_lds[q] = 1024 + (js - 4) * 256;
+      }
     }
-  } else if constexpr (SCM == kScE8Col) {
-    const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se;
-    if (wave == 0) {  // the 4 bytes of tile rows 4*lane .. 4*lane + 3 (clamped to the last full word)
-      r.s_base = SA + m0;
-      r.s_off = static_cast<uint32_t>(min(m0 + 4 * lane, p.M - 4) - m0);
-      r.s_step = p.sa_sk;
-      r.s_lds = kDmaScOff;
-    }
-  } else {
-    const uint8_t* SA = static_cast<const uint8_t*>(p.sa);
-    const uint8_t* SB = static_cast<const uint8_t*>(p.sb);
-    if (wave < 4) {  // E8M0 word (K blocks 4kb..4kb+3) of A row wave*64 + lane
-      const int row = wave * 64 + lane;
-      r.s_base = SA + m0 * p.sa_sm;
-      r.s_off = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm);
-      r.s_step = 4;
-      r.s_lds = kDmaScOff + wave * 256;
-    } else if (wave < 6) {  // and of B row (wave-4)*64 + lane
-      const int row = (wave - 4) * 64 + lane;
-      r.s_base = SB + n0 * p.sb_sn;
-      r.s_off = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.sb_sn);
-      r.s_step = 4;
-      r.s_lds = kDmaScOff + 1024 + (wave - 4) * 256;
-    }
-  }
-  if constexpr (SCM != kScMx) {
-    // the weight-block scale, one fp32 word per step (every lane loads it; the word
-    // lands 64 times in [1024, 1280) of the scale area)
-    if (wave == (SCM == kScF32Row ? 4 : 1)) {
-      const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
-      r.s_base = SB + (n0 / 128) * p.sb_sn * 4;
-      r.s_off = 0;
-      r.s_step = p.sb_sk * 4;
-      r.s_lds = kDmaScOff + 1024;
+    if constexpr (SCM != kScMx) {
+      // the weight-block scale, one fp32 word per step (every lane loads it; the word
+      // lands 64 times in [1024, 1280) of the scale area)
+      if (js == (SCM == kScF32Row ? 4 : 1)) {
+        const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
+        r.s_base[q] = SB + (n0 / 128) * p.sb_sn * 4;
+        r.s_off[q] = 0;
+        r.s_step[q] = p.sb_sk * 4;
+        r.s_lds[q] = 1024;
+      }
     }
   }
 #pragma unroll
   for (int i = 0; i < C::SM; i++)
 #pragma unroll
     for (int j = 0; j < C::SN; j++) r.acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < C::SN; j++) r.pr[1][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // the folds at the start of the first step add 0 * 0 (MFMAs -2 and -1)
+  r.pr[0] = v4f{0.f, 0.f, 0.f, 0.f};
+  r.pr[1] = r.pr[0];
+  r.pr[2] = r.pr[0];
   r.pend_s = 0.f;
 
   const int nkb = r.nkb;
   r.issue(0, 0);
   r.issue(1, min(1, nkb - 1));
   r.issue(2, min(2, nkb - 1));
-  wait_vmcnt<2 * DmaRun<SCM>::kGroup>();  // step 0 has landed; steps 1 and 2 may be in flight
+  wait_vmcnt<2 * R::kGroup>();  // step 0 has landed; steps 1 and 2 may be in flight
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   r.load_ops(0);
@@ -792,12 +841,11 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
     if (kb + 1 < nkb) r.template step<1>(kb + 1);
     if (kb + 2 < nkb) r.template step<2>(kb + 2);
   }
-  if constexpr (SCM != kScMx) {  // the last row's fold is still pending
-#pragma unroll
-    for (int j = 0; j < C::SN; j++)
-#pragma unroll
-      for (int q = 0; q < 4; q++)
-        r.acc[C::SM - 1][j][q] = fmaf(r.pr[(C::SM - 1) & 1][j][q], r.pend_s, r.acc[C::SM - 1][j][q]);
+  if constexpr (SCM != kScMx) {  // the last step's last two folds are still pending
+    const int s_last = (nkb - 1) % kDmaStages;
+    if (s_last == 0) r.template drain<0>();
+    else if (s_last == 1) r.template drain<1>();
+    else r.template drain<2>();
   }
   // no load is in flight and nobody reads a stage any more before the next tile's loads
   wait_vmcnt<0>();
@@ -805,7 +853,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  // epilogue: lane holds Y[m][n..n+3], m = m0+wm*64+i*16+lane%16, n = n0+wn*64+j*16+4*(lane/16)
+  // epilogue: lane holds Y[m][n..n+3], m = m0+wm*WTM+i*16+lane%16, n = n0+wn*WTN+j*16+4*(lane/16)
   uint16_t* Y = p.y + t.e * p.y_se;
   const int wm = r.wm, wn = r.wn;
 #pragma unroll
@@ -831,12 +879,13 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
 }
 
 template <int SCM>
-__global__ __launch_bounds__(Large::kThreads, 1) void gemm_dma_kernel(GemmParams p) {
+__global__ __launch_bounds__(DmaCfg::kThreads, 1) void gemm_dma_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kDmaStages * kDmaStage];
   __shared__ int32_t pref[kDmaMaxPrefix + 1];  // masked only, E + 1 entries
   int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch, used before any load
-  const TileRange tr(build_tile_list<Large>(p, part, pref));
-  for (int64_t t = tr.beg; t < tr.end; t += tr.stride) run_tile_dma<SCM>(p, smem, tile_at<Large>(p, pref, t));
+  const TileRange tr(build_tile_list<DmaCfg>(p, part, pref));
+  for (int64_t t = tr.beg; t < tr.end; t += tr.stride)
+    run_tile_dma<DmaCfg, SCM>(p, smem, tile_at<DmaCfg>(p, pref, t));
 }
 
 // ------------------------------------------------------------------ skinny GEMM (small M)
@@ -999,7 +1048,7 @@ int dma_mode(const GemmParams& p, bool mx) {
 
 template <int SCM>
 void launch_dma(const GemmParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_dma_kernel<SCM>), dim3(grid), dim3(Large::kThreads), 0, s, p);
+  hipLaunchKernelGGL((gemm_dma_kernel<SCM>), dim3(grid), dim3(DmaCfg::kThreads), 0, s, p);
 }
 
 }  // namespace
