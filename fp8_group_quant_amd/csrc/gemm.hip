@@ -524,12 +524,30 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 // scales stored column-major ([K/128][M], M a multiple of 4), fp32 weight-block scales,
 // and MX32 E8M0 bytes stored [rows][K/32] with rows a multiple of 4 bytes apart. Other
 // layouts use the register-staged kernel above.
-enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2 };
+//
+// Scales stored per row along K (fp32 [M][K/128], E8M0 [rows][K/32]) put each row's word
+// of one step in a different cache line. When K is a multiple of 512 and rows are 16-byte
+// aligned, the grouped modes load four steps of a row's scales with one 16-byte load,
+// once every four steps, into a two-slot ring (slot g%2 holds steps 4g..4g+3): group g+1
+// is loaded after the barrier of step 4g-1, when nobody reads group g-1 any more, and is
+// first read four steps later. The scale load of the other steps (and of the wavefronts
+// without a scale to move) rereads group 0 into a 1 KB area nobody reads, so every step
+// still issues the same loads.
+enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp = 4 };
 
-constexpr int kDmaStage = 256 * BK + 128 * BK + 1792;  // A tile, B tile, scales (+ a spare word per lane)
-constexpr int kDmaScOff = 256 * BK + 128 * BK;
 constexpr int kDmaStages = 3;
-constexpr int kDmaMaxPrefix = 2048;  // masked launches: at most this many experts
+
+template <int SCM>
+struct DmaLayout {
+  static constexpr bool kGrouped = SCM == kScF32Grp || SCM == kScMxGrp;
+  static constexpr int kScOff = 256 * BK + 128 * BK;  // per-step modes: scale area inside a stage
+  static constexpr int kStage = kScOff + (kGrouped ? 0 : 1792);  // (+ a spare word per lane)
+  static constexpr int kRing = kDmaStages * kStage;  // grouped modes: two slots, then the dummy area
+  static constexpr int kSlot = 6144;
+  static constexpr int kDummy = kRing + 2 * kSlot;
+  static constexpr int kBytes = kGrouped ? kDummy + 1024 : kDmaStages * kStage;
+  static constexpr int kMaxPrefix = kGrouped ? 700 : 2048;  // masked launches: at most this many experts
+};
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -559,12 +577,14 @@ using DmaCfg = TileCfg<256, 128, 4, 2, 4>;
 // Per-tile state of the direct-to-LDS loop.
 template <class C, int SCM>
 struct DmaRun {
-  static constexpr bool MX = SCM == kScMx;
+  using L = DmaLayout<SCM>;
+  static constexpr bool MX = SCM == kScMx || SCM == kScMxGrp;
+  static constexpr bool F32 = SCM == kScF32Row || SCM == kScF32Grp;
   static constexpr int SM = C::SM, SN = C::SN;
   static_assert(C::BM == 256 && C::BN == 128 && SN == 4 && C::WTN == 64, "256x128 tiles, 64-wide wave tiles");
   static constexpr int kW = C::kWaves;
   static constexpr int kLA = (C::BM / 8) / kW, kLB = (C::BN / 8) / kW;  // 1 KB blocks per wave
-  static constexpr int kSc = 8 / kW;                                   // scale jobs per wave
+  static constexpr int kSc = L::kGrouped ? 1 : 8 / kW;                // scale jobs per wave
   // loads per wave and step: tile blocks, then scale jobs
   static constexpr int kGroup = kLA + kLB + kSc;
   static constexpr int kPerStep = 4 * SM;  // MFMAs per wave and step
@@ -582,6 +602,12 @@ struct DmaRun {
   uint32_t s_off[kSc];
   int64_t s_step[kSc];
   uint32_t s_lds[kSc];
+  // grouped modes: this wave's 16-byte scale load (role: ea/sa rows, eb rows or sb, or
+  // none), its source for group 0, the bytes per group, its ring offset; ngroups = nkb/4
+  const uint8_t* g_base;
+  uint32_t g_off, g_lds;
+  int g_step, ngroups;
+  bool g_role;
   // operands of the current step
   v8i wf[SN];
   v8i x0, x1;
@@ -595,21 +621,46 @@ struct DmaRun {
   float pend_s;
 
   __device__ __forceinline__ void issue(int st, int kb) {
-    const uint32_t base = smem_lds + st * kDmaStage;
+    const uint32_t base = smem_lds + st * L::kStage;
     const uint8_t* ap = a_base + kb * BK;
 #pragma unroll
     for (int q = 0; q < kLA; q++) dma16(base + (wave * kLA + q) * 1024, ap, a_off[q]);
     const uint8_t* bp = b_base + kb * BK;
 #pragma unroll
     for (int q = 0; q < kLB; q++) dma16(base + 256 * BK + (wave * kLB + q) * 1024, bp, b_off[q]);
+    if constexpr (L::kGrouped) {
+      // tiles of step kb carry scale group (kb+2)/4 when kb%4 == 2 (groups 0 and 1 with
+      // the first two steps); the group index is clamped (a reload writes equal bytes)
+      const bool real = g_role && (kb <= 1 || (kb & 3) == 2);
+      const int g = kb <= 1 ? kb : min((kb + 2) >> 2, ngroups - 1);
+      const uint32_t dst = real ? smem_lds + L::kRing + (g & 1) * L::kSlot + g_lds : smem_lds + L::kDummy;
+      dma16(dst, g_base + (real ? g * g_step : 0), g_off);
+    } else {
 #pragma unroll
-    for (int q = 0; q < kSc; q++) dma4(base + kDmaScOff + s_lds[q], s_base[q] + kb * s_step[q], s_off[q]);
+      for (int q = 0; q < kSc; q++) dma4(base + L::kScOff + s_lds[q], s_base[q] + kb * s_step[q], s_off[q]);
+    }
   }
 
-  __device__ __forceinline__ const uint8_t* stage(int st) const { return smem + st * kDmaStage; }
+  __device__ __forceinline__ const uint8_t* stage(int st) const { return smem + st * L::kStage; }
 
-  __device__ __forceinline__ void load_scales(int st) {
-    const uint8_t* sc = stage(st) + kDmaScOff;
+  // scales of step kb (held in stage st, or in the ring)
+  __device__ __forceinline__ void load_scales(int st, int kb) {
+    if constexpr (L::kGrouped) {
+      const uint8_t* ring = smem + L::kRing + ((kb >> 2) & 1) * L::kSlot;
+      const int q = kb & 3;
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < SM; i++) ea[i] = ring[16 * (wm * C::WTM + i * 16 + (lane & 15)) + 4 * q + (lane >> 4)];
+#pragma unroll
+        for (int j = 0; j < SN; j++) eb[j] = ring[4096 + 16 * (wn * 64 + j * 16 + (lane & 15)) + 4 * q + (lane >> 4)];
+      } else {
+#pragma unroll
+        for (int i = 0; i < SM; i++) sa[i] = reinterpret_cast<const float*>(ring)[4 * (wm * C::WTM + i * 16 + (lane & 15)) + q];
+        sb = reinterpret_cast<const float*>(ring + 4096)[q];
+      }
+      return;
+    }
+    const uint8_t* sc = stage(st) + L::kScOff;
     if constexpr (MX) {
 #pragma unroll
       for (int i = 0; i < SM; i++) ea[i] = sc[4 * (wm * C::WTM + i * 16 + (lane & 15)) + (lane >> 4)];
@@ -619,7 +670,7 @@ struct DmaRun {
 #pragma unroll
       for (int i = 0; i < SM; i++) {
         const int row = wm * C::WTM + i * 16 + (lane & 15);
-        if constexpr (SCM == kScF32Row)
+        if constexpr (F32)
           sa[i] = reinterpret_cast<const float*>(sc)[row];
         else
           sa[i] = scale_value<FP8Q_SCALE_UE8M0>(sc[row]);
@@ -635,7 +686,7 @@ struct DmaRun {
     for (int j = 0; j < SN; j++) wf[j] = frag(s + 256 * BK, wn * 64 + j * 16, lane);
     x0 = frag(s, wm * C::WTM, lane);
     x1 = frag(s, wm * C::WTM + 16, lane);
-    load_scales(st);
+    load_scales(st, 0);
   }
 
   // MFMA t = 4i + j of the step computed from stage S, then (BLOCK128) the fold of MFMA
@@ -728,7 +779,7 @@ struct DmaRun {
     // rows 0 and 1, in flight during the whole last row
     x0 = frag(stage(NX), wm * C::WTM, lane);
     x1 = frag(stage(NX), wm * C::WTM + 16, lane);
-    load_scales(NX);
+    load_scales(NX, kb + 1);
     __builtin_amdgcn_sched_barrier(0);
     row<S, NX, SM - 1>(xs[SM - 1], f, ea_c, eb_c);
     if constexpr (!MX) pend_s = f[SM - 1];
@@ -806,7 +857,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_lds[q] = 1024 + (js - 4) * 256;
       }
     }
-    if constexpr (SCM != kScMx) {
+    if constexpr (SCM == kScF32Row || SCM == kScE8Col) {
       // the weight-block scale, one fp32 word per step (every lane loads it; the word
       // lands 64 times in [1024, 1280) of the scale area)
       if (js == (SCM == kScF32Row ? 4 : 1)) {
@@ -816,6 +867,47 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_step[q] = p.sb_sk * 4;
         r.s_lds[q] = 1024;
       }
+    }
+  }
+  // Grouped modes: wave w's 16-byte job moves four steps of scales of 64 rows (w < 4:
+  // activation rows 64w + lane; MX32 w = 4, 5: weight rows 64(w-4) + lane; BLOCK128
+  // w = 4: the weight-block scale, every lane the same 16 bytes). Others only load the
+  // dummy. Ring slot layout: [0, 4 KB) activation rows x 16 bytes, from 4 KB the rest.
+  r.g_role = false;
+  r.g_base = r.a_base;
+  r.g_off = 0;
+  r.g_step = 16;
+  r.g_lds = 0;
+  r.ngroups = r.nkb / 4;
+  if constexpr (SCM == kScF32Grp) {
+    if (wave < 4) {
+      const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
+      const int row = wave * 64 + lane;
+      r.g_role = true;
+      r.g_base = SA + m0 * p.sa_sm * 4;
+      r.g_off = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
+      r.g_lds = wave * 1024;
+    } else if (wave == 4) {
+      const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
+      r.g_role = true;
+      r.g_base = SB + (n0 / 128) * p.sb_sn * 4;
+      r.g_lds = 4096;
+    }
+  } else if constexpr (SCM == kScMxGrp) {
+    if (wave < 4) {
+      const uint8_t* SA = static_cast<const uint8_t*>(p.sa);
+      const int row = wave * 64 + lane;
+      r.g_role = true;
+      r.g_base = SA + m0 * p.sa_sm;
+      r.g_off = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm);
+      r.g_lds = wave * 1024;
+    } else if (wave < 6) {
+      const uint8_t* SB = static_cast<const uint8_t*>(p.sb);
+      const int row = (wave - 4) * 64 + lane;
+      r.g_role = true;
+      r.g_base = SB + n0 * p.sb_sn;
+      r.g_off = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.sb_sn);
+      r.g_lds = 4096 + (wave - 4) * 1024;
     }
   }
 #pragma unroll
@@ -841,7 +933,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
     if (kb + 1 < nkb) r.template step<1>(kb + 1);
     if (kb + 2 < nkb) r.template step<2>(kb + 2);
   }
-  if constexpr (SCM != kScMx) {  // the last step's last two folds are still pending
+  if constexpr (!R::MX) {  // the last step's last two folds are still pending
     const int s_last = (nkb - 1) % kDmaStages;
     if (s_last == 0) r.template drain<0>();
     else if (s_last == 1) r.template drain<1>();
@@ -880,8 +972,8 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
 
 template <int SCM>
 __global__ __launch_bounds__(DmaCfg::kThreads, 1) void gemm_dma_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kDmaStages * kDmaStage];
-  __shared__ int32_t pref[kDmaMaxPrefix + 1];  // masked only, E + 1 entries
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DmaLayout<SCM>::kBytes];
+  __shared__ int32_t pref[DmaLayout<SCM>::kMaxPrefix + 1];  // masked only, E + 1 entries
   int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch, used before any load
   const TileRange tr(build_tile_list<DmaCfg>(p, part, pref));
   for (int64_t t = tr.beg; t < tr.end; t += tr.stride)
@@ -1032,17 +1124,27 @@ int finish(const char* what) {
 bool u32_ok(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
 int dma_mode(const GemmParams& p, bool mx) {
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   if (p.lda >= (int64_t(1) << 24) || p.ldb >= (int64_t(1) << 24)) return -1;
-  if (p.masked_m && p.E > kDmaMaxPrefix) return -1;
+  const bool k512 = p.K % 512 == 0;
   if (mx) {
-    const bool ok = p.sa_sk == 1 && p.sb_sk == 1 && p.sa_sm % 4 == 0 && p.sb_sn % 4 == 0 && u32_ok(p.sa) &&
-                    u32_ok(p.sb) && p.sa_sm < (int64_t(1) << 24) && p.sb_sn < (int64_t(1) << 24);
+    if (p.sa_sk != 1 || p.sb_sk != 1 || p.sa_sm >= (int64_t(1) << 24) || p.sb_sn >= (int64_t(1) << 24)) return -1;
+    if (k512 && p.sa_sm % 16 == 0 && p.sb_sn % 16 == 0 && a16(p.sa) && a16(p.sb)) return kScMxGrp;
+    const bool ok = p.sa_sm % 4 == 0 && p.sb_sn % 4 == 0 && u32_ok(p.sa) && u32_ok(p.sb);
     return ok ? kScMx : -1;
   }
+  const int64_t E = p.masked_m ? p.E : 1;
   if (p.sb_fmt != FP8Q_SCALE_F32) return -1;
-  if (p.sa_fmt == FP8Q_SCALE_F32) return p.sa_sm < (int64_t(1) << 22) ? kScF32Row : -1;
+  if (p.sa_fmt == FP8Q_SCALE_F32) {
+    if (p.sa_sm >= (int64_t(1) << 22)) return -1;
+    const bool grp = k512 && p.sa_sk == 1 && p.sa_sm % 4 == 0 && a16(p.sa) && p.sb_sk == 1 && p.sb_sn % 4 == 0 &&
+                     a16(p.sb) && (E == 1 || (p.sa_se % 4 == 0 && p.sb_se % 4 == 0)) &&
+                     E <= DmaLayout<kScF32Grp>::kMaxPrefix;
+    if (grp) return kScF32Grp;
+    return E <= DmaLayout<kScF32Row>::kMaxPrefix ? kScF32Row : -1;
+  }
   const bool col = p.sa_sm == 1 && p.sa_sk % 4 == 0 && p.M % 4 == 0 && u32_ok(p.sa) &&
-                   (p.masked_m == nullptr || p.sa_se % 4 == 0);
+                   (p.masked_m == nullptr || p.sa_se % 4 == 0) && E <= DmaLayout<kScE8Col>::kMaxPrefix;
   return col ? kScE8Col : -1;
 }
 
@@ -1074,6 +1176,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   }
   const int dm = dma_mode(p, false);
   if (dm == kScF32Row) launch_dma<kScF32Row>(p, grid, stream);
+  else if (dm == kScF32Grp) launch_dma<kScF32Grp>(p, grid, stream);
   else if (dm == kScE8Col) launch_dma<kScE8Col>(p, grid, stream);
   else if (a8 && b8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid, stream);
   else if (a8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, grid, stream);
@@ -1085,7 +1188,9 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
 int launch_gemm_mx32(const GemmParams& p, hipStream_t stream) {
   using C = Large;
   const int64_t tiles = ((p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN);
-  if (dma_mode(p, true) == kScMx) launch_dma<kScMx>(p, grid_for(tiles), stream);
+  const int dm = dma_mode(p, true);
+  if (dm == kScMxGrp) launch_dma<kScMxGrp>(p, grid_for(tiles), stream);
+  else if (dm == kScMx) launch_dma<kScMx>(p, grid_for(tiles), stream);
   else launch<C, true, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid_for(tiles), stream);
   return finish("MXFP8 GEMM launch");
 }

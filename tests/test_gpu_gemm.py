@@ -69,10 +69,11 @@ def test_tiny_workload_full():
 
 # M > 128 with M % 4 == 0 reaches the direct-to-LDS kernel for fp32 weight scales (also
 # with UE8M0 column-major activation scales); M % 4 != 0 or UE8M0 weight scales take the
-# register-staged kernel; K = 128 and 256 cover pipelines shorter than their depth.
+# register-staged kernel; K = 128 and 256 cover pipelines shorter than their depth, and
+# K % 512 == 0 the four-step scale groups (K = 512: a single group).
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 130, 256), (129, 200, 384), (257, 300, 640),
                                    (64, 1024, 1024), (132, 136, 128), (264, 128, 256),
-                                   (260, 300, 640), (516, 136, 384)])
+                                   (260, 300, 640), (516, 136, 384), (132, 136, 512), (260, 300, 1024)])
 @pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col"])
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
 def test_ragged_shapes_full(M, N, K, sa_kind, sb_kind):
@@ -230,7 +231,7 @@ def _gpu_mx(a, ea, b, eb, sk_stride=False):
     return y.cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (130, 96, 256), (300, 260, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (130, 96, 256), (136, 200, 512), (300, 260, 1024)])
 @pytest.mark.parametrize("sk_stride", [False, True])
 def test_mx_full(M, N, K, sk_stride):
     a = synth.weight_codes(70, M, K, tensor_id=1)
