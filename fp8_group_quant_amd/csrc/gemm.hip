@@ -555,13 +555,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)p));
 }
 
-// lane l: LDS [lds + 16 l, +16) <- global [base + voff, +16)
+// lane l: LDS [lds + 16 l, +16) <- global [base + voff, +16). sc1 (device scope): the
+// data has no reuse inside one CU, and this measured a few percent faster than the
+// default policy (nt was much slower).
 __device__ __forceinline__ void dma16(uint32_t lds, const void* base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc1" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
 // lane l: LDS [lds + 4 l, +4) <- global [base + voff, +4)
 __device__ __forceinline__ void dma4(uint32_t lds, const void* base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 sc1" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
 template <int N>
