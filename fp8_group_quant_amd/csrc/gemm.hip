@@ -983,12 +983,13 @@ __global__ __launch_bounds__(DmaCfg::kThreads, 1) void gemm_dma_kernel(GemmParam
 }
 
 // ------------------------------------------------------------------ skinny GEMM (small M)
-// For M <= 128 the product is bound by streaming B (the weights) from HBM, and 256x128
-// tiles would leave most CUs idle. Here each workgroup owns 16 rows of B (one MFMA n
-// slice) against all M rows of A; its four waves split the K blocks four ways (block kb
-// goes to wave kb % 4) and each lane loads its MFMA fragments straight from global memory,
-// U blocks ahead, with no LDS staging. The four partial sums are added through LDS at the
-// end. BLOCK128 only.
+// For M <= 128 the product is bound by streaming B (the weights) from HBM and A from L2,
+// and 256x128 tiles would leave most CUs idle. Each workgroup owns 16 rows of B (one MFMA
+// n slice) against all M rows of A; its four waves split the K blocks four ways (block kb
+// goes to wave kb % 4) and the four partial sums are added through LDS at the end.
+// BLOCK128 only. Two variants: the kernel below loads MFMA fragments straight from global
+// memory into registers, U blocks ahead (any scale layout); the LDS-staged one after it
+// (fp32 weight-block scales) moves whole cache lines and is about twice as fast.
 constexpr int kSkinnyThreads = 256;
 constexpr int64_t kSkinnyMaxM = 128;  // at most 8 m subtiles
 
@@ -1089,6 +1090,177 @@ __global__ __launch_bounds__(kSkinnyThreads) void gemm_skinny_kernel(GemmParams 
   }
 }
 
+// Small M through LDS: the same split (16 rows of B per workgroup, K blocks dealt to the
+// four waves in turn, partial sums added through LDS), but each wave moves its K blocks
+// (all M rows of A plus the 16 rows of B, 128 bytes each) into a private ring of LDS
+// stages with global_load_lds, one full cache line per 8 lanes, kStages-1 blocks ahead.
+// A wave only reads its own stages, so the K loop needs no barrier: the wave's own
+// vmcnt wait makes a stage readable, and its own LDS reads complete before it refills
+// the stage. The activation scales of the workgroup ([K/128][MR]) and the weight-block
+// scales ([K/128]) are read into LDS tables before the loop, so the loop issues no other
+// vector-memory instruction and the vmcnt counts are exact. Fragment reads use the same
+// XOR swizzle as the large kernels. The result equals the register-loading kernel's bit
+// for bit (same per-wave block order and reduction order).
+template <int SM>
+struct SkinnyDmaCfg {
+  static constexpr int MR = 16 * SM;                      // activation rows per block
+  static constexpr int kStage = (MR + 16) * BK;           // A rows, then B rows
+  static constexpr int kStages = SM >= 8 ? 2 : (SM >= 4 ? 3 : 4);
+  static constexpr int kLoads = MR / 8 + 2;               // 1 KB loads per block
+  static constexpr int kRing = 4 * kStages * kStage;      // all four waves
+};
+
+size_t skinny_dma_lds(int sm, int sa_fmt, int64_t nkb) {
+  auto ring = [](int s) -> size_t {
+    switch (s) {
+      case 1: return SkinnyDmaCfg<1>::kRing;
+      case 2: return SkinnyDmaCfg<2>::kRing;
+      case 4: return SkinnyDmaCfg<4>::kRing;
+      default: return SkinnyDmaCfg<8>::kRing;
+    }
+  };
+  const size_t tab = static_cast<size_t>(nkb) * (16 * sm) * (sa_fmt == FP8Q_SCALE_F32 ? 4 : 1);
+  return ring(sm) + ((tab + 15) & ~size_t(15)) + static_cast<size_t>(nkb) * 4;
+}
+
+template <int SM, int SA_FMT>
+__global__ __launch_bounds__(kSkinnyThreads, 1) void gemm_skinny_dma_kernel(GemmParams p) {
+  using D = SkinnyDmaCfg<SM>;
+  constexpr int MR = D::MR, KS = D::kStages, KG = D::kLoads;
+  constexpr int sab = SA_FMT == FP8Q_SCALE_F32 ? 4 : 1;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int nkb = static_cast<int>(p.K / BK);
+  uint8_t* sa_tab = smem + D::kRing;  // [nkb][MR] bytes or floats
+  float* sb_tab = reinterpret_cast<float*>(sa_tab + ((static_cast<size_t>(nkb) * MR * sab + 15) & ~size_t(15)));
+
+  // this wave's loads: lane l of a 1 KB block covers row blk*8 + l/8 at LDS chunk l%8,
+  // which holds logical chunk (l%8) ^ swz(row)
+  const uint32_t ring = lds_addr(smem) + wave * KS * D::kStage;
+  uint32_t xo[MR / 8], wo[2];
+#pragma unroll
+  for (int q = 0; q < MR / 8; q++) {
+    const int row = q * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
+    xo[q] = static_cast<uint32_t>(min(static_cast<int64_t>(row), p.M - 1) * p.lda + c * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int row = q * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
+    wo[q] = static_cast<uint32_t>((min(n0 + row, p.N - 1) - n0) * p.ldb + c * 16);
+  }
+  const uint8_t* wbase = p.b + n0 * p.ldb;
+  const int nblk = (nkb - wave + 3) / 4;  // blocks kb = wave + 4 i
+  // block i of this wave into stage st (past the end: block 0, so every step issues the
+  // same loads and stays inside A and B; such a stage is never read)
+  auto issue = [&](int st, int i) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's reads of the stage are done
+    const int kb = i < nblk ? wave + 4 * i : 0;
+    const uint32_t dst = ring + st * D::kStage;
+#pragma unroll
+    for (int q = 0; q < MR / 8; q++) dma16(dst + q * 1024, p.a + kb * BK, xo[q]);
+#pragma unroll
+    for (int q = 0; q < 2; q++) dma16(dst + MR * BK + q * 1024, wbase + kb * BK, wo[q]);
+  };
+
+  v4f acc[SM];
+#pragma unroll
+  for (int i = 0; i < SM; i++) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS - 1; s++) issue(s, s);
+  // Scale tables (rows past M repeat row M-1; their outputs are never stored). All of a
+  // thread's table loads are issued before any of them is waited for, after the first
+  // blocks' loads, so their latency overlaps; both are complete before the K loop.
+  {
+    constexpr int U = 32;
+    const int total = nkb * MR;
+    for (int base = tid; base < total; base += kSkinnyThreads * U) {
+      uint32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int idx = base + u * kSkinnyThreads;
+        v[u] = 0;
+        if (idx < total) {
+          const int kb = idx / MR;
+          const int64_t m = min(static_cast<int64_t>(idx % MR), p.M - 1);
+          const int64_t si = m * p.sa_sm + kb * p.sa_sk;
+          v[u] = SA_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(p.sa)[si] : static_cast<const uint8_t*>(p.sa)[si];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int idx = base + u * kSkinnyThreads;
+        if (idx < total) {
+          if constexpr (SA_FMT == FP8Q_SCALE_F32)
+            reinterpret_cast<uint32_t*>(sa_tab)[idx] = v[u];
+          else
+            sa_tab[idx] = static_cast<uint8_t>(v[u]);
+        }
+      }
+    }
+    const int64_t nb = n0 / 128;
+    for (int kb = tid; kb < nkb; kb += kSkinnyThreads) sb_tab[kb] = static_cast<const float*>(p.sb)[nb * p.sb_sn + kb * p.sb_sk];
+  }
+  __syncthreads();
+  const uint8_t* ring_p = smem + wave * KS * D::kStage;
+  for (int i = 0; i < nblk; i++) {
+    const int st = i % KS;
+    issue((i + KS - 1) % KS, i + KS - 1);
+    wait_vmcnt<(KS - 1) * KG>();  // block i has landed
+    const uint8_t* s = ring_p + st * D::kStage;
+    const v8i wf = frag(s + MR * BK, 0, lane);
+    v8i xf[SM];
+#pragma unroll
+    for (int j = 0; j < SM; j++) xf[j] = frag(s, j * 16, lane);
+    const int kb = wave + 4 * i;
+    const float sbv = sb_tab[kb];
+#pragma unroll
+    for (int j = 0; j < SM; j++) {
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+      const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[j], z, 0, 0, 0, 0, 0, 0);
+      const int r = kb * MR + j * 16 + (lane & 15);
+      const float sav = SA_FMT == FP8Q_SCALE_F32 ? reinterpret_cast<const float*>(sa_tab)[r]
+                                                 : scale_value<FP8Q_SCALE_UE8M0>(sa_tab[r]);
+      const float sv = sav * sbv;
+#pragma unroll
+      for (int q = 0; q < 4; q++) acc[j][q] = fmaf(pr[q], sv, acc[j][q]);
+    }
+    // (the frags are in registers before the next iteration refills this stage: the
+    // MFMAs above consumed them)
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with its ring; reuse it for the reduction
+  v4f* red = reinterpret_cast<v4f*>(smem);  // [4 waves][SM][64]
+#pragma unroll
+  for (int j = 0; j < SM; j++) red[(wave * SM + j) * 64 + lane] = acc[j];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < SM; j++) {
+      v4f t = red[j * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; w++) {
+        const v4f o = red[(w * SM + j) * 64 + lane];
+        t[0] += o[0]; t[1] += o[1]; t[2] += o[2]; t[3] += o[3];
+      }
+      const int64_t m = j * 16 + (lane & 15);
+      if (m >= p.M) continue;
+      uint16_t* yrow = p.y + m * p.ldy;
+      const int64_t n = n0 + 4 * (lane >> 4);
+      const uint32_t h0 = bf16_rne(t[0]), h1 = bf16_rne(t[1]), h2 = bf16_rne(t[2]), h3 = bf16_rne(t[3]);
+      if (n + 3 < p.N) {
+        *reinterpret_cast<uint32_t*>(yrow + n) = h0 | (h1 << 16);
+        *reinterpret_cast<uint32_t*>(yrow + n + 2) = h2 | (h3 << 16);
+      } else {
+        if (n < p.N) yrow[n] = static_cast<uint16_t>(h0);
+        if (n + 1 < p.N) yrow[n + 1] = static_cast<uint16_t>(h1);
+        if (n + 2 < p.N) yrow[n + 2] = static_cast<uint16_t>(h2);
+      }
+    }
+  }
+}
+
 template <int SM, int SA_FMT, int SB_FMT>
 void launch_skinny(const GemmParams& p, hipStream_t s) {
   const int grid = static_cast<int>((p.N + 15) / 16);
@@ -1101,6 +1273,34 @@ void launch_skinny_m(const GemmParams& p, hipStream_t s) {
   else if (p.M <= 32) launch_skinny<2, SA_FMT, SB_FMT>(p, s);
   else if (p.M <= 64) launch_skinny<4, SA_FMT, SB_FMT>(p, s);
   else launch_skinny<8, SA_FMT, SB_FMT>(p, s);
+}
+
+template <int SM, int SA_FMT>
+int launch_skinny_dma(const GemmParams& p, size_t lds, hipStream_t s) {
+  auto kern = gemm_skinny_dma_kernel<SM, SA_FMT>;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return -1;
+  hipLaunchKernelGGL(kern, dim3(static_cast<int>((p.N + 15) / 16)), dim3(kSkinnyThreads), lds, s, p);
+  return 0;
+}
+
+// The LDS-staged small-M kernel when its scale tables and rings fit (fp32 weight-block
+// scales; any activation-scale layout); returns false to use the register-loading one.
+bool try_skinny_dma(const GemmParams& p, hipStream_t s) {
+  if (p.sb_fmt != FP8Q_SCALE_F32 || p.lda >= (int64_t(1) << 25) || p.ldb >= (int64_t(1) << 28)) return false;
+  const int sm = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : (p.M <= 64 ? 4 : 8));
+  const size_t lds = skinny_dma_lds(sm, p.sa_fmt, p.K / BK);
+  if (lds > 160 * 1024) return false;
+  const bool f = p.sa_fmt == FP8Q_SCALE_F32;
+  int rc;
+  switch (sm) {
+    case 1: rc = f ? launch_skinny_dma<1, FP8Q_SCALE_F32>(p, lds, s) : launch_skinny_dma<1, FP8Q_SCALE_UE8M0>(p, lds, s); break;
+    case 2: rc = f ? launch_skinny_dma<2, FP8Q_SCALE_F32>(p, lds, s) : launch_skinny_dma<2, FP8Q_SCALE_UE8M0>(p, lds, s); break;
+    case 4: rc = f ? launch_skinny_dma<4, FP8Q_SCALE_F32>(p, lds, s) : launch_skinny_dma<4, FP8Q_SCALE_UE8M0>(p, lds, s); break;
+    default: rc = f ? launch_skinny_dma<8, FP8Q_SCALE_F32>(p, lds, s) : launch_skinny_dma<8, FP8Q_SCALE_UE8M0>(p, lds, s); break;
+  }
+  return rc == 0;
 }
 
 template <class C, bool MX, int SA_FMT, int SB_FMT>
@@ -1170,6 +1370,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   const int grid = grid_for(tiles);
   const bool a8 = p.sa_fmt == FP8Q_SCALE_UE8M0, b8 = p.sb_fmt == FP8Q_SCALE_UE8M0;
   if (!p.masked_m && p.M <= kSkinnyMaxM) {
+    if (try_skinny_dma(p, stream)) return finish("block-scaled GEMM launch");
     if (a8 && b8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, stream);
     else if (a8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, stream);
     else if (b8) launch_skinny_m<FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, stream);
