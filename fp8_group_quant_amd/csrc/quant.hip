@@ -70,17 +70,18 @@ struct Raw16<FP8Q_DTYPE_F16> { u32x4 w[2]; };
 template <>
 struct Raw16<FP8Q_DTYPE_F32> { f32x4 w[4]; };
 
-// Inputs are streamed once: non-temporal 16-byte loads of adjacent addresses.
+// 16-byte loads of adjacent addresses with the default cache policy (measured ~6% faster
+// than non-temporal loads on MI355X, although the input is read once).
 template <int DT>
 __device__ __forceinline__ void load_raw(const void* base, int64_t idx, Raw16<DT>& r) {
   if constexpr (DT == FP8Q_DTYPE_F32) {
     const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
 #pragma unroll
-    for (int h = 0; h < 4; h++) r.w[h] = __builtin_nontemporal_load(p + h);
+    for (int h = 0; h < 4; h++) r.w[h] = p[h];
   } else {
     const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx);
-    r.w[0] = __builtin_nontemporal_load(p);
-    r.w[1] = __builtin_nontemporal_load(p + 1);
+    r.w[0] = p[0];
+    r.w[1] = p[1];
   }
 }
 
