@@ -16,13 +16,17 @@
 //     is one fma per accumulator per K block, in fp32 registers.
 //   - MX32 uses the scaled form of the same instruction: the E8M0 bytes of each 16-row
 //     slice and 32-wide K block are applied by the matrix core, and accumulation runs
-//     across the whole K loop inside the MFMA with no fold.
+//     across the whole K loop inside the MFMA with no fold. BLOCK128 with UE8M0 activation
+//     scales uses it too, for the activation side only: the fold then multiplies by the
+//     fp32 weight-block scale, one value per wavefront.
 //   - K layout inside a lane (measured on gfx950): lane l of a 16x16x128 operand holds row
 //     l%16 and two 16-byte runs of K, at 16*(l/16) and 64 + 16*(l/16); the E8M0 scale for
 //     (row i, 32-wide block b) comes from lane i + 16*b.
-//   - 256x128 output tiles, 8 wavefronts of 64(m) x 64(n), K step 128. LDS rows are 128
-//     bytes with the 16-byte chunk index XOR-swizzled by (row/2)%8, which keeps the 16
-//     rows read by one fragment load on distinct banks without padding.
+//   - 256x128 output tiles, 8 wavefronts of 64(m) x 64(n), K step 128; large flat
+//     problems use 256x256 tiles, 8 wavefronts of 128(m) x 64(n), which load a third fewer
+//     operand bytes per output. LDS rows are 128 bytes with the 16-byte chunk index
+//     XOR-swizzled by (row/2)%8, which keeps the 16 rows read by one fragment load on
+//     distinct banks without padding.
 //   - Two ways to fill LDS. The main kernel loads operand tiles and scales straight into
 //     LDS (global_load_lds) through three stages with one barrier per step, so loads have
 //     two steps to land and the next step's first operands are read during the current
@@ -148,11 +152,14 @@ struct TileRegs {
 
 // MFMA operand fragment of 16 rows starting at row r (lane l: row r + l%16, K runs at
 // 16*(l/16) and 64 + 16*(l/16)).
+// r is a multiple of 16, so swz(r + lane%16) = swz(lane%16): the lane part of the address
+// is the same for every fragment of a tile and r*BK can go into the instruction's offset.
 __device__ __forceinline__ v8i frag(const uint8_t* tile, int r, int lane) {
-  const int row = r + (lane & 15);
-  const int c = lane >> 4;
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * BK + ((c ^ swz(row)) << 4));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + row * BK + (((c + 4) ^ swz(row)) << 4));
+  const int l = lane & 15, c = lane >> 4;
+  const uint8_t* rp = tile + r * BK;
+  const int lo_off = l * BK + ((c ^ swz(l)) << 4), hi_off = l * BK + (((c + 4) ^ swz(l)) << 4);
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(rp + lo_off);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(rp + hi_off);
   v8i v;
   v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
   v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
@@ -513,6 +520,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 // first operands of step kb+1 are read into registers while the last row's MFMAs run.
 // A load therefore has two steps to land.
 //
+// 256x256 tiles need 64 KB per step, so only two stages fit: step kb+2 is loaded into
+// stage kb%2 after the barrier of step kb and has one (twice as long) step to land.
+//
 // The loads are written as inline assembly so that the compiler, which cannot tell LDS
 // stages apart, does not wait for them before unrelated LDS reads; the waits are explicit
 // (s_waitcnt vmcnt) and the K loop contains no other vector-memory instruction, so the
@@ -535,18 +545,25 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 // still issues the same loads.
 enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp = 4 };
 
-constexpr int kDmaStages = 3;
-
-template <int SCM>
+// LDS layout of the direct-to-LDS kernel for tile shape C: kStages stages, each holding
+// both operand tiles of one K step and (per-step scale modes) the step's scales, followed
+// by a spare word per lane. 256x128 tiles use three stages; 256x256 tiles (two weight
+// blocks per tile) fit two.
+template <int SCM, class C>
 struct DmaLayout {
   static constexpr bool kGrouped = SCM == kScF32Grp || SCM == kScMxGrp;
-  static constexpr int kScOff = 256 * BK + 128 * BK;  // per-step modes: scale area inside a stage
-  static constexpr int kStage = kScOff + (kGrouped ? 0 : 1792);  // (+ a spare word per lane)
-  static constexpr int kRing = kDmaStages * kStage;  // grouped modes: two slots, then the dummy area
+  static constexpr int kStages = C::BN == 256 ? 2 : 3;
+  static constexpr int kScOff = C::BM * BK + C::BN * BK;  // per-step modes: scale area inside a stage
+  static constexpr int kScArea = C::BN == 256 ? 2304 : 1792;
+  static constexpr int kSpare = kScArea - 256;  // the spare word of each lane
+  static constexpr int kStage = kScOff + (kGrouped ? 0 : kScArea);
+  static constexpr int kRing = kStages * kStage;  // grouped modes: two slots, then the dummy area
   static constexpr int kSlot = 6144;
   static constexpr int kDummy = kRing + 2 * kSlot;
-  static constexpr int kBytes = kGrouped ? kDummy + 1024 : kDmaStages * kStage;
+  static constexpr int kBytes = kGrouped ? kDummy + 1024 : kStages * kStage;
   static constexpr int kMaxPrefix = kGrouped ? 700 : 2048;  // masked launches: at most this many experts
+  static_assert(!kGrouped || C::BN == 128, "grouped scale modes use 256x128 tiles");
+  static_assert(kBytes + 4 * (kMaxPrefix + 1) <= 160 * 1024, "LDS");
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -571,19 +588,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Tile shape of the direct-to-LDS kernel: 256x128 outputs per workgroup, 8 wave tiles of
-// 64(m) x 64(n). (One wavefront per SIMD with 128x64 wave tiles reads 25% less from LDS
-// but measured slower here: no second wavefront covers a stall.)
+// Tile shapes of the direct-to-LDS kernel: 256x128 outputs per workgroup as 8 wave tiles
+// of 64(m) x 64(n), or 256x256 as 8 wave tiles of 128(m) x 64(n). (One wavefront per SIMD
+// with 128x64 wave tiles in a 256x128 tile reads 25% less from LDS but measured slower:
+// no second wavefront covers a stall.)
 using DmaCfg = TileCfg<256, 128, 4, 2, 4>;
+using DmaCfgW = TileCfg<256, 256, 2, 4, 4>;
 
 // Per-tile state of the direct-to-LDS loop.
 template <class C, int SCM>
 struct DmaRun {
-  using L = DmaLayout<SCM>;
+  using L = DmaLayout<SCM, C>;
+  static constexpr int kStages = L::kStages;
   static constexpr bool MX = SCM == kScMx || SCM == kScMxGrp;
   static constexpr bool F32 = SCM == kScF32Row || SCM == kScF32Grp;
+  // UE8M0 activation scales are powers of two: the matrix core applies them (E8M0 operand
+  // scale of the activation rows, weights at 2^0), and the fold multiplies by the
+  // weight-block scale alone, the same for every lane. P * 2^e * sb rounds exactly like
+  // P * (2^e * sb), so the result is the same as folding the product of both scales.
+  static constexpr bool E8 = SCM == kScE8Col;
   static constexpr int SM = C::SM, SN = C::SN;
-  static_assert(C::BM == 256 && C::BN == 128 && SN == 4 && C::WTN == 64, "256x128 tiles, 64-wide wave tiles");
+  static_assert(C::BM == 256 && SN == 4 && C::WTN == 64, "256-row tiles, 64-wide wave tiles");
   static constexpr int kW = C::kWaves;
   static constexpr int kLA = (C::BM / 8) / kW, kLB = (C::BN / 8) / kW;  // 1 KB blocks per wave
   static constexpr int kSc = L::kGrouped ? 1 : 8 / kW;                // scale jobs per wave
@@ -616,9 +641,13 @@ struct DmaRun {
   float sa[SM], sb;
   uint32_t ea[SM], eb[SN];
   v4f acc[SM][SN];
-  // BLOCK128 fold pipeline: the product of MFMA g (counted across steps) sits in
-  // pr[g % 3] and is folded two MFMAs later; the last two of a step are folded at the
-  // start of the next one with that step's last-row factor pend_s.
+  // BLOCK128 fold pipeline: the product of MFMA t of a step from stage S sits in
+  // pr[(kSlot0 * S + t) % 3] and is folded two MFMAs later; the last two of a step are
+  // folded at the start of the next one with that step's last-row factor pend_s. With
+  // three stages the numbering runs on across steps (3 steps hold a multiple of 3 MFMAs);
+  // with two, each step starts at slot 0 and first moves the two pending products to
+  // the slots of MFMAs -2 and -1.
+  static constexpr int kSlot0 = kStages == 3 ? kPerStep : 0;
   v4f pr[3];
   float pend_s;
 
@@ -675,9 +704,11 @@ struct DmaRun {
         if constexpr (F32)
           sa[i] = reinterpret_cast<const float*>(sc)[row];
         else
-          sa[i] = scale_value<FP8Q_SCALE_UE8M0>(sc[row]);
+          ea[i] = sc[row];
       }
-      sb = reinterpret_cast<const float*>(sc + 1024)[0];
+      // the weight-block scale of this wave's 64 columns (one word per 128-column block;
+      // every lane reads the same word)
+      sb = reinterpret_cast<const float*>(sc + 1024 + ((wn * C::WTN) / 128) * 256)[0];
     }
   }
 
@@ -687,7 +718,7 @@ struct DmaRun {
 #pragma unroll
     for (int j = 0; j < SN; j++) wf[j] = frag(s + 256 * BK, wn * 64 + j * 16, lane);
     x0 = frag(s, wm * C::WTM, lane);
-    x1 = frag(s, wm * C::WTM + 16, lane);
+    if constexpr (kAhead == 2) x1 = frag(s, wm * C::WTM + 16, lane);
     load_scales(st, 0);
   }
 
@@ -703,13 +734,17 @@ struct DmaRun {
                                                                    static_cast<int>(ebs[j]), 0,
                                                                    static_cast<int>(eas[i]));
     } else {
-      constexpr int g = kPerStep * S + T;  // MFMA index mod 3 (steps of stage S are kb = S mod 3)
+      constexpr int g = kSlot0 * S + T;
       constexpr int slot = g % 3, pslot = (g + 1) % 3;
       constexpr int ip = T >= 2 ? (T - 2) / 4 : SM - 1;
       constexpr int jp = T >= 2 ? (T - 2) % 4 : T + 2;
       const float sp = T >= 2 ? f[ip] : pend_s;
       const v4f z = {0.f, 0.f, 0.f, 0.f};
-      pr[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
+      if constexpr (E8)
+        pr[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 127, 0,
+                                                                    static_cast<int>(eas[i]));
+      else
+        pr[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; r++) acc[ip][jp][r] = fmaf(pr[pslot][r], sp, acc[ip][jp][r]);
     }
@@ -726,14 +761,19 @@ struct DmaRun {
     mf<S, NXT, 4 * I + 3>(xf, f, eas, ebs);
   }
 
-  // rows 0..SM-2 of a step; row I first reads the activation fragment of row I+2
+  // Activation fragments are read kAhead rows before their MFMAs (the first kAhead of a
+  // step during the previous step's last row): two rows for 64-row wave tiles, one for
+  // 128-row wave tiles, whose accumulators leave no room for more.
+  static constexpr int kAhead = SM >= 8 ? 1 : 2;
+
+  // rows 0..SM-2 of a step; row I first reads the activation fragment of row I+kAhead
   template <int S, int... I>
   __device__ __forceinline__ void rows(v8i (&xs)[SM], const float (&f)[SM], std::integer_sequence<int, I...>) {
     ((pre<S, I>(xs), row<S, -1, I>(xs[I], f, ea, eb)), ...);
   }
   template <int S, int I>
   __device__ __forceinline__ void pre(v8i (&xs)[SM]) {
-    if constexpr (I + 2 < SM) xs[I + 2] = frag(stage(S), wm * C::WTM + (I + 2) * 16, lane);
+    if constexpr (I + kAhead < SM) xs[I + kAhead] = frag(stage(S), wm * C::WTM + (I + kAhead) * 16, lane);
   }
 
   // the folds still pending after the last step (which used stage S)
@@ -741,7 +781,7 @@ struct DmaRun {
   __device__ __forceinline__ void drain() {
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-      const int slot = (kPerStep * S + kPerStep - 2 + q) % 3;
+      const int slot = (kSlot0 * S + kPerStep - 2 + q) % 3;
 #pragma unroll
       for (int r = 0; r < 4; r++) acc[SM - 1][2 + q][r] = fmaf(pr[slot][r], pend_s, acc[SM - 1][2 + q][r]);
     }
@@ -751,36 +791,48 @@ struct DmaRun {
   // the next step's first operands, the last row.
   template <int S>
   __device__ __forceinline__ void step(int kb) {
-    constexpr int NX = (S + 1) % kDmaStages;
+    constexpr int NX = (S + 1) % kStages;
     float f[SM];
     if constexpr (!MX) {
+      // two stages: the previous step's last two products move to the slots of MFMAs -2 and -1
+      constexpr int s0 = (kPerStep - 2) % 3, s1 = (kPerStep - 1) % 3;
+      if constexpr (kStages == 2 && (s0 != 1 || s1 != 2)) {
+        const v4f p0 = pr[s0], p1 = pr[s1];
+        pr[1] = p0;
+        pr[2] = p1;
+      }
+      // (E8: one value for the wave, moved to a scalar register here rather than where it
+      // is read, so the last row of the previous step does not wait for that read)
+      const float sbs = E8 ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sb))) : sb;
 #pragma unroll
-      for (int i = 0; i < SM; i++) f[i] = sa[i] * sb;
+      for (int i = 0; i < SM; i++) f[i] = E8 ? sbs : sa[i] * sbs;
     }
     v8i xs[SM];
     xs[0] = x0;
-    xs[1] = x1;
+    if constexpr (kAhead == 2) xs[1] = x1;
     rows<S>(xs, f, std::make_integer_sequence<int, SM - 1>{});
-    // Every load of step kb+1 by this wave has landed (only step kb+2's group, issued
-    // later, may still be in flight), and its reads of stage S are done.
-    wait_vmcnt<kGroup>();
+    // Every load of step kb+1 by this wave has landed (with three stages, only step
+    // kb+2's group, issued later, may still be in flight), and its reads of stage S are done.
+    wait_vmcnt<(kStages - 2) * kGroup>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // Past the end the step index is clamped: the stage it fills is never read again,
     // and every step keeps the same load count and no branch.
-    issue(S, min(kb + 3, nkb - 1));
+    issue(S, min(kb + kStages, nkb - 1));
     uint32_t ea_c[SM], eb_c[SN];
-    if constexpr (MX) {
+    if constexpr (MX || E8) {
 #pragma unroll
       for (int i = 0; i < SM; i++) ea_c[i] = ea[i];
+    }
+    if constexpr (MX) {
 #pragma unroll
       for (int j = 0; j < SN; j++) eb_c[j] = eb[j];
     }
     // the next step's first activation fragments and scales, into registers freed by
     // rows 0 and 1, in flight during the whole last row
     x0 = frag(stage(NX), wm * C::WTM, lane);
-    x1 = frag(stage(NX), wm * C::WTM + 16, lane);
+    if constexpr (kAhead == 2) x1 = frag(stage(NX), wm * C::WTM + 16, lane);
     load_scales(NX, kb + 1);
     __builtin_amdgcn_sched_barrier(0);
     row<S, NX, SM - 1>(xs[SM - 1], f, ea_c, eb_c);
@@ -818,13 +870,14 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
     r.b_off[q] = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.ldb + c * 16);
   }
   // Scale job js = q * kW + wave (8 per step). Default: 4 bytes of A into the spare area.
+  constexpr int kNb = C::BN / 128;  // weight blocks per tile
 #pragma unroll
   for (int q = 0; q < R::kSc; q++) {
     const int js = q * R::kW + wave;
     r.s_base[q] = r.a_base;
     r.s_off[q] = 0;
     r.s_step[q] = 0;
-    r.s_lds[q] = 1536;
+    r.s_lds[q] = R::L::kSpare;
     if constexpr (SCM == kScF32Row) {
       if (js < 4) {  // fp32 scale of tile row 64 js + lane
         const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
@@ -850,7 +903,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm);
         r.s_step[q] = 4;
         r.s_lds[q] = js * 256;
-      } else if (js < 6) {  // and of B row 64 (js-4) + lane
+      } else if (js < 4 + C::BN / 64) {  // and of B row 64 (js-4) + lane
         const uint8_t* SB = static_cast<const uint8_t*>(p.sb);
         const int row = (js - 4) * 64 + lane;
         r.s_base[q] = SB + n0 * p.sb_sn;
@@ -860,14 +913,16 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
       }
     }
     if constexpr (SCM == kScF32Row || SCM == kScE8Col) {
-      // the weight-block scale, one fp32 word per step (every lane loads it; the word
-      // lands 64 times in [1024, 1280) of the scale area)
-      if (js == (SCM == kScF32Row ? 4 : 1)) {
+      // the scale of weight block nb of the tile, one fp32 word per step (every lane loads
+      // it; the word lands 64 times in [1024 + 256 nb, +256) of the scale area). A block
+      // past the last column reloads the last block's word.
+      const int nb = js - (SCM == kScF32Row ? 4 : 1);
+      if (nb >= 0 && nb < kNb) {
         const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
-        r.s_base[q] = SB + (n0 / 128) * p.sb_sn * 4;
+        r.s_base[q] = SB + min(n0 / 128 + nb, nmax / 128) * p.sb_sn * 4;
         r.s_off[q] = 0;
         r.s_step[q] = p.sb_sk * 4;
-        r.s_lds[q] = 1024;
+        r.s_lds[q] = 1024 + 256 * nb;
       }
     }
   }
@@ -925,21 +980,32 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   const int nkb = r.nkb;
   r.issue(0, 0);
   r.issue(1, min(1, nkb - 1));
-  r.issue(2, min(2, nkb - 1));
-  wait_vmcnt<2 * R::kGroup>();  // step 0 has landed; steps 1 and 2 may be in flight
+  if constexpr (R::kStages == 3) {
+    r.issue(2, min(2, nkb - 1));
+    wait_vmcnt<2 * R::kGroup>();  // step 0 has landed; steps 1 and 2 may be in flight
+  } else {
+    wait_vmcnt<R::kGroup>();  // step 0 has landed; step 1 may be in flight
+  }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   r.load_ops(0);
-  for (int kb = 0; kb < nkb; kb += 3) {
-    r.template step<0>(kb);
-    if (kb + 1 < nkb) r.template step<1>(kb + 1);
-    if (kb + 2 < nkb) r.template step<2>(kb + 2);
+  if constexpr (R::kStages == 3) {
+    for (int kb = 0; kb < nkb; kb += 3) {
+      r.template step<0>(kb);
+      if (kb + 1 < nkb) r.template step<1>(kb + 1);
+      if (kb + 2 < nkb) r.template step<2>(kb + 2);
+    }
+  } else {
+    for (int kb = 0; kb < nkb; kb += 2) {
+      r.template step<0>(kb);
+      if (kb + 1 < nkb) r.template step<1>(kb + 1);
+    }
   }
   if constexpr (!R::MX) {  // the last step's last two folds are still pending
-    const int s_last = (nkb - 1) % kDmaStages;
+    const int s_last = (nkb - 1) % R::kStages;
     if (s_last == 0) r.template drain<0>();
     else if (s_last == 1) r.template drain<1>();
-    else r.template drain<2>();
+    else r.template drain<2 % R::kStages>();
   }
   // no load is in flight and nobody reads a stage any more before the next tile's loads
   wait_vmcnt<0>();
@@ -972,14 +1038,14 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   }
 }
 
-template <int SCM>
-__global__ __launch_bounds__(DmaCfg::kThreads, 1) void gemm_dma_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DmaLayout<SCM>::kBytes];
-  __shared__ int32_t pref[DmaLayout<SCM>::kMaxPrefix + 1];  // masked only, E + 1 entries
+template <int SCM, class C>
+__global__ __launch_bounds__(C::kThreads, 1) void gemm_dma_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DmaLayout<SCM, C>::kBytes];
+  __shared__ int32_t pref[DmaLayout<SCM, C>::kMaxPrefix + 1];  // masked only, E + 1 entries
   int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch, used before any load
-  const TileRange tr(build_tile_list<DmaCfg>(p, part, pref));
+  const TileRange tr(build_tile_list<C>(p, part, pref));
   for (int64_t t = tr.beg; t < tr.end; t += tr.stride)
-    run_tile_dma<DmaCfg, SCM>(p, smem, tile_at<DmaCfg>(p, pref, t));
+    run_tile_dma<C, SCM>(p, smem, tile_at<C>(p, pref, t));
 }
 
 // ------------------------------------------------------------------ skinny GEMM (small M)
@@ -1341,18 +1407,18 @@ int dma_mode(const GemmParams& p, bool mx) {
     if (p.sa_sm >= (int64_t(1) << 22)) return -1;
     const bool grp = k512 && p.sa_sk == 1 && p.sa_sm % 4 == 0 && a16(p.sa) && p.sb_sk == 1 && p.sb_sn % 4 == 0 &&
                      a16(p.sb) && (E == 1 || (p.sa_se % 4 == 0 && p.sb_se % 4 == 0)) &&
-                     E <= DmaLayout<kScF32Grp>::kMaxPrefix;
+                     E <= DmaLayout<kScF32Grp, DmaCfg>::kMaxPrefix;
     if (grp) return kScF32Grp;
-    return E <= DmaLayout<kScF32Row>::kMaxPrefix ? kScF32Row : -1;
+    return E <= DmaLayout<kScF32Row, DmaCfg>::kMaxPrefix ? kScF32Row : -1;
   }
   const bool col = p.sa_sm == 1 && p.sa_sk % 4 == 0 && p.M % 4 == 0 && u32_ok(p.sa) &&
-                   (p.masked_m == nullptr || p.sa_se % 4 == 0) && E <= DmaLayout<kScE8Col>::kMaxPrefix;
+                   (p.masked_m == nullptr || p.sa_se % 4 == 0) && E <= DmaLayout<kScE8Col, DmaCfg>::kMaxPrefix;
   return col ? kScE8Col : -1;
 }
 
-template <int SCM>
+template <int SCM, class C = DmaCfg>
 void launch_dma(const GemmParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_dma_kernel<SCM>), dim3(grid), dim3(DmaCfg::kThreads), 0, s, p);
+  hipLaunchKernelGGL((gemm_dma_kernel<SCM, C>), dim3(grid), dim3(C::kThreads), 0, s, p);
 }
 
 }  // namespace
@@ -1378,6 +1444,17 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
     return finish("block-scaled GEMM launch");
   }
   const int dm = dma_mode(p, false);
+  if (!p.masked_m && (dm == kScE8Col || dm == kScF32Row)) {
+    // 256x256 tiles halve the operand bytes each tile loads per output; used when they
+    // still give every CU a tile
+    using W = DmaCfgW;
+    const int64_t wt = ((p.M + W::BM - 1) / W::BM) * ((p.N + W::BN - 1) / W::BN);
+    if (wt >= kCUs) {
+      if (dm == kScE8Col) launch_dma<kScE8Col, W>(p, grid_for(wt), stream);
+      else launch_dma<kScF32Row, W>(p, grid_for(wt), stream);
+      return finish("block-scaled GEMM launch");
+    }
+  }
   if (dm == kScF32Row) launch_dma<kScF32Row>(p, grid, stream);
   else if (dm == kScF32Grp) launch_dma<kScF32Grp>(p, grid, stream);
   else if (dm == kScE8Col) launch_dma<kScE8Col>(p, grid, stream);

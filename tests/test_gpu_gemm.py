@@ -88,6 +88,33 @@ def test_ragged_shapes_full(M, N, K, sa_kind, sb_kind):
     check(y, ys, ss, K, f"{M}x{N}x{K}")
 
 
+# Flat problems with at least 256 tiles of 256x256 take the two-stage kernel with
+# 256-column tiles (fp32 weight scales; fp32 row or UE8M0 column activation scales, K not
+# a multiple of 512 for fp32 ones). M=4000, N=4200 leaves ragged tiles in both directions;
+# K = 128, 256, 384 run 1, 2 and 3 steps (pipelines shorter than two stages, and both
+# stages ending the loop). Outputs on a grid of rows x columns through tile and wave-tile
+# boundaries plus random ones are compared; every output must be written.
+@pytest.mark.parametrize("K", [128, 256, 384])
+@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col"])
+def test_wide_tiles_ragged_sampled(K, sa_kind):
+    M, N = 4000, 4200
+    w = synth.Workload("t", seed=60 + K, M=M, K=K, N=N, scale_fmt=sa_kind.split("-")[0])
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    layout = sa_kind.split("-")[1]
+    sa_store = sa if layout == "row" else np.ascontiguousarray(sa.T)
+    y = _gpu_block(a, sa_store, b, sb, layout)
+    assert not np.any(y == SENT)
+    g = np.random.default_rng(K)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, 255, 256, 257, 511, 512, 3839, 3840, 3841,
+                                      3967, 3968, 3998, 3999], g.integers(0, M, 46)]))
+    cols = np.unique(np.concatenate([[0, 63, 64, 127, 128, 129, 191, 192, 255, 256, 4095, 4096, 4097,
+                                      4159, 4160, 4198, 4199], g.integers(0, N, 47)]))
+    ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
+    ys, ss = oracle.gemm_block128(a, sa_store, b, sb, _fmt(sa), layout, oracle.SCALE_F32, at=(ms, ns))
+    check(y[ms, ns], ys, ss, K, f"wide {M}x{N}x{K} {sa_kind}")
+
+
 def test_padded_output_rows_untouched():
     w = synth.Workload("t", seed=50, M=70, K=256, N=130, scale_fmt="f32")
     a, sa = synth.gemm_activation(w)
