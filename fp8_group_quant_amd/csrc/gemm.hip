@@ -552,7 +552,7 @@ enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp
 template <int SCM, class C>
 struct DmaLayout {
   static constexpr bool kGrouped = SCM == kScF32Grp || SCM == kScMxGrp;
-  static constexpr int kStages = C::BN == 256 ? 2 : 3;
+  static constexpr int kStages = C::BM * BK + C::BN * BK > 48 * 1024 ? 2 : 3;
   static constexpr int kScOff = C::BM * BK + C::BN * BK;  // per-step modes: scale area inside a stage
   static constexpr int kScArea = C::BN == 256 ? 2304 : 1792;
   static constexpr int kSpare = kScArea - 256;  // the spare word of each lane
@@ -589,11 +589,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Tile shapes of the direct-to-LDS kernel: 256x128 outputs per workgroup as 8 wave tiles
-// of 64(m) x 64(n), or 256x256 as 8 wave tiles of 128(m) x 64(n). (One wavefront per SIMD
+// of 64(m) x 64(n); 256x256 as 8 wave tiles of 128(m) x 64(n); 128x256 as 8 wave tiles of
+// 64x64 (masked launches: less padding in experts with few rows). (One wavefront per SIMD
 // with 128x64 wave tiles in a 256x128 tile reads 25% less from LDS but measured slower:
 // no second wavefront covers a stall.)
 using DmaCfg = TileCfg<256, 128, 4, 2, 4>;
 using DmaCfgW = TileCfg<256, 256, 2, 4, 4>;
+using DmaCfgT = TileCfg<128, 256, 2, 4, 4>;
 
 // Per-tile state of the direct-to-LDS loop.
 template <class C, int SCM>
@@ -608,7 +610,7 @@ struct DmaRun {
   // P * (2^e * sb), so the result is the same as folding the product of both scales.
   static constexpr bool E8 = SCM == kScE8Col;
   static constexpr int SM = C::SM, SN = C::SN;
-  static_assert(C::BM == 256 && SN == 4 && C::WTN == 64, "256-row tiles, 64-wide wave tiles");
+  static_assert((C::BM == 256 || C::BM == 128) && SN == 4 && C::WTN == 64, "64-wide wave tiles");
   static constexpr int kW = C::kWaves;
   static constexpr int kLA = (C::BM / 8) / kW, kLB = (C::BN / 8) / kW;  // 1 KB blocks per wave
   static constexpr int kSc = L::kGrouped ? 1 : 8 / kW;                // scale jobs per wave
@@ -647,8 +649,11 @@ struct DmaRun {
   // three stages the numbering runs on across steps (3 steps hold a multiple of 3 MFMAs);
   // with two, each step starts at slot 0 and first moves the two pending products to
   // the slots of MFMAs -2 and -1.
+  static constexpr int kLag = 3;  // MFMAs between a product and its fold
+  static constexpr int kRingN = kLag + 1;
+  static_assert(kLag == 2 || kPerStep % kRingN == 0, "ring numbering must run on across steps");
   static constexpr int kSlot0 = kStages == 3 ? kPerStep : 0;
-  v4f pr[3];
+  v4f pr[kRingN];
   float pend_s;
 
   __device__ __forceinline__ void issue(int st, int kb) {
@@ -658,7 +663,7 @@ struct DmaRun {
     for (int q = 0; q < kLA; q++) dma16(base + (wave * kLA + q) * 1024, ap, a_off[q]);
     const uint8_t* bp = b_base + kb * BK;
 #pragma unroll
-    for (int q = 0; q < kLB; q++) dma16(base + 256 * BK + (wave * kLB + q) * 1024, bp, b_off[q]);
+    for (int q = 0; q < kLB; q++) dma16(base + C::BM * BK + (wave * kLB + q) * 1024, bp, b_off[q]);
     if constexpr (L::kGrouped) {
       // tiles of step kb carry scale group (kb+2)/4 when kb%4 == 2 (groups 0 and 1 with
       // the first two steps); the group index is clamped (a reload writes equal bytes)
@@ -703,8 +708,10 @@ struct DmaRun {
         const int row = wm * C::WTM + i * 16 + (lane & 15);
         if constexpr (F32)
           sa[i] = reinterpret_cast<const float*>(sc)[row];
-        else
+        else if constexpr (E8)
           ea[i] = sc[row];
+        else
+          sa[i] = scale_value<FP8Q_SCALE_UE8M0>(sc[row]);
       }
       // the weight-block scale of this wave's 64 columns (one word per 128-column block;
       // every lane reads the same word)
@@ -716,7 +723,7 @@ struct DmaRun {
   __device__ __forceinline__ void load_ops(int st) {
     const uint8_t* s = stage(st);
 #pragma unroll
-    for (int j = 0; j < SN; j++) wf[j] = frag(s + 256 * BK, wn * 64 + j * 16, lane);
+    for (int j = 0; j < SN; j++) wf[j] = frag(s + C::BM * BK, wn * 64 + j * 16, lane);
     x0 = frag(s, wm * C::WTM, lane);
     if constexpr (kAhead == 2) x1 = frag(s, wm * C::WTM + 16, lane);
     load_scales(st, 0);
@@ -735,10 +742,10 @@ struct DmaRun {
                                                                    static_cast<int>(eas[i]));
     } else {
       constexpr int g = kSlot0 * S + T;
-      constexpr int slot = g % 3, pslot = (g + 1) % 3;
-      constexpr int ip = T >= 2 ? (T - 2) / 4 : SM - 1;
-      constexpr int jp = T >= 2 ? (T - 2) % 4 : T + 2;
-      const float sp = T >= 2 ? f[ip] : pend_s;
+      constexpr int slot = g % kRingN, pslot = (g + 1) % kRingN;
+      constexpr int ip = T >= kLag ? (T - kLag) / 4 : SM - 1;
+      constexpr int jp = T >= kLag ? (T - kLag) % 4 : 4 - kLag + T;
+      const float sp = T >= kLag ? f[ip] : pend_s;
       const v4f z = {0.f, 0.f, 0.f, 0.f};
       if constexpr (E8)
         pr[slot] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, z, 0, 0, 0, 127, 0,
@@ -748,7 +755,7 @@ struct DmaRun {
 #pragma unroll
       for (int r = 0; r < 4; r++) acc[ip][jp][r] = fmaf(pr[pslot][r], sp, acc[ip][jp][r]);
     }
-    if constexpr (NXT >= 0) wf[j] = frag(stage(NXT) + 256 * BK, wn * 64 + j * 16, lane);
+    if constexpr (NXT >= 0) wf[j] = frag(stage(NXT) + C::BM * BK, wn * 64 + j * 16, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -761,10 +768,9 @@ struct DmaRun {
     mf<S, NXT, 4 * I + 3>(xf, f, eas, ebs);
   }
 
-  // Activation fragments are read kAhead rows before their MFMAs (the first kAhead of a
-  // step during the previous step's last row): two rows for 64-row wave tiles, one for
-  // 128-row wave tiles, whose accumulators leave no room for more.
-  static constexpr int kAhead = SM >= 8 ? 1 : 2;
+  // Activation fragments are read kAhead = 2 rows before their MFMAs (the first two of a
+  // step during the previous step's last row).
+  static constexpr int kAhead = 2;
 
   // rows 0..SM-2 of a step; row I first reads the activation fragment of row I+kAhead
   template <int S, int... I>
@@ -780,10 +786,11 @@ struct DmaRun {
   template <int S>
   __device__ __forceinline__ void drain() {
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-      const int slot = (kSlot0 * S + kPerStep - 2 + q) % 3;
+    for (int q = 0; q < kLag; q++) {
+      const int slot = (kSlot0 * S + kPerStep - kLag + q) % kRingN;
 #pragma unroll
-      for (int r = 0; r < 4; r++) acc[SM - 1][2 + q][r] = fmaf(pr[slot][r], pend_s, acc[SM - 1][2 + q][r]);
+      for (int r = 0; r < 4; r++)
+        acc[SM - 1][4 - kLag + q][r] = fmaf(pr[slot][r], pend_s, acc[SM - 1][4 - kLag + q][r]);
     }
   }
 
@@ -796,7 +803,7 @@ struct DmaRun {
     if constexpr (!MX) {
       // two stages: the previous step's last two products move to the slots of MFMAs -2 and -1
       constexpr int s0 = (kPerStep - 2) % 3, s1 = (kPerStep - 1) % 3;
-      if constexpr (kStages == 2 && (s0 != 1 || s1 != 2)) {
+      if constexpr (kLag == 2 && kStages == 2 && (s0 != 1 || s1 != 2)) {
         const v4f p0 = pr[s0], p1 = pr[s1];
         pr[1] = p0;
         pr[2] = p1;
@@ -971,10 +978,9 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   for (int i = 0; i < C::SM; i++)
 #pragma unroll
     for (int j = 0; j < C::SN; j++) r.acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  // the folds at the start of the first step add 0 * 0 (MFMAs -2 and -1)
-  r.pr[0] = v4f{0.f, 0.f, 0.f, 0.f};
-  r.pr[1] = r.pr[0];
-  r.pr[2] = r.pr[0];
+  // the folds at the start of the first step add 0 * 0 (MFMAs -kLag .. -1)
+#pragma unroll
+  for (int q = 0; q < R::kRingN; q++) r.pr[q] = v4f{0.f, 0.f, 0.f, 0.f};
   r.pend_s = 0.f;
 
   const int nkb = r.nkb;
@@ -1444,6 +1450,15 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
     return finish("block-scaled GEMM launch");
   }
   const int dm = dma_mode(p, false);
+  if (p.masked_m && (dm == kScE8Col || dm == kScF32Row)) {
+    // masked: 128-row tiles pad an expert's rows to a multiple of 128 instead of 256
+    using T = DmaCfgT;
+    const int64_t rows = expected_m > 0 ? std::min<int64_t>(expected_m, p.M) : p.M;
+    const int64_t tt = p.E * ((rows + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
+    if (dm == kScE8Col) launch_dma<kScE8Col, T>(p, grid_for(tt), stream);
+    else launch_dma<kScF32Row, T>(p, grid_for(tt), stream);
+    return finish("block-scaled grouped GEMM launch");
+  }
   if (!p.masked_m && (dm == kScE8Col || dm == kScF32Row)) {
     // 256x256 tiles halve the operand bytes each tile loads per output; used when they
     // still give every CU a tile

@@ -200,6 +200,28 @@ def test_masked_small_full():
         assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
 
 
+def test_masked_f32_row_scales():
+    """fp32 activation scales stored row-major per expert ([E][cap][K/128]); K not a multiple
+    of 512 selects the per-step scale loads; counts around the 128-row tile boundary."""
+    E, cap, N, K = 4, 260, 384, 384
+    w = synth.Workload("m", seed=62, M=cap, K=K, N=N, E=E, scale_fmt="f32", layout="row", masked=True)
+    ops = [synth.gemm_activation(w, e) + synth.weights(w, e) for e in range(E)]
+    a, sa, b, sb = (np.stack([o[i] for o in ops]) for i in range(4))
+    mm = np.array([260, 0, 129, 37], dtype=np.int32)
+    f = fq()
+    y = torch.full((E, cap, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_grouped_gemm_masked(_dev(a), _dev(sa), _dev(b), _dev(sb), y.view(torch.bfloat16),
+                               _dev(mm), 0)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().view(np.uint16)
+    for e in range(E):
+        r = mm[e]
+        if r > 0:
+            ys, ss = oracle.gemm_block128(a[e, :r], sa[e, :r], b[e], sb[e], oracle.SCALE_F32, "row")
+            check(y[e, :r], ys, ss, K, f"expert {e}")
+        assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
+
+
 def test_masked_result_independent_of_expected_m():
     E, cap, N, K = 6, 300, 384, 256
     a, sa, b, sb = _masked_operands(E, cap, N, K, 61)
