@@ -562,7 +562,7 @@ struct DmaLayout {
   static constexpr int kDummy = kRing + 2 * kSlot;
   static constexpr int kBytes = kGrouped ? kDummy + 1024 : kStages * kStage;
   static constexpr int kMaxPrefix = kGrouped ? 700 : 2048;  // masked launches: at most this many experts
-  static_assert(!kGrouped || C::BN == 128, "grouped scale modes use 256x128 tiles");
+  static_assert(SCM != kScMxGrp || C::BN == 128, "grouped MX32 scales use 256x128 tiles");
   static_assert(kBytes + 4 * (kMaxPrefix + 1) <= 160 * 1024, "LDS");
 };
 
@@ -692,7 +692,7 @@ struct DmaRun {
       } else {
 #pragma unroll
         for (int i = 0; i < SM; i++) sa[i] = reinterpret_cast<const float*>(ring)[4 * (wm * C::WTM + i * 16 + (lane & 15)) + q];
-        sb = reinterpret_cast<const float*>(ring + 4096)[q];
+        sb = reinterpret_cast<const float*>(ring + 4096 + ((wn * C::WTN) / 128) * 1024)[q];
       }
       return;
     }
@@ -935,8 +935,9 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   }
   // Grouped modes: wave w's 16-byte job moves four steps of scales of 64 rows (w < 4:
   // activation rows 64w + lane; MX32 w = 4, 5: weight rows 64(w-4) + lane; BLOCK128
-  // w = 4: the weight-block scale, every lane the same 16 bytes). Others only load the
-  // dummy. Ring slot layout: [0, 4 KB) activation rows x 16 bytes, from 4 KB the rest.
+  // w = 4 (and 5 in 256-column tiles): the scale of weight block w-4 of the tile, every
+  // lane the same 16 bytes, at 4 KB + 1 KB (w-4)). Others only load the dummy. Ring slot
+  // layout: [0, 4 KB) activation rows x 16 bytes, from 4 KB the rest.
   r.g_role = false;
   r.g_base = r.a_base;
   r.g_off = 0;
@@ -951,11 +952,11 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
       r.g_base = SA + m0 * p.sa_sm * 4;
       r.g_off = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
       r.g_lds = wave * 1024;
-    } else if (wave == 4) {
+    } else if (wave - 4 < kNb) {  // weight block wave-4 of the tile (clamped past the last column)
       const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
       r.g_role = true;
-      r.g_base = SB + (n0 / 128) * p.sb_sn * 4;
-      r.g_lds = 4096;
+      r.g_base = SB + min(n0 / 128 + (wave - 4), nmax / 128) * p.sb_sn * 4;
+      r.g_lds = 4096 + (wave - 4) * 1024;
     }
   } else if constexpr (SCM == kScMxGrp) {
     if (wave < 4) {
@@ -1459,13 +1460,14 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
     else launch_dma<kScF32Row, T>(p, grid_for(tt), stream);
     return finish("block-scaled grouped GEMM launch");
   }
-  if (!p.masked_m && (dm == kScE8Col || dm == kScF32Row)) {
+  if (!p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp)) {
     // 256x256 tiles halve the operand bytes each tile loads per output; used when they
     // still give every CU a tile
     using W = DmaCfgW;
     const int64_t wt = ((p.M + W::BM - 1) / W::BM) * ((p.N + W::BN - 1) / W::BN);
     if (wt >= kCUs) {
       if (dm == kScE8Col) launch_dma<kScE8Col, W>(p, grid_for(wt), stream);
+      else if (dm == kScF32Grp) launch_dma<kScF32Grp, W>(p, grid_for(wt), stream);
       else launch_dma<kScF32Row, W>(p, grid_for(wt), stream);
       return finish("block-scaled GEMM launch");
     }

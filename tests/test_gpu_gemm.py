@@ -89,12 +89,13 @@ def test_ragged_shapes_full(M, N, K, sa_kind, sb_kind):
 
 
 # Flat problems with at least 256 tiles of 256x256 take the two-stage kernel with
-# 256-column tiles (fp32 weight scales; fp32 row or UE8M0 column activation scales, K not
-# a multiple of 512 for fp32 ones). M=4000, N=4200 leaves ragged tiles in both directions;
-# K = 128, 256, 384 run 1, 2 and 3 steps (pipelines shorter than two stages, and both
-# stages ending the loop). Outputs on a grid of rows x columns through tile and wave-tile
-# boundaries plus random ones are compared; every output must be written.
-@pytest.mark.parametrize("K", [128, 256, 384])
+# 256-column tiles (fp32 weight scales; fp32 row or UE8M0 column activation scales; fp32
+# ones in four-step groups when K is a multiple of 512). M=4000, N=4200 leaves ragged
+# tiles in both directions; K = 128, 256, 384 run 1, 2 and 3 steps (pipelines shorter
+# than two stages, and both stages ending the loop), K = 512 and 1024 one and two scale
+# groups. Outputs on a grid of rows x columns through tile and wave-tile boundaries plus
+# random ones are compared; every output must be written.
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 1024])
 @pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col"])
 def test_wide_tiles_ragged_sampled(K, sa_kind):
     M, N = 4000, 4200
