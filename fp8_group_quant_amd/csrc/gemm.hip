@@ -1486,6 +1486,13 @@ int launch_gemm_mx32(const GemmParams& p, hipStream_t stream) {
   using C = Large;
   const int64_t tiles = ((p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN);
   const int dm = dma_mode(p, true);
+  using W = DmaCfgW;
+  const int64_t wt = ((p.M + W::BM - 1) / W::BM) * ((p.N + W::BN - 1) / W::BN);
+  if (dm >= 0 && wt >= kCUs) {
+    // 256x256 tiles with per-step scale loads (8 jobs: 256 activation and 256 weight rows)
+    launch_dma<kScMx, W>(p, grid_for(wt), stream);
+    return finish("MXFP8 GEMM launch");
+  }
   if (dm == kScMxGrp) launch_dma<kScMxGrp>(p, grid_for(tiles), stream);
   else if (dm == kScMx) launch_dma<kScMx>(p, grid_for(tiles), stream);
   else launch<C, true, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid_for(tiles), stream);

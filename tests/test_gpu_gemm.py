@@ -293,6 +293,26 @@ def test_mx_full(M, N, K, sk_stride):
     check(y, ys, ss, K, f"mx {M}x{N}x{K}")
 
 
+# At least 256 tiles of 256x256 take the two-stage kernel (per-step scale loads); ragged in
+# both directions, 2 and 8 K steps, scales with unit or row stride along K.
+@pytest.mark.parametrize("K", [256, 1024])
+@pytest.mark.parametrize("sk_stride", [False, True])
+def test_mx_wide_ragged_sampled(K, sk_stride):
+    M, N = 4000, 4200
+    a = synth.weight_codes(71, M, K, tensor_id=1)
+    b = synth.weight_codes(71, N, K, tensor_id=2)
+    ea = synth.e8m0_exponents(71, M, K // 32, tensor_id=3)
+    eb = synth.e8m0_exponents(71, N, K // 32, tensor_id=4)
+    y = _gpu_mx(a, ea, b, eb, sk_stride)
+    assert not np.any(y == SENT)
+    g = np.random.default_rng(K + 1)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 3839, 3840, 3999], g.integers(0, M, 40)]))
+    cols = np.unique(np.concatenate([[0, 63, 64, 191, 192, 255, 256, 4095, 4096, 4199], g.integers(0, N, 40)]))
+    ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
+    ys, ss = oracle.gemm_mx32(a, ea, b, eb, at=(ms, ns))
+    check(y[ms, ns], ys, ss, K, f"mx wide {M}x{N}x{K}")
+
+
 def test_mx_workload_sampled():
     w = synth.MX
     a, b, ea, eb = synth.mx_operands(w)
