@@ -119,11 +119,15 @@ def run(args) -> dict:
         step(i)
     torch.cuda.synchronize()
 
-    def timed(fn, n):
-        """average ms of n back-to-back launches between two events on the kernels' stream"""
+    def timed(fn, n, warm=0):
+        """average ms of n back-to-back launches between two events on the kernels' stream,
+        after `warm` untimed launches queued right before them (the GPU is busy, not idle
+        after a synchronize, when the first timed launch starts)"""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        for i in range(warm):
+            fn(n + i)
         e0.record(stream)
         for i in range(n):
             fn(i)
@@ -144,9 +148,10 @@ def run(args) -> dict:
 
     # the timed steps: exactly args.steps passes of the whole path
     ms_step = timed(lambda i: step(args.warmup + i), args.steps)
-    # per-kernel averages (each kernel alone, same buffer rotation)
-    quant_ms = timed(quant_only, args.steps)
-    gemm_ms = timed(gemm_only, args.steps)
+    # per-kernel averages (each kernel alone, same buffer rotation, warmed like the steps)
+    kwarm = max(args.warmup, 10)
+    quant_ms = timed(quant_only, args.steps, kwarm)
+    gemm_ms = timed(gemm_only, args.steps, kwarm)
 
     flops = 2.0 * M * N * K
     qbytes = quant_bytes(M, K, G, 2, 1 if ue8m0 else 4, w.silu)
@@ -211,11 +216,14 @@ def cpu_baseline(w, x_host, w_host, sw_host, rows: int) -> dict:
                       f"({t2 - t0:.1f} s); step time extrapolated per row / per output = {t_step:.0f} s"}
 
 
-def _timed(fn, n):
+def _timed(fn, n, warm=0):
+    """average ms of n back-to-back launches, after `warm` untimed ones queued right before"""
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    for i in range(warm):
+        fn(n + i)
     e0.record()
     for i in range(n):
         fn(i)
@@ -252,9 +260,7 @@ def suite(steps: int, warmup: int) -> list:
         print(json.dumps(rec), flush=True)
 
     def run(fn, n_sets):
-        for i in range(warmup):
-            fn(i)
-        return _timed(fn, steps)
+        return _timed(fn, steps, max(warmup, 10))
 
     # flat workloads: quant then block-scaled GEMM
     for w in (synth.TINY, synth.dense(1), synth.dense(16), synth.dense(128), synth.dense(4096), synth.SILU):

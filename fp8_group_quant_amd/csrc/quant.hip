@@ -289,7 +289,9 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
           for (int q = 0; q < 4; q++)
             w[q] = cvt4(clamp448(v[4 * q] * inv), clamp448(v[4 * q + 1] * inv), clamp448(v[4 * q + 2] * inv),
                         clamp448(v[4 * q + 3] * inv));
-          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(qrow + k));
+          // default cache policy: the codes stay in the Infinity Cache for the GEMM that
+          // reads them next (quant + GEMM measured ~3% faster than with non-temporal stores)
+          *reinterpret_cast<u32x4*>(qrow + k) = w;
           if ((lane & (LANES - 1)) == 0) {
             const int64_t sidx = srow + (k / G) * p.s_sg;
             if constexpr (FMT == FP8Q_SCALE_UE8M0)
