@@ -24,11 +24,11 @@ LIB_PATH = os.path.join(HERE, "libfp8q.so")
 # constants of include/fp8q.h
 OK, EINVAL, EUNSUPPORTED, EALIGN, EDEVICE, ELAUNCH = 0, 1, 2, 3, 4, 5
 DTYPE_BF16, DTYPE_F16, DTYPE_F32 = 0, 1, 2
-SCALE_F32, SCALE_UE8M0 = 0, 1
+SCALE_F32, SCALE_UE8M0, SCALE_UE8M0_PACKED = 0, 1, 2
 GEMM_BLOCK128, GEMM_MX32 = 0, 1
 
 _DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16, torch.float32: DTYPE_F32}
-_SCALE_FMT = {"f32": SCALE_F32, "ue8m0": SCALE_UE8M0}
+_SCALE_FMT = {"f32": SCALE_F32, "ue8m0": SCALE_UE8M0, "ue8m0_packed": SCALE_UE8M0_PACKED}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -124,7 +124,10 @@ def _scale_fmt_of(s: torch.Tensor) -> int:
         return SCALE_F32
     if s.dtype == torch.uint8:
         return SCALE_UE8M0
-    raise ValueError("scales must be float32 (fp32 scales) or uint8 (UE8M0 bytes)")
+    if s.dtype == torch.int32:
+        return SCALE_UE8M0_PACKED
+    raise ValueError("scales must be float32 (fp32 scales), uint8 (UE8M0 bytes) or int32 "
+                     "(UE8M0 bytes packed 4 groups per word)")
 
 
 # ------------------------------------------------------------------------------ quant
@@ -165,8 +168,13 @@ def fp8q_silu_mul_group_quant(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
 
 def alloc_scales(E: int | None, M: int, ng: int, scale_fmt: str, layout: str, device) -> torch.Tensor:
     """Scale tensor viewed as [.., M, ng]: row-major storage, or column-major storage
-    [.., ng, M] returned transposed (the strides carry the layout)."""
-    dt = torch.float32 if scale_fmt == "f32" else torch.uint8
+    [.., ng, M] returned transposed (the strides carry the layout). "ue8m0_packed" returns
+    int32 words of 4 groups each, viewed as [.., M, ng / 4]."""
+    dt = {"f32": torch.float32, "ue8m0": torch.uint8, "ue8m0_packed": torch.int32}[scale_fmt]
+    if scale_fmt == "ue8m0_packed":
+        if ng % 4:
+            raise ValueError("packed UE8M0 scales need a multiple of 4 groups per row")
+        ng //= 4
     lead = () if E is None else (E,)
     if layout == "row":
         return torch.empty(*lead, M, ng, dtype=dt, device=device)

@@ -18,12 +18,16 @@ int check_operands(const std::string& pre, const uint8_t* a, int64_t lda, const 
                    int64_t rows, int64_t N, int64_t K, int mode) {
   if (mode != FP8Q_GEMM_BLOCK128 && mode != FP8Q_GEMM_MX32)
     return fail(FP8Q_EUNSUPPORTED, pre + "mode must be BLOCK128 or MX32");
-  if (!valid_fmt(sa_fmt) || !valid_fmt(sb_fmt))
-    return fail(FP8Q_EUNSUPPORTED, pre + "scale formats must be F32 or UE8M0");
+  const bool packed = sa_fmt == FP8Q_SCALE_UE8M0_PACKED;
+  if (!(valid_fmt(sa_fmt) || (packed && mode == FP8Q_GEMM_BLOCK128)) || !valid_fmt(sb_fmt))
+    return fail(FP8Q_EUNSUPPORTED, pre + "scale formats must be F32 or UE8M0 (activation scales also "
+                                         "UE8M0_PACKED in BLOCK128 mode)");
   if (mode == FP8Q_GEMM_MX32 && (sa_fmt != FP8Q_SCALE_UE8M0 || sb_fmt != FP8Q_SCALE_UE8M0))
     return fail(FP8Q_EUNSUPPORTED, pre + "MX32 scales must be E8M0 bytes (FP8Q_SCALE_UE8M0)");
   if (rows < 0 || N < 0 || K < 0) return fail(FP8Q_EINVAL, pre + "negative size");
   if (K % 128 != 0) return fail(FP8Q_EINVAL, pre + "K must be a multiple of 128");
+  if (packed && K % 512 != 0)
+    return fail(FP8Q_EINVAL, pre + "packed UE8M0 activation scales need K a multiple of 512");
   if (lda < 0 || ldb < 0 || ldy < 0 || sa_sm < 0 || sa_sk < 0 || sb_sn < 0 || sb_sk < 0)
     return fail(FP8Q_EINVAL, pre + "negative stride");
   if (rows == 0 || N == 0 || K == 0) return FP8Q_OK;
@@ -33,8 +37,8 @@ int check_operands(const std::string& pre, const uint8_t* a, int64_t lda, const 
   if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0)
     return fail(FP8Q_EALIGN, pre + "a, b and their row strides must be 16-byte aligned");
   if (!aligned(y, 4) || ldy % 2 != 0) return fail(FP8Q_EALIGN, pre + "y must be 4-byte aligned with an even ldy");
-  if ((sa_fmt == FP8Q_SCALE_F32 && !aligned(sa, 4)) || (sb_fmt == FP8Q_SCALE_F32 && !aligned(sb, 4)))
-    return fail(FP8Q_EALIGN, pre + "fp32 scales must be 4-byte aligned");
+  if ((sa_fmt != FP8Q_SCALE_UE8M0 && !aligned(sa, 4)) || (sb_fmt == FP8Q_SCALE_F32 && !aligned(sb, 4)))
+    return fail(FP8Q_EALIGN, pre + "fp32 scales and packed UE8M0 words must be 4-byte aligned");
   return FP8Q_OK;
 }
 
@@ -73,7 +77,8 @@ int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda, const void* sa, int sa_
   p.sa_sk = sa_sk;
   p.sb_sn = sb_sn;
   p.sb_sk = sb_sk;
-  p.sa_fmt = sa_fmt;
+  p.sa_packed = sa_fmt == FP8Q_SCALE_UE8M0_PACKED ? 1 : 0;
+  p.sa_fmt = p.sa_packed ? FP8Q_SCALE_UE8M0 : sa_fmt;
   p.sb_fmt = sb_fmt;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return mode == FP8Q_GEMM_MX32 ? launch_gemm_mx32(p, s) : launch_gemm_block128(p, 0, s);
@@ -128,7 +133,8 @@ int fp8q_grouped_gemm_masked(const uint8_t* a, int64_t a_se, int64_t lda, const 
   p.sb_sn = sb_sn;
   p.sb_sk = sb_sk;
   p.sb_se = sb_se;
-  p.sa_fmt = sa_fmt;
+  p.sa_packed = sa_fmt == FP8Q_SCALE_UE8M0_PACKED ? 1 : 0;
+  p.sa_fmt = p.sa_packed ? FP8Q_SCALE_UE8M0 : sa_fmt;
   p.sb_fmt = sb_fmt;
   return launch_gemm_block128(p, expected_m, static_cast<hipStream_t>(stream));
 }

@@ -18,8 +18,8 @@ int quant_entry(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K, in
   const std::string pre = std::string(fn) + ": ";
   if (in_dtype != FP8Q_DTYPE_BF16 && in_dtype != FP8Q_DTYPE_F16 && in_dtype != FP8Q_DTYPE_F32)
     return fail(FP8Q_EUNSUPPORTED, pre + "in_dtype must be BF16, F16 or F32");
-  if (scale_fmt != FP8Q_SCALE_F32 && scale_fmt != FP8Q_SCALE_UE8M0)
-    return fail(FP8Q_EUNSUPPORTED, pre + "scale_fmt must be F32 or UE8M0");
+  if (scale_fmt != FP8Q_SCALE_F32 && scale_fmt != FP8Q_SCALE_UE8M0 && scale_fmt != FP8Q_SCALE_UE8M0_PACKED)
+    return fail(FP8Q_EUNSUPPORTED, pre + "scale_fmt must be F32, UE8M0 or UE8M0_PACKED");
   if (group_size != 32 && group_size != 64 && group_size != 128)
     return fail(FP8Q_EUNSUPPORTED, pre + "group_size must be 32, 64 or 128");
   if (E < 0 || M < 0 || K < 0) return fail(FP8Q_EINVAL, pre + "negative size");
@@ -27,6 +27,9 @@ int quant_entry(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K, in
     return fail(FP8Q_EINVAL, pre + "negative stride");
   if (expected_m < 0) return fail(FP8Q_EINVAL, pre + "expected_m must be >= 0");
   if (K % group_size != 0) return fail(FP8Q_EINVAL, pre + "K must be a multiple of group_size");
+  const bool packed = scale_fmt == FP8Q_SCALE_UE8M0_PACKED;
+  if (packed && (K / group_size) % 4 != 0)
+    return fail(FP8Q_EINVAL, pre + "packed UE8M0 scales need a multiple of 4 groups per row");
   if (masked_m && E > kMaxMaskedExperts)
     return fail(FP8Q_EUNSUPPORTED, pre + "masked dispatch supports at most 4096 experts");
   if (masked_m && E * M >= (int64_t(1) << 31))
@@ -35,7 +38,7 @@ int quant_entry(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K, in
   if (!x || !q || !s) return fail(FP8Q_EINVAL, pre + "null tensor pointer");
 
   const int64_t width = silu ? 2 * K : K;  // input row length
-  const int64_t ng = K / group_size;
+  const int64_t ng = packed ? K / group_size / 4 : K / group_size;  // scale elements per row
   const int64_t esz = in_dtype == FP8Q_DTYPE_F32 ? 4 : 2;
   // outputs must not overlap themselves (inputs may)
   if (M > 1 && q_sm < K) return fail(FP8Q_EINVAL, pre + "q rows overlap (q_sm < K)");
@@ -51,8 +54,8 @@ int quant_entry(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K, in
     return fail(FP8Q_EALIGN, pre + "x and its row/expert strides must be 16-byte aligned");
   if (!aligned16(q) || q_sm % 16 != 0 || q_se % 16 != 0)
     return fail(FP8Q_EALIGN, pre + "q and its row/expert strides must be 16-byte aligned");
-  if (scale_fmt == FP8Q_SCALE_F32 && (reinterpret_cast<uintptr_t>(s) & 3u) != 0)
-    return fail(FP8Q_EALIGN, pre + "fp32 scales must be 4-byte aligned");
+  if (scale_fmt != FP8Q_SCALE_UE8M0 && (reinterpret_cast<uintptr_t>(s) & 3u) != 0)
+    return fail(FP8Q_EALIGN, pre + "fp32 scales and packed UE8M0 words must be 4-byte aligned");
 
   const int dev = check_current_device();
   if (dev != FP8Q_OK) return dev;
@@ -72,7 +75,8 @@ int quant_entry(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K, in
   p.s_se = s_se;
   p.s_sm = s_sm;
   p.s_sg = s_sg;
-  return launch_group_quant(in_dtype, scale_fmt, group_size, silu, p, expected_m,
+  p.packed = packed ? 1 : 0;
+  return launch_group_quant(in_dtype, packed ? FP8Q_SCALE_UE8M0 : scale_fmt, group_size, silu, p, expected_m,
                             static_cast<hipStream_t>(stream));
 }
 

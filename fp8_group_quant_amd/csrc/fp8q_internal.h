@@ -27,7 +27,8 @@ struct QuantParams {
   int64_t E, M, K;          // K = quantized width
   int64_t x_se, x_sm;       // input strides (elements)
   int64_t q_se, q_sm;       // output strides (bytes)
-  int64_t s_se, s_sm, s_sg; // scale strides (scale elements)
+  int64_t s_se, s_sm, s_sg; // scale strides (scale elements; packed UE8M0: 32-bit words of 4 groups)
+  int32_t packed;           // UE8M0 exponents packed 4 per word (group g in byte g % 4 of word g / 4)
   int64_t nseg;             // segments per row
   int32_t chunks_per_seg;   // 512-element chunks per segment (1..8)
   int32_t chunks_per_row;   // ceil(K / 512)
@@ -51,6 +52,7 @@ struct GemmParams {
   int64_t sa_sm, sa_sk, sa_se;
   int64_t sb_sn, sb_sk, sb_se;
   int sa_fmt, sb_fmt;
+  int sa_packed;  // UE8M0 activation scales packed 4 K blocks per 32-bit word (sa strides in words)
 };
 
 int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t stream);

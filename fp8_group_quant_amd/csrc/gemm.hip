@@ -181,6 +181,12 @@ __device__ __forceinline__ float scale_value(uint32_t raw) {
   }
 }
 
+// Element index of activation scale (m, kb) from sa: packed UE8M0 words hold K blocks
+// 4j..4j+3 of a row in bytes 0..3 (strides in words), other layouts one element per (m, kb).
+__device__ __forceinline__ int64_t sa_index(const GemmParams& p, int64_t m, int kb) {
+  return p.sa_packed ? 4 * (m * p.sa_sm + (kb >> 2) * p.sa_sk) + (kb & 3) : m * p.sa_sm + kb * p.sa_sk;
+}
+
 // Scale staging for one K step: thread t < BM fetches the scale(s) of tile row t of A;
 // thread BM + u fetches those of B (MX32: row u of the tile; BLOCK128: N block u). The
 // raw word is held in one register from the top of a step to its end (no use before
@@ -218,7 +224,7 @@ struct ScaleStage {
       }
     } else {
       if (tid < C::BM) {
-        const int64_t idx = min(m0 + tid, rmax) * p.sa_sm + kb * p.sa_sk;
+        const int64_t idx = sa_index(p, min(m0 + tid, rmax), kb);
         v = SA_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(SA)[idx] : static_cast<const uint8_t*>(SA)[idx];
       } else if (tid < C::BM + C::BN / 128) {
         const int64_t nb = min(n0 / 128 + (tid - C::BM), (p.N - 1) / 128);
@@ -531,9 +537,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 //
 // Scales reach LDS the same way, which limits this path to scale layouts that can be
 // moved in aligned 4-byte pieces: fp32 activation scales (any strides), UE8M0 activation
-// scales stored column-major ([K/128][M], M a multiple of 4), fp32 weight-block scales,
-// and MX32 E8M0 bytes stored [rows][K/32] with rows a multiple of 4 bytes apart. Other
-// layouts use the register-staged kernel above.
+// scales stored column-major ([K/128][M], M a multiple of 4) or packed four K blocks per
+// word (any word strides: each step loads a row's word and reads byte kb % 4), fp32
+// weight-block scales, and MX32 E8M0 bytes stored [rows][K/32] with rows a multiple of 4
+// bytes apart. Other layouts use the register-staged kernel above.
 //
 // Scales stored per row along K (fp32 [M][K/128], E8M0 [rows][K/32]) put each row's word
 // of one step in a different cache line. When K is a multiple of 512 and rows are 16-byte
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 // first read four steps later. The scale load of the other steps (and of the wavefronts
 // without a scale to move) rereads group 0 into a 1 KB area nobody reads, so every step
 // still issues the same loads.
-enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp = 4 };
+enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp = 4, kScE8Pk = 5 };
 
 // LDS layout of the direct-to-LDS kernel for tile shape C: kStages stages, each holding
 // both operand tiles of one K step and (per-step scale modes) the step's scales, followed
@@ -608,7 +615,7 @@ struct DmaRun {
   // scale of the activation rows, weights at 2^0), and the fold multiplies by the
   // weight-block scale alone, the same for every lane. P * 2^e * sb rounds exactly like
   // P * (2^e * sb), so the result is the same as folding the product of both scales.
-  static constexpr bool E8 = SCM == kScE8Col;
+  static constexpr bool E8 = SCM == kScE8Col || SCM == kScE8Pk;
   static constexpr int SM = C::SM, SN = C::SN;
   static_assert((C::BM == 256 || C::BM == 128) && SN == 4 && C::WTN == 64, "64-wide wave tiles");
   static constexpr int kW = C::kWaves;
@@ -630,6 +637,7 @@ struct DmaRun {
   const uint8_t* s_base[kSc];
   uint32_t s_off[kSc];
   int64_t s_step[kSc];
+  int s_shift[kSc];  // the job's source advances by s_step every 2^s_shift steps
   uint32_t s_lds[kSc];
   // grouped modes: this wave's 16-byte scale load (role: ea/sa rows, eb rows or sb, or
   // none), its source for group 0, the bytes per group, its ring offset; ngroups = nkb/4
@@ -673,7 +681,8 @@ struct DmaRun {
       dma16(dst, g_base + (real ? g * g_step : 0), g_off);
     } else {
 #pragma unroll
-      for (int q = 0; q < kSc; q++) dma4(base + L::kScOff + s_lds[q], s_base[q] + kb * s_step[q], s_off[q]);
+      for (int q = 0; q < kSc; q++)
+        dma4(base + L::kScOff + s_lds[q], s_base[q] + (kb >> s_shift[q]) * s_step[q], s_off[q]);
     }
   }
 
@@ -708,6 +717,8 @@ struct DmaRun {
         const int row = wm * C::WTM + i * 16 + (lane & 15);
         if constexpr (F32)
           sa[i] = reinterpret_cast<const float*>(sc)[row];
+        else if constexpr (SCM == kScE8Pk)
+          ea[i] = sc[4 * row + (kb & 3)];  // the row's word of K blocks 4(kb/4) .. +3
         else if constexpr (E8)
           ea[i] = sc[row];
         else
@@ -884,8 +895,19 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
     r.s_base[q] = r.a_base;
     r.s_off[q] = 0;
     r.s_step[q] = 0;
+    r.s_shift[q] = 0;
     r.s_lds[q] = R::L::kSpare;
-    if constexpr (SCM == kScF32Row) {
+    if constexpr (SCM == kScE8Pk) {
+      if (js < 4) {  // packed word (K blocks 4(kb/4)..+3) of tile row 64 js + lane
+        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
+        const int row = js * 64 + lane;
+        r.s_base[q] = SA + m0 * p.sa_sm * 4;
+        r.s_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
+        r.s_step[q] = p.sa_sk * 4;
+        r.s_shift[q] = 2;
+        r.s_lds[q] = js * 256;
+      }
+    } else if constexpr (SCM == kScF32Row) {
       if (js < 4) {  // fp32 scale of tile row 64 js + lane
         const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
         const int row = js * 64 + lane;
@@ -919,11 +941,11 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_lds[q] = 1024 + (js - 4) * 256;
       }
     }
-    if constexpr (SCM == kScF32Row || SCM == kScE8Col) {
+    if constexpr (SCM == kScF32Row || SCM == kScE8Col || SCM == kScE8Pk) {
       // the scale of weight block nb of the tile, one fp32 word per step (every lane loads
       // it; the word lands 64 times in [1024 + 256 nb, +256) of the scale area). A block
       // past the last column reloads the last block's word.
-      const int nb = js - (SCM == kScF32Row ? 4 : 1);
+      const int nb = js - (SCM == kScE8Col ? 1 : 4);
       if (nb >= 0 && nb < kNb) {
         const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
         r.s_base[q] = SB + min(n0 / 128 + nb, nmax / 128) * p.sb_sn * 4;
@@ -1111,7 +1133,7 @@ __global__ __launch_bounds__(kSkinnyThreads) void gemm_skinny_kernel(GemmParams 
 #pragma unroll
       for (int i = 0; i < SM; i++) {
         xf[u][i] = frag_global(xrow[i], kb, lane);
-        const int64_t si = mrow[i] * p.sa_sm + kb * p.sa_sk;
+        const int64_t si = sa_index(p, mrow[i], kb);
         sa_raw[u][i] = SA_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(p.sa)[si]
                                                 : static_cast<const uint8_t*>(p.sa)[si];
       }
@@ -1257,7 +1279,7 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void gemm_skinny_dma_kernel(Gemm
         if (idx < total) {
           const int kb = idx / MR;
           const int64_t m = min(static_cast<int64_t>(idx % MR), p.M - 1);
-          const int64_t si = m * p.sa_sm + kb * p.sa_sk;
+          const int64_t si = sa_index(p, m, kb);
           v[u] = SA_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(p.sa)[si] : static_cast<const uint8_t*>(p.sa)[si];
         }
       }
@@ -1410,6 +1432,8 @@ int dma_mode(const GemmParams& p, bool mx) {
   }
   const int64_t E = p.masked_m ? p.E : 1;
   if (p.sb_fmt != FP8Q_SCALE_F32) return -1;
+  if (p.sa_packed)
+    return p.sa_sm < (int64_t(1) << 22) && E <= DmaLayout<kScE8Pk, DmaCfg>::kMaxPrefix ? kScE8Pk : -1;
   if (p.sa_fmt == FP8Q_SCALE_F32) {
     if (p.sa_sm >= (int64_t(1) << 22)) return -1;
     const bool grp = k512 && p.sa_sk == 1 && p.sa_sm % 4 == 0 && a16(p.sa) && p.sb_sk == 1 && p.sb_sn % 4 == 0 &&
@@ -1451,22 +1475,24 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
     return finish("block-scaled GEMM launch");
   }
   const int dm = dma_mode(p, false);
-  if (p.masked_m && (dm == kScE8Col || dm == kScF32Row)) {
+  if (p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScE8Pk)) {
     // masked: 128-row tiles pad an expert's rows to a multiple of 128 instead of 256
     using T = DmaCfgT;
     const int64_t rows = expected_m > 0 ? std::min<int64_t>(expected_m, p.M) : p.M;
     const int64_t tt = p.E * ((rows + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
     if (dm == kScE8Col) launch_dma<kScE8Col, T>(p, grid_for(tt), stream);
+    else if (dm == kScE8Pk) launch_dma<kScE8Pk, T>(p, grid_for(tt), stream);
     else launch_dma<kScF32Row, T>(p, grid_for(tt), stream);
     return finish("block-scaled grouped GEMM launch");
   }
-  if (!p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp)) {
+  if (!p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp || dm == kScE8Pk)) {
     // 256x256 tiles halve the operand bytes each tile loads per output; used when they
     // still give every CU a tile
     using W = DmaCfgW;
     const int64_t wt = ((p.M + W::BM - 1) / W::BM) * ((p.N + W::BN - 1) / W::BN);
     if (wt >= kCUs) {
       if (dm == kScE8Col) launch_dma<kScE8Col, W>(p, grid_for(wt), stream);
+      else if (dm == kScE8Pk) launch_dma<kScE8Pk, W>(p, grid_for(wt), stream);
       else if (dm == kScF32Grp) launch_dma<kScF32Grp, W>(p, grid_for(wt), stream);
       else launch_dma<kScF32Row, W>(p, grid_for(wt), stream);
       return finish("block-scaled GEMM launch");
@@ -1475,6 +1501,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   if (dm == kScF32Row) launch_dma<kScF32Row>(p, grid, stream);
   else if (dm == kScF32Grp) launch_dma<kScF32Grp>(p, grid, stream);
   else if (dm == kScE8Col) launch_dma<kScE8Col>(p, grid, stream);
+  else if (dm == kScE8Pk) launch_dma<kScE8Pk>(p, grid, stream);
   else if (a8 && b8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid, stream);
   else if (a8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, grid, stream);
   else if (b8) launch<C, false, FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, grid, stream);

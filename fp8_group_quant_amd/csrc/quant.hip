@@ -293,7 +293,9 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
           // reads them next (quant + GEMM measured ~3% faster than with non-temporal stores)
           *reinterpret_cast<u32x4*>(qrow + k) = w;
           if ((lane & (LANES - 1)) == 0) {
-            const int64_t sidx = srow + (k / G) * p.s_sg;
+            const int64_t g = k / G;
+            // packed: group g is byte g % 4 of word g / 4 (little-endian), strides in words
+            const int64_t sidx = p.packed ? 4 * (srow + (g >> 2) * p.s_sg) + (g & 3) : srow + g * p.s_sg;
             if constexpr (FMT == FP8Q_SCALE_UE8M0)
               static_cast<uint8_t*>(p.s)[sidx] = static_cast<uint8_t>(sbits);
             else

@@ -60,6 +60,9 @@ extern "C" {
 /* scale formats */
 #define FP8Q_SCALE_F32 0   /* one IEEE float per group: s = amax / 448 */
 #define FP8Q_SCALE_UE8M0 1 /* one byte per group: s = 2^(byte-127), the smallest power of two >= amax/448 */
+#define FP8Q_SCALE_UE8M0_PACKED 2 /* the same bytes, 4 groups per 32-bit word: group g is byte g % 4 (least
+                                     significant first) of word g / 4; strides count words [PR30924 item 1,
+                                     the `aligned` trait: number of groups a multiple of 4, UE8M0 only] */
 
 /* GEMM scaling modes */
 #define FP8Q_GEMM_BLOCK128 0 /* a: 1x128 scales per (row, K block); b: 128x128 scales per (N block, K block) */
@@ -82,6 +85,9 @@ extern "C" {
  * scale elements (4-byte floats or single bytes). The layout is read from the strides:
  * s_sg == 1 means row-major [M][K/G], s_sm == 1 means column-major [K/G][M]; any other
  * combination is FP8Q_EINVAL.
+ * FP8Q_SCALE_UE8M0_PACKED stores the same UE8M0 bytes 4 groups to a 32-bit word: byte
+ * g % 4 of word (e, m, g / 4), which is at s + 4 * (e*s_se + m*s_sm + (g/4)*s_sg) bytes
+ * (strides in words; row-major [M][K/G/4] or column-major [K/G/4][M] words as above).
  *
  * Dispatch:
  *   masked_m == NULL: flat — every row m < M of every e < E is processed.
@@ -95,7 +101,8 @@ extern "C" {
  *   in_dtype in {BF16, F16, F32} and group_size in {32, 64, 128}       [EUNSUPPORTED]
  *   K % group_size == 0, E, M, K >= 0, strides non-negative             [EINVAL]
  *   x and q 16-byte aligned; x_sm, x_se (in bytes) and q_sm, q_se
- *   multiples of 16 bytes; F32 scales 4-byte aligned                    [EALIGN]
+ *   multiples of 16 bytes; F32 scales and packed words 4-byte aligned   [EALIGN]
+ *   UE8M0_PACKED: (K / group_size) % 4 == 0                              [EINVAL]
  *   E <= 4096 when masked                                                [EUNSUPPORTED]
  */
 int fp8q_group_quant(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K,
@@ -135,7 +142,9 @@ int fp8q_silu_mul_group_quant(const void* x, int in_dtype, int64_t E, int64_t M,
  * operands are K-major ("NT"). Y is [M][N] bf16 (element (m, n) at y + m*ldy + n, passed
  * as uint16_t bits).
  *   mode FP8Q_GEMM_BLOCK128:
- *     sa: one scale per (m, kb), kb = k/128, at sa + m*sa_sm + kb*sa_sk; sa_fmt F32 or UE8M0.
+ *     sa: one scale per (m, kb), kb = k/128, at sa + m*sa_sm + kb*sa_sk; sa_fmt F32 or UE8M0;
+ *         or UE8M0_PACKED: byte kb % 4 of the 32-bit word at sa + 4*(m*sa_sm + (kb/4)*sa_sk)
+ *         bytes (strides in words; K % 512 == 0 [EINVAL]; sa 4-byte aligned [EALIGN]).
  *     sb: one scale per (nb, kb), nb = n/128, at sb + nb*sb_sn + kb*sb_sk; sb_fmt F32 or UE8M0.
  *     Y[m][n] = bf16_rne( sum_kb sa(m,kb) * sb(n/128,kb) * sum_{k in kb} dec(A[m][k]) * dec(B[n][k]) )
  *   mode FP8Q_GEMM_MX32:

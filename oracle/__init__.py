@@ -16,6 +16,8 @@ Parity status of each function (what pins it is in tests/test_oracle_*.py):
   group_quant               pinned: golden group, dequant-error bound, layout/mask invariants
   gemm                      pinned: exact Fraction arithmetic, torch float64 dequant-matmul,
                             one-hot operands
+  pack_ue8m0, unpack_ue8m0  layout only (no arithmetic); pinned: hand-written words of known
+                            bytes, round trip
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "libfp8q_oracle.so")
 
 BF16, F16, F32 = 0, 1, 2
-SCALE_F32, SCALE_UE8M0 = 0, 1
+SCALE_F32, SCALE_UE8M0, SCALE_UE8M0_PACKED = 0, 1, 2
 GEMM_BLOCK128, GEMM_MX32 = 0, 1
 
 _lib = None
@@ -153,6 +155,27 @@ def group_quant(x: np.ndarray, group_size: int, scale_fmt: int, layout: str = "r
     if x.ndim == 2:
         return q[0], s[0]
     return q, s
+
+
+def pack_ue8m0(s: np.ndarray) -> np.ndarray:
+    """UE8M0 bytes [.., rows, ng] (ng a multiple of 4) -> int32 words [.., rows, ng / 4].
+    Group g of a row becomes byte g % 4 of word g / 4, counting bytes from the least
+    significant: the four-groups-per-word layout that the `aligned` trait enables
+    ([PR30924] 实现拆解 1; UE8M0 only, number of groups a multiple of 4)."""
+    b = np.asarray(s, dtype=np.uint8).astype(np.uint32)
+    if b.shape[-1] % 4:
+        raise ValueError("packed UE8M0 needs a multiple of 4 groups per row")
+    w = b[..., 0::4] | (b[..., 1::4] << 8) | (b[..., 2::4] << 16) | (b[..., 3::4] << 24)
+    return w.astype(np.uint32).view(np.int32)
+
+
+def unpack_ue8m0(w: np.ndarray) -> np.ndarray:
+    """Inverse of pack_ue8m0: int32 words [.., rows, n] -> UE8M0 bytes [.., rows, 4 n]."""
+    u = np.asarray(w).astype(np.int64) & 0xFFFFFFFF
+    out = np.empty(u.shape[:-1] + (4 * u.shape[-1],), dtype=np.uint8)
+    for i in range(4):
+        out[..., i::4] = (u >> (8 * i)) & 0xFF
+    return out
 
 
 # --------------------------------------------------------------------------- gemm

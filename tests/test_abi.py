@@ -60,6 +60,7 @@ def test_header_constants_match_binding():
     assert consts["FP8Q_EDEVICE"] == fq.EDEVICE and consts["FP8Q_ELAUNCH"] == fq.ELAUNCH
     assert consts["FP8Q_DTYPE_BF16"] == fq.DTYPE_BF16 and consts["FP8Q_DTYPE_F32"] == fq.DTYPE_F32
     assert consts["FP8Q_SCALE_F32"] == fq.SCALE_F32 and consts["FP8Q_SCALE_UE8M0"] == fq.SCALE_UE8M0
+    assert consts["FP8Q_SCALE_UE8M0_PACKED"] == fq.SCALE_UE8M0_PACKED
     assert consts["FP8Q_GEMM_BLOCK128"] == fq.GEMM_BLOCK128 and consts["FP8Q_GEMM_MX32"] == fq.GEMM_MX32
 
 

@@ -353,3 +353,76 @@ def test_empty_gemm_is_noop():
                             torch.zeros((128, 128), dtype=torch.uint8, device="cuda"),
                             torch.ones((1, 1), dtype=torch.float32, device="cuda"), y.view(torch.bfloat16))
     torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- packed UE8M0
+def _packed_words(sa_bytes, layout):
+    """UE8M0 bytes [rows, K/128] -> device int32 words viewed as [rows, K/512] (row- or
+    column-major storage)."""
+    w = oracle.pack_ue8m0(sa_bytes)
+    if layout == "row":
+        return _dev(w)
+    return _dev(np.ascontiguousarray(w.T)).t()
+
+
+def _gpu_block_packed(a, sa_bytes, b, sb, layout):
+    f = fq()
+    M, K = a.shape
+    N = b.shape[0]
+    y = torch.full((M, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_gemm_blockscaled(_dev(a), _packed_words(sa_bytes, layout), _dev(b), _dev(sb), y.view(torch.bfloat16),
+                            f.GEMM_BLOCK128)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16)
+
+
+# Packed activation scales (four K blocks per word; K a multiple of 512) on every path: the
+# small-M kernel (M <= 128), the register-staged kernel (UE8M0 weight scales), the
+# direct-to-LDS 256x128 kernel with ragged M, N.
+@pytest.mark.parametrize("M,N,K", [(1, 256, 512), (100, 200, 1024), (130, 136, 512), (260, 300, 1024)])
+@pytest.mark.parametrize("layout", ["row", "col"])
+@pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
+def test_packed_activation_scales_full(M, N, K, layout, sb_kind):
+    w = synth.Workload("t", seed=80 + M, M=M, K=K, N=N, scale_fmt="ue8m0")
+    a, sa = synth.gemm_activation(w)
+    b, sbf = synth.weights(w)
+    sb = sbf if sb_kind == "f32" else synth.e8m0_exponents(8, sbf.shape[0], sbf.shape[1], tensor_id=78)
+    y = _gpu_block_packed(a, sa, b, sb, layout)
+    ys, ss = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_UE8M0, "row", _fmt(sb))
+    check(y, ys, ss, K, f"packed {M}x{N}x{K} {layout}")
+
+
+def test_packed_activation_scales_wide_sampled():
+    M, N, K = 4000, 4200, 1024
+    w = synth.Workload("t", seed=90, M=M, K=K, N=N, scale_fmt="ue8m0")
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    y = _gpu_block_packed(a, sa, b, sb, "col")
+    assert not np.any(y == SENT)
+    g = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, 256, 3839, 3840, 3999], g.integers(0, M, 40)]))
+    cols = np.unique(np.concatenate([[0, 63, 64, 255, 256, 4095, 4096, 4199], g.integers(0, N, 40)]))
+    ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
+    ys, ss = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_UE8M0, "row", at=(ms, ns))
+    check(y[ms, ns], ys, ss, K, "packed wide")
+
+
+def test_packed_activation_scales_masked():
+    E, cap, N, K = 5, 200, 384, 512
+    w = synth.Workload("m", seed=91, M=cap, K=K, N=N, E=E, scale_fmt="ue8m0", masked=True)
+    ops = [synth.gemm_activation(w, e) + synth.weights(w, e) for e in range(E)]
+    a, sa, b, sb = (np.stack([o[i] for o in ops]) for i in range(4))
+    words = oracle.pack_ue8m0(sa)  # [E, cap, K/512]
+    sa_dev = _dev(np.ascontiguousarray(words.transpose(0, 2, 1))).transpose(1, 2)  # column-major per expert
+    mm = np.array([0, 1, 200, 129, 128], dtype=np.int32)
+    f = fq()
+    y = torch.full((E, cap, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_grouped_gemm_masked(_dev(a), sa_dev, _dev(b), _dev(sb), y.view(torch.bfloat16), _dev(mm), 0)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().view(np.uint16)
+    for e in range(E):
+        r = mm[e]
+        if r > 0:
+            ys, ss = oracle.gemm_block128(a[e, :r], sa[e, :r], b[e], sb[e], oracle.SCALE_UE8M0, "row")
+            check(y[e, :r], ys, ss, K, f"expert {e}")
+        assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"

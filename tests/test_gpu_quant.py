@@ -351,3 +351,61 @@ def test_device_check():
     f = fq()
     assert f.fp8q_device_check(0) == f.OK
     assert f.fp8q_device_check(1000) == f.EDEVICE
+
+
+# ----------------------------------------------------------------- packed UE8M0 scales
+def _gpu_quant_packed(x_np, G, layout, silu=False, masked_m=None):
+    """GPU quant with FP8Q_SCALE_UE8M0_PACKED output: returns (q, words) with the words as
+    stored, [.., M, ng/4] ("row") or [.., ng/4, M] ("col"), as int32."""
+    f = fq()
+    x = _to_dev(x_np, oracle.BF16)
+    x3 = x if x.dim() == 3 else x[None]
+    E, M, W = x3.shape
+    K = W // 2 if silu else W
+    nw = K // G // 4
+    q = torch.full((E, M, K), FILL, dtype=torch.uint8, device="cuda")
+    shape = (E, M, 4 * nw) if layout == "row" else (E, nw, 4 * M)
+    s_store = torch.full(shape, FILL, dtype=torch.uint8, device="cuda").view(torch.int32)
+    s_view = s_store if layout == "row" else s_store.transpose(1, 2)
+    mm = None if masked_m is None else torch.from_numpy(np.asarray(masked_m, dtype=np.int32)).cuda()
+    fn = f.fp8q_silu_mul_group_quant if silu else f.fp8q_group_quant
+    fn(x3, q, s_view, G, masked_m=mm)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s_store.cpu().numpy()
+
+
+def _packed_case(x_np, G, layout, silu=False, masked_m=None):
+    x3 = x_np if x_np.ndim == 3 else x_np[None]
+    qg, wg = _gpu_quant_packed(x3, G, layout, silu, masked_m)
+    qo, so = oracle.group_quant(x3, G, oracle.SCALE_UE8M0, "row", silu=silu, masked_m=masked_m, fill=FILL)
+    wo = oracle.pack_ue8m0(so)  # [E, M, ng/4]; untouched rows keep FILL bytes in every word
+    if layout == "col":
+        wo = np.ascontiguousarray(wo.transpose(0, 2, 1))
+    _assert_same(qg, qo, "q")
+    _assert_same(wg, wo, "packed scale words")
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_packed_ue8m0_scales(G, layout):
+    x = synth.activations_bf16(41, 70, 1024, outlier_p=0.01)
+    _packed_case(x, G, layout)
+
+
+def test_packed_ue8m0_masked_and_silu():
+    E, M, K = 6, 40, 1024
+    x = _masked_input(E, M, K, 42)
+    mm = np.array([0, 1, 40, 39, 17, 3], dtype=np.int32)
+    _packed_case(x, 128, "col", masked_m=mm)
+    xs = _masked_input(5, 24, 2 * 512, 43)
+    _packed_case(xs, 128, "col", silu=True, masked_m=np.array([24, 0, 5, 23, 1], dtype=np.int32))
+
+
+def test_packed_ue8m0_needs_groups_in_fours():
+    f = fq()
+    x = torch.zeros((4, 384), dtype=torch.bfloat16, device="cuda")  # 3 groups of 128
+    q = torch.empty((4, 384), dtype=torch.uint8, device="cuda")
+    s = torch.full((4, 1), 7, dtype=torch.int32, device="cuda")
+    with pytest.raises(RuntimeError, match="multiple of 4 groups"):
+        f.fp8q_group_quant(x, q, s, 128)
+    assert torch.all(s == 7)

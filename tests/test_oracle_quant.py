@@ -232,3 +232,27 @@ def test_fused_silu_quant_equals_quant_of_silu_values():
     y = oracle.silu_mul(hf[:, :K], hf[:, K:])
     q2, s2 = oracle.group_quant(y, 128, oracle.SCALE_F32, "row", in_dtype=oracle.F32)
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+# ----------------------------------------------------------------- packed UE8M0 layout
+def test_pack_ue8m0_known_words():
+    """Group g of a row is byte g % 4 of word g / 4, least significant byte first."""
+    b = np.array([[1, 2, 3, 4, 5, 6, 7, 0x88], [0x7F, 0x80, 0, 0xFF, 9, 9, 9, 9]], dtype=np.uint8)
+    w = oracle.pack_ue8m0(b).astype(np.int64) & 0xFFFFFFFF
+    assert w.tolist() == [[0x04030201, 0x88070605], [0xFF00807F, 0x09090909]]
+
+
+def test_packed_format_constant_matches_header():
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "fp8q.h")).read()
+    assert int(re.search(r"#define FP8Q_SCALE_UE8M0_PACKED (\d+)", hdr).group(1)) == oracle.SCALE_UE8M0_PACKED
+
+
+def test_pack_ue8m0_round_trip_and_shape():
+    g = np.random.default_rng(3)
+    b = g.integers(0, 256, size=(3, 5, 16), dtype=np.uint8)
+    w = oracle.pack_ue8m0(b)
+    assert w.shape == (3, 5, 4) and w.dtype == np.int32
+    assert np.array_equal(oracle.unpack_ue8m0(w), b)
+    with pytest.raises(ValueError):
+        oracle.pack_ue8m0(b[..., :6])
