@@ -311,6 +311,35 @@ def suite(steps: int, warmup: int) -> list:
     del wq, q, y
     torch.cuda.empty_cache()
 
+    # MoE second stage: masked silu_and_mul + quant into packed UE8M0 words (column-major,
+    # four groups per word), then the masked grouped down-projection GEMM
+    w = synth.MASKED_DOWN
+    E, cap, K, N, G = w.E, w.M, w.K, w.N, w.G
+    mm = synth.masked_rows(w.seed, E, cap)
+    rows = int(mm.sum())
+    h = torch.from_numpy(np.stack([synth.quant_input(w, e) for e in range(E)])).to(dev).view(torch.bfloat16)
+    mmd = torch.from_numpy(mm).to(dev)
+    q = torch.empty((E, cap, K), dtype=torch.uint8, device=dev)
+    sq = fq.alloc_scales(E, cap, K // G, "ue8m0_packed", "col", dev)
+    ms = run(lambda i: fq.fp8q_silu_mul_group_quant(h, q, sq, G, masked_m=mmd, expected_m=cap // 2), 1)
+    report(w.name, "silu_mul_group_quant_masked", ms, nbytes=quant_bytes(rows, K, G, 2, 1, True),
+           extra={"sum_masked_m": rows, "scales": "ue8m0 packed, column-major words"})
+    del h
+    wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+    for e in range(E):
+        a, b = synth.weights(w, e)
+        wq[e].copy_(torch.from_numpy(a))
+        ws[e].copy_(torch.from_numpy(b))
+    y = torch.empty((E, cap, N), dtype=torch.bfloat16, device=dev)
+    ms = run(lambda i: fq.fp8q_grouped_gemm_masked(q, sq, wq, ws, y, mmd, cap // 2), 1)
+    active = int((mm > 0).sum())
+    report(w.name, "grouped_gemm_masked", ms, flops=2.0 * rows * N * K,
+           nbytes=rows * K + active * N * K + rows * (K // 128) + active * ws[0].numel() * 4 + rows * N * 2,
+           extra={"sum_masked_m": rows})
+    del wq, q, y
+    torch.cuda.empty_cache()
+
     # MXFP8
     w = synth.MX
     a, b, ea, eb = synth.mx_operands(w)

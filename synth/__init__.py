@@ -138,6 +138,10 @@ SILU = Workload("silu_down", seed=2, M=8192, K=2048, N=7168, scale_fmt="f32", la
 MASKED = Workload("masked_moe", seed=3, M=512, K=7168, N=4096, E=32, scale_fmt="ue8m0", layout="col",
                   masked=True)
 MX = Workload("mxfp8", seed=4, M=8192, K=8192, N=8192, mx=True)
+# MoE second stage: the masked expert buffer's gate|up halves (intermediate width 2048) go
+# through silu_and_mul + quant into the down projection back to the 7168-wide hidden size
+MASKED_DOWN = Workload("masked_moe_down", seed=5, M=512, K=2048, N=7168, E=32, scale_fmt="ue8m0",
+                       layout="col", masked=True, silu=True)
 
 
 def quant_input(w: Workload, expert: int | None = None) -> np.ndarray:

@@ -426,3 +426,44 @@ def test_packed_activation_scales_masked():
             ys, ss = oracle.gemm_block128(a[e, :r], sa[e, :r], b[e], sb[e], oracle.SCALE_UE8M0, "row")
             check(y[e, :r], ys, ss, K, f"expert {e}")
         assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
+
+
+def test_moe_second_stage_sampled():
+    """MoE second stage at full shape (the masked_moe_down workload's first 8 experts:
+    capacity 512, gate|up 2x2048 -> K=2048, N=7168): the GPU quantizes with silu into packed
+    UE8M0 words and feeds its own output to the masked GEMM. Expected values come from the
+    oracle alone: its quantization of sampled rows (compared bit-exactly with the GPU's) and
+    its GEMM of those rows on its own quantized operands."""
+    w = synth.MASKED_DOWN
+    E, cap, K, N, G = 8, w.M, w.K, w.N, w.G
+    mm = synth.masked_rows(w.seed, w.E, cap)[:E]
+    h = np.stack([synth.quant_input(w, e) for e in range(E)])  # [E, cap, 2K] bf16 bits
+    f = fq()
+    q = torch.full((E, cap, K), 0x5A, dtype=torch.uint8, device="cuda")
+    sq = f.alloc_scales(E, cap, K // G, "ue8m0_packed", "col", "cuda")
+    sq.fill_(0x5A5A5A5A)
+    mmd = _dev(mm.astype(np.int32))
+    f.fp8q_silu_mul_group_quant(_dev(h).view(torch.bfloat16), q, sq, G, masked_m=mmd, expected_m=cap // 2)
+    wts = [synth.weights(w, e) for e in range(E)]
+    wq = _dev(np.stack([t[0] for t in wts]))
+    ws = _dev(np.stack([t[1] for t in wts]))
+    y = torch.full((E, cap, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_grouped_gemm_masked(q, sq, wq, ws, y.view(torch.bfloat16), mmd, cap // 2)
+    torch.cuda.synchronize()
+    qg, wg, yg = q.cpu().numpy(), sq.cpu().numpy(), y.cpu().numpy().view(np.uint16)
+    g = np.random.default_rng(12)
+    got, want, size = [], [], []  # one compared set over all experts (as the other sampled tests)
+    for e in range(E):
+        r = int(mm[e])
+        assert np.all(yg[e, r:] == SENT), f"expert {e}: rows past masked_m written"
+        if r == 0:
+            continue
+        rows = np.unique(np.concatenate([[0, r - 1], g.integers(0, r, 6)]))
+        qo, so = oracle.group_quant(h[e][rows], G, oracle.SCALE_UE8M0, "row", silu=True)
+        assert np.array_equal(qg[e][rows], qo), f"expert {e}: codes"
+        assert np.array_equal(wg[e][rows], oracle.pack_ue8m0(so)), f"expert {e}: packed scale words"
+        cols = np.unique(np.concatenate([[0, 127, 128, N - 1], g.integers(0, N, 60)]))
+        ms, ns = (v.ravel() for v in np.meshgrid(np.arange(rows.size), cols, indexing="ij"))
+        ys, ss = oracle.gemm_block128(qo, so, wts[e][0], wts[e][1], oracle.SCALE_UE8M0, "row", at=(ms, ns))
+        got.append(yg[e][rows][ms, ns]); want.append(ys); size.append(ss)
+    check(np.concatenate(got), np.concatenate(want), np.concatenate(size), K, "moe second stage")
