@@ -43,6 +43,10 @@ _SIGNATURES = {
                               _I64, _I64, _I64, _INT, _P],
     "fp8q_grouped_gemm_masked": [_P, _I64, _I64, _P, _INT, _I64, _I64, _I64, _P, _I64, _I64, _P, _INT,
                                  _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64, _P],
+    "fp8q_grouped_gemm_segments": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _I64, _P, _INT, _I64, _I64, _I64,
+                                   _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P],
+    "fp8q_grouped_gemm_contiguous": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _I64, _P, _INT, _I64, _I64, _I64,
+                                     _P, _I64, _P, _I64, _I64, _I64, _I64, _P],
     "fp8q_status_string": [_INT],
     "fp8q_last_error": [],
     "fp8q_device_check": [_INT],
@@ -238,6 +242,56 @@ def fp8q_grouped_gemm_masked(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor,
         sa.stride(2), _ptr(b8), b8.stride(0), b8.stride(1), _ptr(sb), _scale_fmt_of(sb), sb.stride(0),
         sb.stride(1), sb.stride(2), _ptr(y), y.stride(0), y.stride(1), _ptr(masked_m), int(expected_m),
         E, cap, N, K, _stream(stream)))
+
+
+def _packed_rows_operands(a, sa, b, sb, y):
+    a8, b8 = _u8(a), _u8(b)
+    T, K = a8.shape
+    W, N = b8.shape[0], b8.shape[1]
+    if b8.dim() != 3 or b8.shape[2] != K or tuple(y.shape) != (T, N) or sb.dim() != 3:
+        raise ValueError("shape mismatch: a [T, K], b [W, N, K], sb [W, N/128, K/128], y [T, N]")
+    if a8.stride(1) != 1 or b8.stride(2) != 1 or y.stride(1) != 1:
+        raise ValueError("a, b and y must have unit stride along their last dimension")
+    return a8, b8, T, K, W, N
+
+
+def _dev_i32(t: torch.Tensor, what: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_cuda or t.dim() != 1 or t.stride(0) != 1:
+        raise ValueError(f"{what} must be a contiguous 1-D device int32 tensor")
+    return t
+
+
+def fp8q_grouped_gemm_segments(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                               y: torch.Tensor, seg_indptr: torch.Tensor, seg_weight: torch.Tensor | None = None,
+                               expected_rows: int = 0, stream=None) -> None:
+    """Rows [seg_indptr[s], seg_indptr[s+1]) of a [T, K] times weight seg_weight[s] (default s)
+    of b [W, N, K] into the same rows of y [T, N] (bf16). sa viewed as [T, K/128] (or packed
+    words [T, K/512]); sb as [W, N/128, K/128]."""
+    a8, b8, T, K, W, N = _packed_rows_operands(a, sa, b, sb, y)
+    si = _dev_i32(seg_indptr, "seg_indptr")
+    sw = None if seg_weight is None else _dev_i32(seg_weight, "seg_weight")
+    S = si.numel() - 1
+    if S < 0 or (sw is not None and sw.numel() != S):
+        raise ValueError("seg_indptr needs S + 1 entries and seg_weight S")
+    _check(load_library().fp8q_grouped_gemm_segments(
+        _ptr(a8), a8.stride(0), _ptr(sa), _scale_fmt_of(sa), sa.stride(0), sa.stride(1),
+        _ptr(b8), b8.stride(0), b8.stride(1), _ptr(sb), _scale_fmt_of(sb), sb.stride(0), sb.stride(1),
+        sb.stride(2), _ptr(y), y.stride(0), _ptr(si), _ptr(sw), S, T, W, N, K, int(expected_rows),
+        _stream(stream)))
+
+
+def fp8q_grouped_gemm_contiguous(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                                 y: torch.Tensor, m_indices: torch.Tensor, stream=None) -> None:
+    """Rows of a [T, K] tagged m_indices[t] (-1: padding; blocks of 128 rows, see the header)
+    times weight m_indices[t] of b [W, N, K] into y [T, N] (bf16)."""
+    a8, b8, T, K, W, N = _packed_rows_operands(a, sa, b, sb, y)
+    mi = _dev_i32(m_indices, "m_indices")
+    if mi.numel() != T:
+        raise ValueError("m_indices needs one entry per row of a")
+    _check(load_library().fp8q_grouped_gemm_contiguous(
+        _ptr(a8), a8.stride(0), _ptr(sa), _scale_fmt_of(sa), sa.stride(0), sa.stride(1),
+        _ptr(b8), b8.stride(0), b8.stride(1), _ptr(sb), _scale_fmt_of(sb), sb.stride(0), sb.stride(1),
+        sb.stride(2), _ptr(y), y.stride(0), _ptr(mi), T, W, N, K, _stream(stream)))
 
 
 def fp8q_device_check(device: int = 0) -> int:

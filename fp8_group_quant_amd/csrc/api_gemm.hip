@@ -42,6 +42,56 @@ int check_operands(const std::string& pre, const uint8_t* a, int64_t lda, const 
   return FP8Q_OK;
 }
 
+// shared tail of the two packed-row grouped calls: checks, then the launch
+int grouped_rows_entry(const std::string& pre, const uint8_t* a, int64_t lda, const void* sa, int sa_fmt,
+                       int64_t sa_sm, int64_t sa_sk, const uint8_t* b, int64_t b_se, int64_t ldb, const void* sb,
+                       int sb_fmt, int64_t sb_se, int64_t sb_sn, int64_t sb_sk, uint16_t* y, int64_t ldy,
+                       const int32_t* seg_indptr, const int32_t* seg_weight, const int32_t* m_indices, int64_t S,
+                       int64_t T, int64_t W, int64_t N, int64_t K, int64_t expected_rows, void* stream) {
+  set_error("");
+  if (S < 0 || T < 0 || W < 0 || b_se < 0 || sb_se < 0 || expected_rows < 0)
+    return fail(FP8Q_EINVAL, pre + "negative size, stride or expected_rows");
+  if (T >= (int64_t(1) << 31)) return fail(FP8Q_EUNSUPPORTED, pre + "at most 2^31 - 1 rows");
+  if (seg_indptr && S > 2048) return fail(FP8Q_EUNSUPPORTED, pre + "at most 2048 segments");
+  int rc = check_operands(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy, T, N,
+                          K, FP8Q_GEMM_BLOCK128);
+  if (rc != FP8Q_OK) return rc;
+  if (T == 0 || N == 0 || K == 0 || W == 0 || (seg_indptr && S == 0)) return FP8Q_OK;
+  if ((seg_indptr == nullptr) == (m_indices == nullptr)) return fail(FP8Q_EINVAL, pre + "row mapping is required");
+  if (b_se % 16 != 0) return fail(FP8Q_EALIGN, pre + "weight stride of b must be a multiple of 16 bytes");
+  if (W > 1 && b_se < (N - 1) * ldb + K) return fail(FP8Q_EINVAL, pre + "weights of b overlap");
+  rc = check_current_device();
+  if (rc != FP8Q_OK) return rc;
+  GemmParams p{};
+  p.a = a;
+  p.sa = sa;
+  p.b = b;
+  p.sb = sb;
+  p.y = y;
+  p.masked_m = nullptr;
+  p.seg_indptr = seg_indptr;
+  p.seg_weight = seg_indptr ? seg_weight : nullptr;
+  p.m_indices = m_indices;
+  p.M = T;
+  p.N = N;
+  p.K = K;
+  p.E = seg_indptr ? S : 1;
+  p.W = W;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldy = ldy;
+  p.b_se = b_se;
+  p.sa_sm = sa_sm;
+  p.sa_sk = sa_sk;
+  p.sb_sn = sb_sn;
+  p.sb_sk = sb_sk;
+  p.sb_se = sb_se;
+  p.sa_packed = sa_fmt == FP8Q_SCALE_UE8M0_PACKED ? 1 : 0;
+  p.sa_fmt = p.sa_packed ? FP8Q_SCALE_UE8M0 : sa_fmt;
+  p.sb_fmt = sb_fmt;
+  return launch_gemm_block128(p, expected_rows, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 }  // namespace fp8q
 
@@ -121,6 +171,7 @@ int fp8q_grouped_gemm_masked(const uint8_t* a, int64_t a_se, int64_t lda, const 
   p.N = N;
   p.K = K;
   p.E = E;
+  p.W = E;
   p.lda = lda;
   p.ldb = ldb;
   p.ldy = ldy;
@@ -137,6 +188,34 @@ int fp8q_grouped_gemm_masked(const uint8_t* a, int64_t a_se, int64_t lda, const 
   p.sa_fmt = p.sa_packed ? FP8Q_SCALE_UE8M0 : sa_fmt;
   p.sb_fmt = sb_fmt;
   return launch_gemm_block128(p, expected_m, static_cast<hipStream_t>(stream));
+}
+
+int fp8q_grouped_gemm_segments(const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t sa_sm,
+                               int64_t sa_sk, const uint8_t* b, int64_t b_se, int64_t ldb, const void* sb,
+                               int sb_fmt, int64_t sb_se, int64_t sb_sn, int64_t sb_sk, uint16_t* y, int64_t ldy,
+                               const int32_t* seg_indptr, const int32_t* seg_weight, int64_t S, int64_t T,
+                               int64_t W, int64_t N, int64_t K, int64_t expected_rows, void* stream) {
+  if (seg_indptr == nullptr && S > 0 && T > 0 && N > 0 && K > 0 && W > 0) {
+    fp8q::set_error("");
+    return fp8q::fail(FP8Q_EINVAL, "fp8q_grouped_gemm_segments: seg_indptr is required");
+  }
+  return fp8q::grouped_rows_entry("fp8q_grouped_gemm_segments: ", a, lda, sa, sa_fmt, sa_sm, sa_sk, b, b_se, ldb, sb,
+                            sb_fmt, sb_se, sb_sn, sb_sk, y, ldy, seg_indptr, seg_weight, nullptr, S, T, W, N, K,
+                            expected_rows, stream);
+}
+
+int fp8q_grouped_gemm_contiguous(const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t sa_sm,
+                                 int64_t sa_sk, const uint8_t* b, int64_t b_se, int64_t ldb, const void* sb,
+                                 int sb_fmt, int64_t sb_se, int64_t sb_sn, int64_t sb_sk, uint16_t* y, int64_t ldy,
+                                 const int32_t* m_indices, int64_t T, int64_t W, int64_t N, int64_t K,
+                                 void* stream) {
+  if (m_indices == nullptr && T > 0 && N > 0 && K > 0 && W > 0) {
+    fp8q::set_error("");
+    return fp8q::fail(FP8Q_EINVAL, "fp8q_grouped_gemm_contiguous: m_indices is required");
+  }
+  return fp8q::grouped_rows_entry("fp8q_grouped_gemm_contiguous: ", a, lda, sa, sa_fmt, sa_sm, sa_sk, b, b_se, ldb, sb,
+                            sb_fmt, sb_se, sb_sn, sb_sk, y, ldy, nullptr, nullptr, m_indices, 0, T, W, N, K, 0,
+                            stream);
 }
 
 }  // extern "C"

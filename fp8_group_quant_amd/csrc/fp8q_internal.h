@@ -45,8 +45,12 @@ struct GemmParams {
   const void* sb;
   uint16_t* y;
   const int32_t* masked_m;  // grouped masked only
-  int64_t M, N, K;          // M = capacity per expert when grouped
-  int64_t E;                // experts (1 for the dense GEMM)
+  const int32_t* seg_indptr;  // segments only: device int32[E + 1] row ranges of the packed rows
+  const int32_t* seg_weight;  // segments only: device int32[E] weight of each segment (or nullptr)
+  const int32_t* m_indices;   // grouped contiguous only: device int32[M] weight of each row, -1 = none
+  int64_t M, N, K;          // M = capacity per expert (masked) or packed rows (segments, contiguous)
+  int64_t E;                // experts (masked), segments, or 1
+  int64_t W;                // weights that B and sb hold (weight indices outside [0, W) are skipped)
   int64_t lda, ldb, ldy;
   int64_t a_se, b_se, y_se;
   int64_t sa_sm, sa_sk, sa_se;

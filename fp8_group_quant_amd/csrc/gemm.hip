@@ -107,9 +107,26 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 struct Tile {
-  int64_t e, tm, tn;
-  int64_t rows;  // valid rows of A for this expert (M, or clamped masked_m[e])
+  int64_t e, tm, tn;  // e: expert of A, its scales and Y (masked), else 0
+  int64_t rows;  // valid rows from row0 (M, clamped masked_m[e], or the segment's length)
+  int64_t row0;  // first row of the segment in A, its scales and Y (else 0)
+  int64_t we;    // weight (B, sb): the expert, the segment's weight, or the block's m_indices
+  bool skip;     // nothing to compute (weight index outside [0, W), or a padding block)
 };
+
+// rows of group g: masked experts (clamped masked_m[g]) or segments (clamped seg_indptr)
+__device__ __forceinline__ int64_t seg_begin(const GemmParams& p, int64_t g) {
+  const int64_t b = p.seg_indptr[g];
+  return b < 0 ? 0 : (b > p.M ? p.M : b);
+}
+__device__ __forceinline__ int64_t group_rows(const GemmParams& p, int64_t g) {
+  if (p.masked_m) {
+    const int64_t r = p.masked_m[g];
+    return r < 0 ? 0 : (r > p.M ? p.M : r);
+  }
+  const int64_t b = seg_begin(p, g), e = p.seg_indptr[g + 1];
+  return e < b ? 0 : (e > p.M ? p.M : e) - b;
+}
 
 // Global -> register staging of one K step of both operand tiles. Chunk i (16 bytes) of
 // a tile is row i/8, logical chunk i%8; consecutive threads read consecutive chunks of a
@@ -357,13 +374,14 @@ template <class C, bool MX, int SA_FMT, int SB_FMT>
 __device__ void run_tile(const GemmParams& p, Stage<C>& s0, Stage<C>& s1, const Tile& t) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int sa_w = (MX || SA_FMT == FP8Q_SCALE_UE8M0) ? 1 : 4;
+  // bytes per unit of the scale strides (packed UE8M0 strides count 4-byte words)
+  const int sa_w = MX ? 1 : (SA_FMT == FP8Q_SCALE_UE8M0 ? (p.sa_packed ? 4 : 1) : 4);
   const int sb_w = (MX || SB_FMT == FP8Q_SCALE_UE8M0) ? 1 : 4;
   TileRun<C, MX, SA_FMT, SB_FMT> r{p};
-  r.A = p.a + t.e * p.a_se;
-  r.B = p.b + t.e * p.b_se;
-  r.SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * sa_w;
-  r.SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * sb_w;
+  r.A = p.a + t.e * p.a_se + t.row0 * p.lda;
+  r.B = p.b + t.we * p.b_se;
+  r.SA = static_cast<const uint8_t*>(p.sa) + (t.e * p.sa_se + t.row0 * p.sa_sm) * sa_w;
+  r.SB = static_cast<const uint8_t*>(p.sb) + t.we * p.sb_se * sb_w;
   r.m0 = t.tm * C::BM;
   r.n0 = t.tn * C::BN;
   r.rmax = t.rows - 1;
@@ -401,11 +419,11 @@ __device__ void run_tile(const GemmParams& p, Stage<C>& s0, Stage<C>& s1, const 
   v4f (&acc)[C::SM][C::SN] = r.acc;
 
   // epilogue: lane holds Y[m][n..n+3], m = m0+wm*WTM+i*16+lane%16, n = n0+wn*WTN+j*16+4*(lane/16)
-  uint16_t* Y = p.y + t.e * p.y_se;
+  uint16_t* Y = p.y + t.e * p.y_se + t.row0 * p.ldy;
 #pragma unroll
   for (int i = 0; i < C::SM; i++) {
     const int64_t m = m0 + wm * C::WTM + i * 16 + (lane & 15);
-    if (m >= t.rows) continue;
+    if (m >= t.rows || (p.m_indices && p.m_indices[m] != t.we)) continue;
     uint16_t* yrow = Y + m * p.ldy;
 #pragma unroll
     for (int j = 0; j < C::SN; j++) {
@@ -432,14 +450,13 @@ template <class C>
 __device__ int64_t build_tile_list(const GemmParams& p, int32_t* part, int32_t* pref) {
   const int tid = threadIdx.x;
   const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
-  if (!p.masked_m) return ((p.M + C::BM - 1) / C::BM) * tiles_n;
+  if (!p.masked_m && !p.seg_indptr) return ((p.M + C::BM - 1) / C::BM) * tiles_n;
   const int E = static_cast<int>(p.E);
   const int per = (E + C::kThreads - 1) / C::kThreads;
   const int beg = min(tid * per, E), end = min(beg + per, E);
   int32_t local = 0;
   for (int i = beg; i < end; i++) {
-    int64_t r = p.masked_m[i];
-    r = r < 0 ? 0 : (r > p.M ? p.M : r);
+    const int64_t r = group_rows(p, i);
     local += static_cast<int32_t>(((r + C::BM - 1) / C::BM) * tiles_n);
   }
   part[tid] = local;
@@ -453,8 +470,7 @@ __device__ int64_t build_tile_list(const GemmParams& p, int32_t* part, int32_t* 
   int32_t run = part[tid] - local;
   for (int i = beg; i < end; i++) {
     pref[i] = run;
-    int64_t r = p.masked_m[i];
-    r = r < 0 ? 0 : (r > p.M ? p.M : r);
+    const int64_t r = group_rows(p, i);
     run += static_cast<int32_t>(((r + C::BM - 1) / C::BM) * tiles_n);
   }
   if (tid == C::kThreads - 1) pref[E] = part[C::kThreads - 1];
@@ -466,20 +482,29 @@ template <class C>
 __device__ Tile tile_at(const GemmParams& p, const int32_t* pref, int64_t t) {
   const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
   Tile tile;
-  if (p.masked_m) {
+  tile.row0 = 0;
+  tile.skip = false;
+  if (p.masked_m || p.seg_indptr) {
     int lo = 0, hi = static_cast<int>(p.E);  // pref[lo] <= t < pref[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (pref[mid] <= t) lo = mid; else hi = mid;
     }
-    int64_t r = p.masked_m[lo];
-    r = r < 0 ? 0 : (r > p.M ? p.M : r);
+    const int64_t r = group_rows(p, lo);
     const int64_t tm_e = (r + C::BM - 1) / C::BM;
     const int64_t local = t - pref[lo];
-    tile.e = lo;
-    tile.tm = local % tm_e;  // m tiles of one (expert, n tile) are adjacent
+    tile.tm = local % tm_e;  // m tiles of one (group, n tile) are adjacent
     tile.tn = local / tm_e;
     tile.rows = r;
+    if (p.masked_m) {
+      tile.e = lo;
+      tile.we = lo;
+    } else {
+      tile.e = 0;
+      tile.row0 = seg_begin(p, lo);
+      tile.we = p.seg_weight ? p.seg_weight[lo] : lo;
+      tile.skip = tile.we < 0 || tile.we >= p.W;
+    }
   } else {
     const int64_t tiles_m = (p.M + C::BM - 1) / C::BM;
     const int64_t in_group = C::GROUP_M * tiles_n;
@@ -489,7 +514,23 @@ __device__ Tile tile_at(const GemmParams& p, const int32_t* pref, int64_t t) {
     tile.tm = first_m + (t % in_group) % gm;
     tile.tn = (t % in_group) / gm;
     tile.rows = p.M;
+    tile.we = 0;
+    if (p.m_indices) {  // the block's weight is its first row's (blocks of BM = 128 rows)
+      tile.we = p.m_indices[tile.tm * C::BM];
+      tile.skip = tile.we < 0 || tile.we >= p.W;
+    }
   }
+  // The tile is the same for every lane; say so to the compiler, which cannot tell for values
+  // read from memory, so that the addresses built from it stay in scalar registers (every
+  // field is below 2^31).
+  auto u = [](int64_t v) { return static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(v))); };
+  tile.e = u(tile.e);
+  tile.tm = u(tile.tm);
+  tile.tn = u(tile.tn);
+  tile.rows = u(tile.rows);
+  tile.row0 = u(tile.row0);
+  tile.we = u(tile.we);
+  tile.skip = u(tile.skip ? 1 : 0) != 0;
   return tile;
 }
 
@@ -513,7 +554,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   extern __shared__ int32_t pref[];  // masked only, E + 1 entries
   const TileRange tr(build_tile_list<C>(p, part, pref));
   for (int64_t t = tr.beg; t < tr.end; t += tr.stride)
-    run_tile<C, MX, SA_FMT, SB_FMT>(p, stage0, stage1, tile_at<C>(p, pref, t));
+  {
+    const Tile tile = tile_at<C>(p, pref, t);
+    if (!tile.skip) run_tile<C, MX, SA_FMT, SB_FMT>(p, stage0, stage1, tile);  // (uniform per workgroup)
+  }
 }
 
 // ------------------------------------------------------------------ direct-to-LDS pipeline
@@ -872,8 +916,8 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   const int lane = r.lane, wave = r.wave;
   const int64_t m0 = t.tm * C::BM, n0 = t.tn * C::BN;
   const int64_t rmax = t.rows - 1, nmax = p.N - 1;
-  const uint8_t* A = p.a + t.e * p.a_se;
-  const uint8_t* B = p.b + t.e * p.b_se;
+  const uint8_t* A = p.a + t.e * p.a_se + t.row0 * p.lda;
+  const uint8_t* B = p.b + t.we * p.b_se;
   r.a_base = A + m0 * p.lda;
   r.b_base = B + n0 * p.ldb;
   // lane l of a 1 KB block: tile row blk*8 + l/8, LDS chunk l%8 = logical chunk ^ swz(row)
@@ -899,7 +943,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
     r.s_lds[q] = R::L::kSpare;
     if constexpr (SCM == kScE8Pk) {
       if (js < 4) {  // packed word (K blocks 4(kb/4)..+3) of tile row 64 js + lane
-        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
+        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + (t.e * p.sa_se + t.row0 * p.sa_sm) * 4;
         const int row = js * 64 + lane;
         r.s_base[q] = SA + m0 * p.sa_sm * 4;
         r.s_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
@@ -909,7 +953,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
       }
     } else if constexpr (SCM == kScF32Row) {
       if (js < 4) {  // fp32 scale of tile row 64 js + lane
-        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
+        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + (t.e * p.sa_se + t.row0 * p.sa_sm) * 4;
         const int row = js * 64 + lane;
         r.s_base[q] = SA + m0 * p.sa_sm * 4;
         r.s_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
@@ -918,7 +962,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
       }
     } else if constexpr (SCM == kScE8Col) {
       if (js == 0) {  // the 4 bytes of tile rows 4*lane .. 4*lane + 3 (clamped to the last full word)
-        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se;
+        const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se + t.row0;  // (row0 % 4 == 0)
         r.s_base[q] = SA + m0;
         r.s_off[q] = static_cast<uint32_t>(min(m0 + 4 * lane, p.M - 4) - m0);
         r.s_step[q] = p.sa_sk;
@@ -947,7 +991,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
       // past the last column reloads the last block's word.
       const int nb = js - (SCM == kScE8Col ? 1 : 4);
       if (nb >= 0 && nb < kNb) {
-        const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
+        const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.we * p.sb_se * 4;
         r.s_base[q] = SB + min(n0 / 128 + nb, nmax / 128) * p.sb_sn * 4;
         r.s_off[q] = 0;
         r.s_step[q] = p.sb_sk * 4;
@@ -968,14 +1012,14 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   r.ngroups = r.nkb / 4;
   if constexpr (SCM == kScF32Grp) {
     if (wave < 4) {
-      const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se * 4;
+      const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + (t.e * p.sa_se + t.row0 * p.sa_sm) * 4;
       const int row = wave * 64 + lane;
       r.g_role = true;
       r.g_base = SA + m0 * p.sa_sm * 4;
       r.g_off = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm * 4);
       r.g_lds = wave * 1024;
     } else if (wave - 4 < kNb) {  // weight block wave-4 of the tile (clamped past the last column)
-      const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.e * p.sb_se * 4;
+      const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.we * p.sb_se * 4;
       r.g_role = true;
       r.g_base = SB + min(n0 / 128 + (wave - 4), nmax / 128) * p.sb_sn * 4;
       r.g_lds = 4096 + (wave - 4) * 1024;
@@ -1043,12 +1087,12 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
   asm volatile("" ::: "memory");
 
   // epilogue: lane holds Y[m][n..n+3], m = m0+wm*WTM+i*16+lane%16, n = n0+wn*WTN+j*16+4*(lane/16)
-  uint16_t* Y = p.y + t.e * p.y_se;
+  uint16_t* Y = p.y + t.e * p.y_se + t.row0 * p.ldy;
   const int wm = r.wm, wn = r.wn;
 #pragma unroll
   for (int i = 0; i < C::SM; i++) {
     const int64_t m = m0 + wm * C::WTM + i * 16 + (lane & 15);
-    if (m >= t.rows) continue;
+    if (m >= t.rows || (p.m_indices && p.m_indices[m] != t.we)) continue;
     uint16_t* yrow = Y + m * p.ldy;
 #pragma unroll
     for (int j = 0; j < C::SN; j++) {
@@ -1074,7 +1118,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_dma_kernel(GemmParams p) 
   int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch, used before any load
   const TileRange tr(build_tile_list<C>(p, part, pref));
   for (int64_t t = tr.beg; t < tr.end; t += tr.stride)
-    run_tile_dma<C, SCM>(p, smem, tile_at<C>(p, pref, t));
+  {
+    const Tile tile = tile_at<C>(p, pref, t);
+    if (!tile.skip) run_tile_dma<C, SCM>(p, smem, tile);  // (uniform per workgroup)
+  }
 }
 
 // ------------------------------------------------------------------ skinny GEMM (small M)
@@ -1400,7 +1447,7 @@ bool try_skinny_dma(const GemmParams& p, hipStream_t s) {
 
 template <class C, bool MX, int SA_FMT, int SB_FMT>
 void launch(const GemmParams& p, int grid, hipStream_t s) {
-  const size_t lds = p.masked_m ? static_cast<size_t>(p.E + 1) * sizeof(int32_t) : 0;
+  const size_t lds = (p.masked_m || p.seg_indptr) ? static_cast<size_t>(p.E + 1) * sizeof(int32_t) : 0;
   hipLaunchKernelGGL((gemm_kernel<C, MX, SA_FMT, SB_FMT>), dim3(grid), dim3(C::kThreads), lds, s, p);
 }
 
@@ -1430,7 +1477,7 @@ int dma_mode(const GemmParams& p, bool mx) {
     const bool ok = p.sa_sm % 4 == 0 && p.sb_sn % 4 == 0 && u32_ok(p.sa) && u32_ok(p.sb);
     return ok ? kScMx : -1;
   }
-  const int64_t E = p.masked_m ? p.E : 1;
+  const int64_t E = (p.masked_m || p.seg_indptr) ? p.E : 1;  // groups in the device tile list
   if (p.sb_fmt != FP8Q_SCALE_F32) return -1;
   if (p.sa_packed)
     return p.sa_sm < (int64_t(1) << 22) && E <= DmaLayout<kScE8Pk, DmaCfg>::kMaxPrefix ? kScE8Pk : -1;
@@ -1442,7 +1489,8 @@ int dma_mode(const GemmParams& p, bool mx) {
     if (grp) return kScF32Grp;
     return E <= DmaLayout<kScF32Row, DmaCfg>::kMaxPrefix ? kScF32Row : -1;
   }
-  const bool col = p.sa_sm == 1 && p.sa_sk % 4 == 0 && p.M % 4 == 0 && u32_ok(p.sa) &&
+  // (segments start at any row, so their byte columns are not 4-byte aligned)
+  const bool col = p.sa_sm == 1 && p.sa_sk % 4 == 0 && p.M % 4 == 0 && u32_ok(p.sa) && !p.seg_indptr &&
                    (p.masked_m == nullptr || p.sa_se % 4 == 0) && E <= DmaLayout<kScE8Col, DmaCfg>::kMaxPrefix;
   return col ? kScE8Col : -1;
 }
@@ -1456,17 +1504,19 @@ void launch_dma(const GemmParams& p, int grid, hipStream_t s) {
 
 int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t stream) {
   using C = Large;
-  const int64_t tiles_n = (p.N + C::BN - 1) / C::BN;
-  int64_t tiles;
-  if (p.masked_m) {
+  // launch sizing only (the device tile list decides the work): masked and segment launches
+  // use the row hint; a segment adds at most one partial tile
+  auto tiles_for = [&](int64_t bm, int64_t bn) -> int64_t {
+    const int64_t tn = (p.N + bn - 1) / bn;
     const int64_t rows = expected_m > 0 ? std::min<int64_t>(expected_m, p.M) : p.M;
-    tiles = p.E * ((rows + C::BM - 1) / C::BM) * tiles_n;
-  } else {
-    tiles = ((p.M + C::BM - 1) / C::BM) * tiles_n;
-  }
-  const int grid = grid_for(tiles);
+    if (p.masked_m) return p.E * ((rows + bm - 1) / bm) * tn;
+    if (p.seg_indptr) return ((rows + bm - 1) / bm + p.E) * tn;
+    return ((p.M + bm - 1) / bm) * tn;
+  };
+  const int grid = grid_for(tiles_for(C::BM, C::BN));
   const bool a8 = p.sa_fmt == FP8Q_SCALE_UE8M0, b8 = p.sb_fmt == FP8Q_SCALE_UE8M0;
-  if (!p.masked_m && p.M <= kSkinnyMaxM) {
+  const bool grouped = p.masked_m || p.seg_indptr || p.m_indices;
+  if (!grouped && p.M <= kSkinnyMaxM) {
     if (try_skinny_dma(p, stream)) return finish("block-scaled GEMM launch");
     if (a8 && b8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, stream);
     else if (a8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, stream);
@@ -1475,17 +1525,22 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
     return finish("block-scaled GEMM launch");
   }
   const int dm = dma_mode(p, false);
-  if (p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScE8Pk)) {
-    // masked: 128-row tiles pad an expert's rows to a multiple of 128 instead of 256
+  if (p.m_indices && dm < 0)
+    return fail(FP8Q_EUNSUPPORTED, "block-scaled contiguous grouped GEMM: activation scales must be fp32, UE8M0 "
+                                   "column-major (rows a multiple of 4) or packed UE8M0 words, weight scales fp32");
+  if ((p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScE8Pk)) || (p.seg_indptr && dm >= 0) ||
+      p.m_indices) {
+    // grouped: 128-row tiles pad a group's rows to a multiple of 128 instead of 256 (and
+    // are the aligned blocks of the contiguous layout)
     using T = DmaCfgT;
-    const int64_t rows = expected_m > 0 ? std::min<int64_t>(expected_m, p.M) : p.M;
-    const int64_t tt = p.E * ((rows + T::BM - 1) / T::BM) * ((p.N + T::BN - 1) / T::BN);
-    if (dm == kScE8Col) launch_dma<kScE8Col, T>(p, grid_for(tt), stream);
-    else if (dm == kScE8Pk) launch_dma<kScE8Pk, T>(p, grid_for(tt), stream);
-    else launch_dma<kScF32Row, T>(p, grid_for(tt), stream);
+    const int g = grid_for(tiles_for(T::BM, T::BN));
+    if (dm == kScE8Col) launch_dma<kScE8Col, T>(p, g, stream);
+    else if (dm == kScE8Pk) launch_dma<kScE8Pk, T>(p, g, stream);
+    else if (dm == kScF32Grp) launch_dma<kScF32Grp, T>(p, g, stream);
+    else launch_dma<kScF32Row, T>(p, g, stream);
     return finish("block-scaled grouped GEMM launch");
   }
-  if (!p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp || dm == kScE8Pk)) {
+  if (!grouped && (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp || dm == kScE8Pk)) {
     // 256x256 tiles halve the operand bytes each tile loads per output; used when they
     // still give every CU a tile
     using W = DmaCfgW;

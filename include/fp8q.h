@@ -183,6 +183,55 @@ int fp8q_grouped_gemm_masked(const uint8_t* a, int64_t a_se, int64_t lda,
                              const int32_t* masked_m, int64_t expected_m,
                              int64_t E, int64_t cap, int64_t N, int64_t K, void* stream);
 
+/*
+ * fp8q_grouped_gemm_segments — BLOCK128 GEMM over ragged segments of packed rows
+ * [FI section 7: SegmentGEMM, x[sum(seg_lens), d_in] with weights[num_weights, d_out, d_in]
+ *  mapped through seg_indptr; Group GEMM for MoE experts with different token counts]
+ *
+ * a is [T][K] e4m3 packed rows (row t at a + t*lda) with activation scales sa indexed as
+ * in fp8q_gemm_blockscaled over the T rows; b holds W weights of [N][K] e4m3 (weight w at
+ * b + w*b_se, row stride ldb) with 128x128 scales sb + w*sb_se (indexed as in
+ * fp8q_gemm_blockscaled); y is [T][N] bf16 (row t at y + t*ldy).
+ * seg_indptr is a DEVICE int32[S + 1]: segment s is rows [seg_indptr[s], seg_indptr[s+1])
+ * (both ends clamped to [0, T], an end below its start meaning an empty segment).
+ * seg_weight is a DEVICE int32[S] or NULL: segment s uses weight seg_weight[s] (NULL: weight
+ * s); a segment whose weight index is outside [0, W) is skipped. Each row of a segment gets
+ * Y[t] = BLOCK128 product of row t of A and its segment's weight; rows of y in no computed
+ * segment are never written (rows in two segments get either). expected_rows is a host hint of
+ * the rows in all segments, for the launch size only (0: T).
+ * Requirements as for fp8q_gemm_blockscaled, plus S <= 2048, T < 2^31 [EUNSUPPORTED];
+ * b_se a multiple of 16 [EALIGN], weights not overlapping [EINVAL].
+ */
+int fp8q_grouped_gemm_segments(const uint8_t* a, int64_t lda,
+                               const void* sa, int sa_fmt, int64_t sa_sm, int64_t sa_sk,
+                               const uint8_t* b, int64_t b_se, int64_t ldb,
+                               const void* sb, int sb_fmt, int64_t sb_se, int64_t sb_sn, int64_t sb_sk,
+                               uint16_t* y, int64_t ldy,
+                               const int32_t* seg_indptr, const int32_t* seg_weight,
+                               int64_t S, int64_t T, int64_t W, int64_t N, int64_t K,
+                               int64_t expected_rows, void* stream);
+
+/*
+ * fp8q_grouped_gemm_contiguous — grouped GEMM over packed rows tagged with their expert
+ * [FI section 7: DeepGEMM GroupedContiguous, packed tokens + m_indices]
+ *
+ * Operands as in fp8q_grouped_gemm_segments. m_indices is a DEVICE int32[T]: the weight of
+ * each row, or -1 for a padding row. Rows are taken in aligned blocks of 128: a block whose
+ * first row holds a weight index e in [0, W) computes, for each of its rows t with
+ * m_indices[t] == e, Y[t] = BLOCK128 product of row t of A and weight e; every other row
+ * (padding, or a row whose index differs from its block's first row) is never written.
+ * (The layout this serves puts each expert's rows at a 128-aligned offset and pads them
+ * with -1 to a multiple of 128.)
+ * Activation scales: fp32 (any strides), UE8M0 column-major with T % 4 == 0, or
+ * UE8M0_PACKED; weight scales fp32 [EUNSUPPORTED otherwise]. Other requirements as above.
+ */
+int fp8q_grouped_gemm_contiguous(const uint8_t* a, int64_t lda,
+                                 const void* sa, int sa_fmt, int64_t sa_sm, int64_t sa_sk,
+                                 const uint8_t* b, int64_t b_se, int64_t ldb,
+                                 const void* sb, int sb_fmt, int64_t sb_se, int64_t sb_sn, int64_t sb_sk,
+                                 uint16_t* y, int64_t ldy, const int32_t* m_indices,
+                                 int64_t T, int64_t W, int64_t N, int64_t K, void* stream);
+
 /* Human-readable name of a status code. Never returns NULL. */
 const char* fp8q_status_string(int status);
 

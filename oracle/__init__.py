@@ -16,6 +16,8 @@ Parity status of each function (what pins it is in tests/test_oracle_*.py):
   group_quant               pinned: golden group, dequant-error bound, layout/mask invariants
   gemm                      pinned: exact Fraction arithmetic, torch float64 dequant-matmul,
                             one-hot operands
+  gemm_segments,            compositions of gemm_block128 over row slices (the plain definition);
+  gemm_contiguous           pinned: hand-derived row coverage, equality with whole-matrix calls
   pack_ue8m0, unpack_ue8m0  layout only (no arithmetic); pinned: hand-written words of known
                             bytes, round trip
 """
@@ -212,12 +214,61 @@ def gemm_block128(a: np.ndarray, sa: np.ndarray, b: np.ndarray, sb: np.ndarray, 
     b = np.ascontiguousarray(b)
     sa = np.ascontiguousarray(sa)
     sb = np.ascontiguousarray(sb)
+    for arr, fmt in ((sa, sa_fmt), (sb, sb_fmt)):
+        if arr.dtype != (np.float32 if fmt == SCALE_F32 else np.uint8):
+            raise ValueError("scale array dtype does not match its format")
     M, K = a.shape
     N = b.shape[0]
     kb = K // 128
     sa_sm, sa_sk = (kb, 1) if sa_layout == "row" else (1, M)
     return gemm_raw(a, K, sa, sa_fmt, sa_sm, sa_sk, b, K, sb, sb_fmt, kb, 1, M, N, K,
                     GEMM_BLOCK128, at)
+
+
+def _rows_of(sa: np.ndarray, lo: int, hi: int, sa_layout: str) -> np.ndarray:
+    return sa[lo:hi] if sa_layout == "row" else sa[:, lo:hi]
+
+
+def gemm_segments(a: np.ndarray, sa: np.ndarray, sa_fmt: int, b: np.ndarray, sb: np.ndarray,
+                  seg_indptr, seg_weight=None, sa_layout: str = "row", sb_fmt: int = SCALE_F32):
+    """SegmentGEMM over packed rows ([FI] section 7: ragged segments of x mapped by seg_indptr,
+    each against one of several weights): rows [seg_indptr[s], seg_indptr[s+1]) of a [T, K]
+    (ends clamped to [0, T]; an end below its start is an empty segment) times weight
+    w = seg_weight[s] (default s) of b [W, N, K] with scales sb [W, N/128, K/128]; a segment
+    whose w is outside [0, W) is skipped. sa is [T, K/128] ("row") or [K/128, T] ("col").
+    Returns (Y [T, N], S [T, N]) in fp64 as gemm_block128 does, NaN in rows no segment computes."""
+    T, N, W = a.shape[0], b.shape[1], b.shape[0]
+    Y = np.full((T, N), np.nan)
+    S = np.full((T, N), np.nan)
+    for s in range(len(seg_indptr) - 1):
+        lo = min(max(int(seg_indptr[s]), 0), T)
+        hi = min(int(seg_indptr[s + 1]), T)
+        w = s if seg_weight is None else int(seg_weight[s])
+        if hi <= lo or not 0 <= w < W:
+            continue
+        Y[lo:hi], S[lo:hi] = gemm_block128(a[lo:hi], _rows_of(sa, lo, hi, sa_layout), b[w], sb[w], sa_fmt,
+                                           sa_layout, sb_fmt)
+    return Y, S
+
+
+def gemm_contiguous(a: np.ndarray, sa: np.ndarray, sa_fmt: int, b: np.ndarray, sb: np.ndarray,
+                    m_indices, sa_layout: str = "row", block: int = 128, sb_fmt: int = SCALE_F32):
+    """Grouped contiguous layout ([FI] section 7: DeepGEMM packed tokens + m_indices): rows are
+    taken in aligned blocks of `block`; a block whose first row holds weight index e in
+    [0, W) computes its rows t with m_indices[t] == e against weight e; every other row is
+    left out (NaN). Operands as in gemm_segments."""
+    T, N, W = a.shape[0], b.shape[1], b.shape[0]
+    Y = np.full((T, N), np.nan)
+    S = np.full((T, N), np.nan)
+    mi = np.asarray(m_indices)
+    for b0 in range(0, T, block):
+        e = int(mi[b0])
+        if not 0 <= e < W:
+            continue
+        rows = b0 + np.nonzero(mi[b0:b0 + block] == e)[0]
+        sar = sa[rows] if sa_layout == "row" else sa[:, rows]
+        Y[rows], S[rows] = gemm_block128(a[rows], sar, b[e], sb[e], sa_fmt, sa_layout, sb_fmt)
+    return Y, S
 
 
 def gemm_mx32(a: np.ndarray, ea: np.ndarray, b: np.ndarray, eb: np.ndarray,

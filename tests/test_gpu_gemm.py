@@ -407,11 +407,16 @@ def test_packed_activation_scales_wide_sampled():
     check(y[ms, ns], ys, ss, K, "packed wide")
 
 
-def test_packed_activation_scales_masked():
+# fp32 weight scales: the 128x256 kernel; UE8M0 weight scales: the register-staged kernel,
+# whose expert offset into packed words counts 4 bytes per word
+@pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
+def test_packed_activation_scales_masked(sb_kind):
     E, cap, N, K = 5, 200, 384, 512
     w = synth.Workload("m", seed=91, M=cap, K=K, N=N, E=E, scale_fmt="ue8m0", masked=True)
     ops = [synth.gemm_activation(w, e) + synth.weights(w, e) for e in range(E)]
     a, sa, b, sb = (np.stack([o[i] for o in ops]) for i in range(4))
+    if sb_kind == "ue8m0":
+        sb = synth.e8m0_exponents(10, E * sb.shape[1], sb.shape[2], tensor_id=80).reshape(sb.shape)
     words = oracle.pack_ue8m0(sa)  # [E, cap, K/512]
     sa_dev = _dev(np.ascontiguousarray(words.transpose(0, 2, 1))).transpose(1, 2)  # column-major per expert
     mm = np.array([0, 1, 200, 129, 128], dtype=np.int32)
@@ -423,7 +428,7 @@ def test_packed_activation_scales_masked():
     for e in range(E):
         r = mm[e]
         if r > 0:
-            ys, ss = oracle.gemm_block128(a[e, :r], sa[e, :r], b[e], sb[e], oracle.SCALE_UE8M0, "row")
+            ys, ss = oracle.gemm_block128(a[e, :r], sa[e, :r], b[e], sb[e], oracle.SCALE_UE8M0, "row", _fmt(sb))
             check(y[e, :r], ys, ss, K, f"expert {e}")
         assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
 
@@ -467,3 +472,85 @@ def test_moe_second_stage_sampled():
         ys, ss = oracle.gemm_block128(qo, so, wts[e][0], wts[e][1], oracle.SCALE_UE8M0, "row", at=(ms, ns))
         got.append(yg[e][rows][ms, ns]); want.append(ys); size.append(ss)
     check(np.concatenate(got), np.concatenate(want), np.concatenate(size), K, "moe second stage")
+
+
+# ----------------------------------------------------------------------------- segments / contiguous
+def _grouped_operands(T, N, K, W, seed, scale_fmt):
+    w = synth.Workload("s", seed=seed, M=T, K=K, N=N, scale_fmt=scale_fmt)
+    a, sa = synth.gemm_activation(w)
+    ws = [synth.weights(w, e) for e in range(W)]
+    return a, sa, np.stack([x[0] for x in ws]), np.stack([x[1] for x in ws])
+
+
+def _sa_dev(sa, kind):
+    """sa [T, K/128] (fp32 or UE8M0 bytes) stored as kind: '<fmt>-row' or '<fmt>-col', fmt
+    f32, ue8m0 or packed (UE8M0 words of 4 K blocks)."""
+    if kind.startswith("packed"):
+        sa = oracle.pack_ue8m0(sa)
+    return _dev(sa) if kind.endswith("row") else _dev(np.ascontiguousarray(sa.T)).t()
+
+
+def _check_rows(yg, Y, S, K, what):
+    done = ~np.isnan(Y[:, 0])
+    assert np.all(yg[~done] == SENT), f"{what}: rows outside the computed ones were written"
+    check(yg[done], Y[done], S[done], K, what)
+
+
+# fp32 row scales with K % 512 == 0 take the 128x256 kernel with four-step scale groups, fp32
+# column scales its per-step loads, packed words their per-step word loads; UE8M0 bytes and
+# UE8M0 weight scales the register-staged kernel (segments start at any row).
+@pytest.mark.parametrize("kind", ["f32-row", "f32-col", "packed-col", "packed-row", "ue8m0-col"])
+@pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
+def test_segments_full(kind, sb_kind):
+    T, N, K, W = 720, 300, 1024, 3
+    a, sa, b, sbf = _grouped_operands(T, N, K, W, 70, "f32" if kind.startswith("f32") else "ue8m0")
+    sb = sbf if sb_kind == "f32" else synth.e8m0_exponents(9, W * sbf.shape[1], sbf.shape[2], tensor_id=79).reshape(sbf.shape)
+    indptr = np.array([10, 110, 110, 380, 700], dtype=np.int32)  # gaps [0,10) and [700,720)
+    weight = np.array([2, 0, 7, 1], dtype=np.int32)               # segment 2 uses no valid weight
+    f = fq()
+    y = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_grouped_gemm_segments(_dev(a), _sa_dev(sa, kind), _dev(b), _dev(sb), y.view(torch.bfloat16),
+                                 _dev(indptr), _dev(weight), expected_rows=600)
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy().view(np.uint16)
+    Y, S = oracle.gemm_segments(a, sa, _fmt(sa), b, sb, indptr, weight, sb_fmt=_fmt(sb))
+    _check_rows(yg, Y, S, K, f"segments {kind} sb {sb_kind}")
+
+
+def _contiguous_indices():
+    """640 rows in 5 blocks of 128: weight 1 (216 rows, then 40 padding), weight 0 (100 rows,
+    one stray index 2 at row 300, padding), a padding block, weight 2 with a stray 1."""
+    mi = np.full(640, -1, dtype=np.int32)
+    mi[0:216] = 1
+    mi[256:356] = 0
+    mi[300] = 2
+    mi[512:600] = 2
+    mi[620] = 1
+    return mi
+
+
+@pytest.mark.parametrize("kind", ["f32-row", "ue8m0-col", "packed-col"])
+def test_contiguous_full(kind):
+    T, N, K, W = 640, 300, 1024, 3
+    a, sa, b, sb = _grouped_operands(T, N, K, W, 71, "f32" if kind.startswith("f32") else "ue8m0")
+    mi = _contiguous_indices()
+    f = fq()
+    y = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, kind), _dev(b), _dev(sb), y.view(torch.bfloat16), _dev(mi))
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy().view(np.uint16)
+    Y, S = oracle.gemm_contiguous(a, sa, _fmt(sa), b, sb, mi)
+    _check_rows(yg, Y, S, K, f"contiguous {kind}")
+
+
+def test_contiguous_unsupported_scale_layout_writes_nothing():
+    T, N, K, W = 256, 128, 512, 2
+    a, sa, b, sb = _grouped_operands(T, N, K, W, 72, "ue8m0")
+    f = fq()
+    y = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
+    with pytest.raises(f.Fp8qError) as ei:  # UE8M0 bytes row-major: not moved by the 128-row kernel
+        f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, "ue8m0-row"), _dev(b), _dev(sb), y.view(torch.bfloat16),
+                                       _dev(np.zeros(T, dtype=np.int32)))
+    assert ei.value.status == f.EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(y == SENT_I16)

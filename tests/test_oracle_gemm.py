@@ -149,3 +149,48 @@ def test_mx32_scale_block_is_32_wide():
     eb = np.array([[129, 127]], dtype=np.uint8)  # 4, 1
     y, _ = oracle.gemm_mx32(a, ea, b, eb)
     assert y[0, 0] == 32 * 1 * 4 + 32 * 2 * 1
+
+
+# ------------------------------------------------------------- segments / contiguous
+def _seg_operands(T=20, K=256, N=40, W=3, seed=5):
+    g = np.random.default_rng(seed)
+    a = oracle.e4m3_encode(g.normal(0, 60, (T, K)).astype(np.float32))
+    sa = (2.0 ** g.integers(-8, -5, (T, K // 128))).astype(np.float32)
+    b = oracle.e4m3_encode(g.normal(0, 1, (W, N, K)).astype(np.float32))
+    sb = np.exp(g.normal(0, 0.5, (W, (N + 127) // 128, K // 128))).astype(np.float32)
+    return a, sa, b, sb
+
+
+def test_gemm_segments_rows_and_weights():
+    """Each computed row equals the whole-matrix product against its segment's weight; clamped
+    ends, empty segments, out-of-range weights and gaps leave rows out."""
+    a, sa, b, sb = _seg_operands()
+    full = [oracle.gemm_block128(a, sa, b[w], sb[w], oracle.SCALE_F32)[0] for w in range(3)]
+    indptr = [-3, 4, 4, 9, 12, 30]          # [0,4) [4,4) [4,9) [9,12) [12,20)
+    weight = [2, 0, 1, 7, 0]                 # segment 3 uses a weight outside [0, 3)
+    Y, _ = oracle.gemm_segments(a, sa, oracle.SCALE_F32, b, sb, indptr, weight)
+    want_w = {**{t: 2 for t in range(0, 4)}, **{t: 1 for t in range(4, 9)}, **{t: 0 for t in range(12, 20)}}
+    for t in range(20):
+        if t in want_w:
+            assert np.array_equal(Y[t], full[want_w[t]][t]), t
+        else:
+            assert np.all(np.isnan(Y[t])), t
+    # default weights (segment s uses weight s) and column-major scale storage give the same rows
+    Y2, _ = oracle.gemm_segments(a, np.ascontiguousarray(sa.T), oracle.SCALE_F32, b, sb, [0, 5, 20], None, "col")
+    assert np.array_equal(Y2[:5], full[0][:5]) and np.array_equal(Y2[5:], full[1][5:])
+
+
+def test_gemm_contiguous_block_rule():
+    """Blocks take the weight of their first row; rows with another index (padding -1, or a
+    stray index) are left out; a block starting with -1 or an index outside [0, W) is skipped."""
+    a, sa, b, sb = _seg_operands(T=24)
+    full = [oracle.gemm_block128(a, sa, b[w], sb[w], oracle.SCALE_F32)[0] for w in range(3)]
+    mi = np.array([1] * 6 + [-1] * 2 + [0, 0, 2, 0, -1, -1, -1, -1] + [-1] * 4 + [5] * 4, dtype=np.int32)
+    Y, _ = oracle.gemm_contiguous(a, sa, oracle.SCALE_F32, b, sb, mi, block=8)
+    for t in range(24):
+        if t < 6:
+            assert np.array_equal(Y[t], full[1][t]), t
+        elif t in (8, 9, 11):
+            assert np.array_equal(Y[t], full[0][t]), t
+        else:
+            assert np.all(np.isnan(Y[t])), t
