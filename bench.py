@@ -305,10 +305,42 @@ def suite(steps: int, warmup: int) -> list:
     y = torch.empty((E, cap, N), dtype=torch.bfloat16, device=dev)
     ms = run(lambda i: fq.fp8q_grouped_gemm_masked(q, sq, wq, ws, y, mmd, cap // 2), 1)
     active = int((mm > 0).sum())
-    report(w.name, "grouped_gemm_masked", ms, flops=2.0 * rows * N * K,
-           nbytes=rows * K + active * N * K + rows * (K // 128) + active * ws[0].numel() * 4 + rows * N * 2,
+    gemm_bytes = rows * K + active * N * K + rows * (K // 128) + active * ws[0].numel() * 4 + rows * N * 2
+    report(w.name, "grouped_gemm_masked", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
            extra={"sum_masked_m": rows})
-    del wq, q, y
+    del y
+    # the same experts' rows packed one after another: the contiguous layout (each expert at a
+    # 128-aligned offset, padded with m_indices = -1; UE8M0 column-major scales) and segments
+    # (no padding; packed UE8M0 words, which are the row-major bytes read as int32)
+    sq_store = sq.transpose(1, 2)  # [E, K/128, cap] storage
+    blocks = (mm.astype(np.int64) + 127) // 128
+    offs = np.concatenate([[0], np.cumsum(blocks * 128)])
+    Tc = int(offs[-1])
+    ac = torch.zeros((Tc, K), dtype=torch.uint8, device=dev)
+    sc = torch.zeros((K // G, Tc), dtype=torch.uint8, device=dev)
+    mi = torch.full((Tc,), -1, dtype=torch.int32, device=dev)
+    seg = np.concatenate([[0], np.cumsum(mm.astype(np.int64))])
+    asg = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+    ssg = torch.empty((rows, K // G), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        m, o, so = int(mm[e]), int(offs[e]), int(seg[e])
+        ac[o:o + m] = q[e, :m]
+        sc[:, o:o + m] = sq_store[e, :, :m]
+        mi[o:o + m] = e
+        asg[so:so + m] = q[e, :m]
+        ssg[so:so + m] = sq_store[e, :, :m].t()
+    yc = torch.empty((Tc, N), dtype=torch.bfloat16, device=dev)
+    ms = run(lambda i: fq.fp8q_grouped_gemm_contiguous(ac, sc.t(), wq, ws, yc, mi), 1)
+    report("contiguous_moe", "grouped_gemm_contiguous", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
+           extra={"rows": rows, "padded_rows": Tc, "layout": "masked_moe experts, 128-aligned, m_indices"})
+    del yc, ac, sc, mi
+    ys = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+    sid = torch.from_numpy(seg.astype(np.int32)).to(dev)
+    ms = run(lambda i: fq.fp8q_grouped_gemm_segments(asg, ssg.view(torch.int32), wq, ws, ys, sid,
+                                                     expected_rows=rows), 1)
+    report("segments_moe", "grouped_gemm_segments", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
+           extra={"rows": rows, "layout": "masked_moe experts, seg_indptr, packed UE8M0 words"})
+    del ys, asg, ssg, wq, q
     torch.cuda.empty_cache()
 
     # MoE second stage: masked silu_and_mul + quant into packed UE8M0 words (column-major,
