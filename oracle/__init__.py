@@ -13,7 +13,10 @@ Parity status of each function (what pins it is in tests/test_oracle_*.py):
                             hand-derived golden codes
   ue8m0_byte                pinned: exact rational ceil-power-of-two over every bf16 amax
   exp_spec, silu_mul        pinned: accuracy vs math.exp (<= 2 ulp), special values
-  group_quant               pinned: golden group, dequant-error bound, layout/mask invariants
+  group_quant               pinned: golden group, dequant-error bound, layout/mask invariants;
+                            per-token (G = K) and int8 output: brute-force rows in plain
+                            Python/fractions, the int8 dequant bound
+  int8_encode               pinned: hand-written ties, numpy's rint over a dense sweep
   gemm                      pinned: exact Fraction arithmetic, torch float64 dequant-matmul,
                             one-hot operands
   gemm_segments,            compositions of gemm_block128 over row slices (the plain definition);
@@ -50,13 +53,13 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     lib.ora_group_quant.restype = ctypes.c_int
     lib.ora_group_quant.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64,
-                                    _P, ctypes.c_int, _I64, _I64, _I64, ctypes.c_int, _P, ctypes.c_int,
-                                    _P, _P, _I64]
+                                    _P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, ctypes.c_int,
+                                    ctypes.c_int, _P, _P, _I64]
     lib.ora_gemm.restype = ctypes.c_int
     lib.ora_gemm.argtypes = [_P, _I64, _P, ctypes.c_int, _I64, _I64, _P, _I64, _P, ctypes.c_int,
                              _I64, _I64, _I64, _I64, _I64, ctypes.c_int, _P, _P, _I64, _P, _P]
     for name in ("ora_e4m3_decode_array", "ora_e4m3_encode_array", "ora_ue8m0_byte_array",
-                 "ora_exp_spec_array"):
+                 "ora_exp_spec_array", "ora_int8_encode_array"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [_P, _P, _I64]
     lib.ora_silu_mul_array.restype = None
@@ -82,6 +85,14 @@ def e4m3_encode(values) -> np.ndarray:
     v = np.ascontiguousarray(values, dtype=np.float32)
     out = np.empty(v.shape, dtype=np.uint8)
     _load().ora_e4m3_encode_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def int8_encode(values) -> np.ndarray:
+    """Nearest integer (ties to even) of fp32 values already within [-127, 127], as int8."""
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.int8)
+    _load().ora_int8_encode_array(_ptr(v), _ptr(out), v.size)
     return out
 
 
@@ -113,8 +124,10 @@ def group_quant_raw(x: np.ndarray, in_dtype: int, E: int, M: int, K: int, x_se: 
                     q: np.ndarray, q_se: int, q_sm: int, s: np.ndarray, scale_fmt: int,
                     s_se: int, s_sm: int, s_sg: int, group_size: int,
                     masked_m: np.ndarray | None = None, silu: bool = False,
-                    rows: tuple[np.ndarray, np.ndarray] | None = None) -> None:
-    """Same arguments as fp8q_group_quant (strides in elements), on host arrays.
+                    rows: tuple[np.ndarray, np.ndarray] | None = None,
+                    out_int8: bool = False) -> None:
+    """Same arguments as fp8q_group_quant (strides in elements), on host arrays; with
+    out_int8 those of fp8q_group_quant_int8. group_size == K is per-token quantization.
     `rows` = (e_indices, m_indices) restricts the work to those rows."""
     mm = None if masked_m is None else np.ascontiguousarray(masked_m, dtype=np.int32)
     re = rm = None
@@ -125,7 +138,7 @@ def group_quant_raw(x: np.ndarray, in_dtype: int, E: int, M: int, K: int, x_se: 
         n_rows = re.size
     rc = _load().ora_group_quant(_ptr(x), in_dtype, E, M, K, x_se, x_sm, _ptr(q), q_se, q_sm,
                                  _ptr(s), scale_fmt, s_se, s_sm, s_sg, group_size, _ptr(mm),
-                                 int(silu), _ptr(re), _ptr(rm), n_rows)
+                                 int(silu), int(out_int8), _ptr(re), _ptr(rm), n_rows)
     if rc != 0:
         raise ValueError("oracle group_quant: unsupported arguments")
 
@@ -133,10 +146,11 @@ def group_quant_raw(x: np.ndarray, in_dtype: int, E: int, M: int, K: int, x_se: 
 def group_quant(x: np.ndarray, group_size: int, scale_fmt: int, layout: str = "row",
                 in_dtype: int = BF16, silu: bool = False, masked_m: np.ndarray | None = None,
                 rows: tuple[np.ndarray, np.ndarray] | None = None,
-                fill: int = 0) -> tuple[np.ndarray, np.ndarray]:
+                fill: int = 0, out_int8: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """Quantizes x ([M, K] or [E, M, K]; with silu the last dim is 2K) into freshly
-    allocated outputs: q [.., M, K] uint8 and scales [.., M, K/G] (layout "row") or
-    [.., K/G, M] (layout "col"), float32 or uint8. Untouched entries hold `fill`."""
+    allocated outputs: q [.., M, K] uint8 (e4m3 bytes; int8 with out_int8) and scales
+    [.., M, K/G] (layout "row") or [.., K/G, M] (layout "col"), float32 or uint8.
+    group_size == K gives per-token scales [.., M, 1]. Untouched entries hold `fill`."""
     x3 = x if x.ndim == 3 else x[None]
     E, M, W = x3.shape
     K = W // 2 if silu else W
@@ -153,7 +167,9 @@ def group_quant(x: np.ndarray, group_size: int, scale_fmt: int, layout: str = "r
     if scale_fmt == SCALE_F32:
         s = s.view(np.float32)
     group_quant_raw(x3, in_dtype, E, M, K, M * W, W, q, M * K, K, s, scale_fmt, M * ng, s_sm, s_sg,
-                    group_size, masked_m, silu, rows)
+                    group_size, masked_m, silu, rows, out_int8)
+    if out_int8:
+        q = q.view(np.int8)
     if x.ndim == 2:
         return q[0], s[0]
     return q, s

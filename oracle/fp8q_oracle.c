@@ -30,9 +30,17 @@
  *     scale" shape as the printed UE8M0 reference.
  *   - Rounding to e4m3 is round-to-nearest, ties to even mantissa, after the clamp.
  *   - exp inside silu is a fixed fp32 sequence (declared in fp8q.h and ora_exp_spec).
+ *   - Per-token quantization ([TF] per-token FP8 example: scale [M, 1]) is the group rule
+ *     with one group spanning the whole row (G = K).
+ *   - The int8 output ([PR30924] 关键文件: the ref_int8 test reference; 风险与影响: int8
+ *     codes that move by one when the division is approximate) is not printed: the same
+ *     shape as the fp32-scale rule with 127 in place of 448, i.e. s = amax/127 stored as
+ *     fp32, multiplier 1/s, clamp to +-127, round to the nearest integer with ties to
+ *     even, stored as a two's-complement byte. fp32 scales only.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------------------------
@@ -66,6 +74,24 @@ uint8_t ora_e4m3_encode(float v) {
     }
   }
   return (uint8_t)((signbit(v) ? 0x80 : 0x00) | best);
+}
+
+/* ------------------------------------------------------------------------------------
+ * int8 code: nearest integer, ties to the even integer. v must be finite with
+ * |v| <= 127 (the caller clamps first). Written out with floor so the tie rule is visible.
+ * ---------------------------------------------------------------------------------- */
+int8_t ora_int8_encode(float v) {
+  double d = (double)v; /* exact */
+  double f = floor(d);
+  double frac = d - f; /* exact: f and d are within one unit */
+  double r;
+  if (frac > 0.5)
+    r = f + 1.0;
+  else if (frac < 0.5)
+    r = f;
+  else
+    r = (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+  return (int8_t)(int)r;
 }
 
 /* ------------------------------------------------------------------------------------
@@ -103,6 +129,7 @@ static float load_elem(const void* base, int dtype, int64_t idx) {
  * group scale  [PR30924 ref_fp8_ue8m0]
  * ---------------------------------------------------------------------------------- */
 #define ORA_FMAX 448.0f
+#define ORA_IMAX 127.0f /* int8 output: largest code used */
 #define ORA_EPS 1e-10f
 
 /* UE8M0 byte: fp32 r = amax / 448; exponent field of r, plus one when r's mantissa
@@ -170,16 +197,17 @@ float ora_silu_mul(float g, float u) {
 /* ------------------------------------------------------------------------------------
  * group quantization of one row  [PR30924 items 1-2, ref_fp8_ue8m0; TF]
  * row_in points at element (e, m, 0); with silu the row holds 2K elements
- * (gate = [0, K), up = [K, 2K)).
+ * (gate = [0, K), up = [K, 2K)). vals is caller scratch of at least G floats.
+ * out_int8: int8 codes and fp32 scales s = amax/127 (reading above); otherwise e4m3.
  * ---------------------------------------------------------------------------------- */
 static void quant_row(const void* x, int in_dtype, int64_t row_off, int64_t K, int silu,
                       uint8_t* q_row, void* s, int scale_fmt, int64_t s_row_off, int64_t s_sg,
-                      int G) {
+                      int64_t G, int out_int8, float* vals) {
   int64_t ngroups = K / G;
+  float qmax = out_int8 ? ORA_IMAX : ORA_FMAX;
   for (int64_t g = 0; g < ngroups; g++) {
     /* values of this group, in fp32 */
-    float vals[128];
-    for (int i = 0; i < G; i++) {
+    for (int64_t i = 0; i < G; i++) {
       int64_t k = g * G + i;
       if (silu)
         vals[i] = ora_silu_mul(load_elem(x, in_dtype, row_off + k),
@@ -189,7 +217,7 @@ static void quant_row(const void* x, int in_dtype, int64_t row_off, int64_t K, i
     }
     /* group absmax, not below EPS */
     float amax = 0.0f;
-    for (int i = 0; i < G; i++) {
+    for (int64_t i = 0; i < G; i++) {
       float a = fabsf(vals[i]);
       if (a > amax) amax = a;
     }
@@ -202,37 +230,46 @@ static void quant_row(const void* x, int in_dtype, int64_t row_off, int64_t K, i
       ((uint8_t*)s)[sidx] = e;
       inv = ora_ue8m0_multiplier(e);
     } else {
-      float sc = amax / ORA_FMAX;
+      float sc = amax / qmax;
       ((float*)s)[sidx] = sc;
       inv = 1.0f / sc;
     }
-    /* multiply, clamp to [-448, 448], round to e4m3 */
-    for (int i = 0; i < G; i++) {
+    /* multiply, clamp to [-qmax, qmax], round to the output code */
+    for (int64_t i = 0; i < G; i++) {
       float v = vals[i] * inv;
-      if (v > ORA_FMAX) v = ORA_FMAX;
-      if (v < -ORA_FMAX) v = -ORA_FMAX;
-      q_row[g * G + i] = ora_e4m3_encode(v);
+      if (v > qmax) v = qmax;
+      if (v < -qmax) v = -qmax;
+      if (out_int8)
+        q_row[g * G + i] = (uint8_t)ora_int8_encode(v);
+      else
+        q_row[g * G + i] = ora_e4m3_encode(v);
     }
   }
 }
 
-/* Mirrors fp8q_group_quant / fp8q_silu_mul_group_quant on host memory. masked_m is a
- * host int32[E] or NULL (flat). If rows_e/rows_m are non-NULL only those n_rows rows
- * are processed (they must be rows the call would process); otherwise all rows are.
- * Returns 0, or -1 for arguments the oracle does not handle. */
+/* Mirrors fp8q_group_quant / fp8q_silu_mul_group_quant (out_int8 = 0) and
+ * fp8q_group_quant_int8 (out_int8 = 1) on host memory. G is 32, 64, 128, or K (one group
+ * per row: per-token quantization). masked_m is a host int32[E] or NULL (flat). If
+ * rows_e/rows_m are non-NULL only those n_rows rows are processed (they must be rows the
+ * call would process); otherwise all rows are. Returns 0, or -1 for arguments the oracle
+ * does not handle. */
 int ora_group_quant(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K,
                     int64_t x_se, int64_t x_sm, uint8_t* q, int64_t q_se, int64_t q_sm,
                     void* s, int scale_fmt, int64_t s_se, int64_t s_sm, int64_t s_sg,
-                    int G, const int32_t* masked_m, int silu,
+                    int64_t G, const int32_t* masked_m, int silu, int out_int8,
                     const int64_t* rows_e, const int64_t* rows_m, int64_t n_rows) {
-  if (G != 32 && G != 64 && G != 128) return -1;
-  if (K % G != 0) return -1;
+  if (G != 32 && G != 64 && G != 128 && G != K) return -1;
+  if (G <= 0 || K % G != 0) return -1;
+  if (out_int8 && scale_fmt != ORA_SCALE_F32) return -1;
+  float* vals = (float*)malloc((size_t)G * sizeof(float));
+  if (!vals) return -1;
   if (rows_e && rows_m) {
     for (int64_t i = 0; i < n_rows; i++) {
       int64_t e = rows_e[i], m = rows_m[i];
       quant_row(x, in_dtype, e * x_se + m * x_sm, K, silu, q + e * q_se + m * q_sm, s,
-                scale_fmt, e * s_se + m * s_sm, s_sg, G);
+                scale_fmt, e * s_se + m * s_sm, s_sg, G, out_int8, vals);
     }
+    free(vals);
     return 0;
   }
   for (int64_t e = 0; e < E; e++) {
@@ -244,8 +281,9 @@ int ora_group_quant(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K
     }
     for (int64_t m = 0; m < rows; m++)
       quant_row(x, in_dtype, e * x_se + m * x_sm, K, silu, q + e * q_se + m * q_sm, s,
-                scale_fmt, e * s_se + m * s_sm, s_sg, G);
+                scale_fmt, e * s_se + m * s_sm, s_sg, G, out_int8, vals);
   }
+  free(vals);
   return 0;
 }
 
@@ -319,6 +357,10 @@ void ora_e4m3_decode_array(const uint8_t* in, double* out, int64_t n) {
 
 void ora_e4m3_encode_array(const float* in, uint8_t* out, int64_t n) {
   for (int64_t i = 0; i < n; i++) out[i] = ora_e4m3_encode(in[i]);
+}
+
+void ora_int8_encode_array(const float* in, int8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = ora_int8_encode(in[i]);
 }
 
 void ora_ue8m0_byte_array(const float* amax, uint8_t* out, int64_t n) {

@@ -133,6 +133,108 @@ def test_per_token_group_equals_whole_row():
     assert np.array_equal(s[:, 0], (amax / np.float32(448)).astype(np.float32))
 
 
+@pytest.mark.parametrize("K", [1024, 7168])
+def test_per_token_scale_is_the_row_maximum(K):
+    """G = K: one scale per row, from the maximum over the whole row (numpy's max, not
+    the oracle's loop); the dequant bound holds against that one scale."""
+    x = synth.activations_bf16(30, 6, K, outlier_p=0.002)
+    xf = _bf16_to_f32(x)
+    amax = np.abs(xf).max(1)
+    qu, su = oracle.group_quant(x, K, oracle.SCALE_UE8M0, "row")
+    assert su.shape == (6, 1)
+    assert np.array_equal(su[:, 0], oracle.ue8m0_byte(amax))
+    _dequant_check(oracle.SCALE_UE8M0, x, K, 0.0)
+    qf, sf = oracle.group_quant(x, K, oracle.SCALE_F32, "col")
+    assert sf.shape == (1, 6)
+    assert np.array_equal(sf[0], amax / np.float32(448))
+    _dequant_check(oracle.SCALE_F32, x, K, 2.0 ** -22)
+
+
+def test_per_token_equals_group_quant_when_every_group_holds_the_row_max():
+    """Rows whose every 128-group contains the row's largest magnitude have the same
+    scale in every group, so per-token and G = 128 quantization agree code for code."""
+    M, K = 8, 1024
+    x = synth.activations_bf16(31, M, K)
+    xf = _bf16_to_f32(x).copy()
+    big = np.float32(6.5)  # larger than any N(0,1) draw here, bf16-exact
+    assert np.abs(xf).max() < big
+    for g in range(K // 128):
+        xf[:, g * 128 + (g * 37) % 128] = np.where(np.arange(M) % 2 == 0, big, -big)
+    xb = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    for fmt in (oracle.SCALE_UE8M0, oracle.SCALE_F32):
+        qt, st = oracle.group_quant(xb, K, fmt, "row")
+        qg, sg = oracle.group_quant(xb, 128, fmt, "row")
+        assert np.array_equal(qt, qg)
+        assert np.all(sg == st)
+
+
+# ----------------------------------------------------------------------------- int8 output
+def test_int8_encode_ties_to_even():
+    v = np.float32([2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5, -1.5, 126.5, -126.5, 127, -127, 0.49999997, 2.5000002])
+    assert oracle.int8_encode(v).tolist() == [2, 4, -2, -4, 0, 0, 2, -2, 126, -126, 127, -127, 0, 3]
+
+
+def test_int8_encode_matches_numpy_rint():
+    v = np.linspace(-127.0, 127.0, 2_000_001, dtype=np.float64).astype(np.float32)
+    halves = (np.arange(-254, 255) / 2.0).astype(np.float32)
+    v = np.concatenate([v, halves, np.nextafter(halves, np.float32(0)), np.nextafter(halves, np.float32(200))])
+    v = np.clip(v, -127, 127)
+    assert np.array_equal(oracle.int8_encode(v), np.rint(v).astype(np.int8))
+
+
+def test_int8_golden_groups():
+    """Hand-derived: a group whose amax is 127 has s = 1 and multiplier 1, so each code is
+    the input rounded to the nearest integer (ties to even); amax 254 gives s = 2 and
+    multiplier 1/2."""
+    a = [127.0, -127.0, 2.5, 3.5, -2.5, 0.5, 1.5, 99.5, -0.25, 64.0]
+    b = [254.0, 5.0, 7.0, -254.0, -3.0, 0.75, 100.0, 1.0, -1.0, 2.0]
+    ca = [127, -127, 2, 4, -2, 0, 2, 100, 0, 64]
+    cb = [127, 2, 4, -127, -2, 0, 50, 0, 0, 1]
+    pad = [0.0] * (32 - len(a))
+    x = _bf16([a + pad, b + pad])
+    assert np.array_equal(_bf16_to_f32(x).astype(np.float64), np.array([a + pad, b + pad]))
+    q, s = oracle.group_quant(x, 32, oracle.SCALE_F32, "row", out_int8=True)
+    assert q.dtype == np.int8
+    assert q[0, :10].tolist() == ca and q[1, :10].tolist() == cb
+    assert np.all(q[:, 10:] == 0)
+    assert s[:, 0].tolist() == [1.0, 2.0]
+
+
+@pytest.mark.parametrize("G", [32, 128, 1024])
+def test_int8_dequant_error_within_half_step(G):
+    """|q * s - x| <= s / 2 (plus a few fp32 roundings of x * (1/s)), codes within
+    [-127, 127], and each group's largest magnitude maps to +-127."""
+    M, K = 16, 1024
+    x = synth.activations_bf16(32, M, K, outlier_p=0.01)
+    xf = _bf16_to_f32(x).astype(np.float64)
+    q, s = oracle.group_quant(x, G, oracle.SCALE_F32, "row", out_int8=True)
+    sc = np.repeat(s.astype(np.float64), G, axis=1)
+    err = np.abs(q.astype(np.float64) * sc - xf)
+    assert np.all(err <= 0.5 * sc * (1 + 2.0 ** -20) + 2.0 ** -22 * np.abs(xf))
+    assert q.min() >= -127 and q.max() <= 127
+    amax = np.abs(xf).reshape(M, K // G, G).max(-1)
+    assert np.array_equal(np.abs(q.astype(np.int64)).reshape(M, K // G, G).max(-1), np.full(amax.shape, 127))
+    assert np.array_equal(s, (amax.astype(np.float32) / np.float32(127)).astype(np.float32))
+
+
+def test_int8_all_zero_row_and_ue8m0_rejected():
+    x = np.zeros((1, 128), dtype=np.uint16)
+    q, s = oracle.group_quant(x, 128, oracle.SCALE_F32, "row", out_int8=True)
+    assert np.all(q == 0) and s[0, 0] == np.float32(1e-10) / np.float32(127)
+    with pytest.raises(ValueError):
+        oracle.group_quant(x, 128, oracle.SCALE_UE8M0, "row", out_int8=True)
+
+
+def test_int8_silu_equals_int8_of_silu_values():
+    M, K = 4, 256
+    h = synth.activations_bf16(33, M, 2 * K)
+    q, s = oracle.group_quant(h, 64, oracle.SCALE_F32, "row", silu=True, out_int8=True)
+    hf = _bf16_to_f32(h)
+    y = oracle.silu_mul(hf[:, :K], hf[:, K:])
+    q2, s2 = oracle.group_quant(y, 64, oracle.SCALE_F32, "row", in_dtype=oracle.F32, out_int8=True)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
 def test_masked_rows_untouched_and_flat_rows_match():
     E, M, K = 4, 16, 256
     x = np.stack([synth.activations_bf16(17, M, K, tensor_id=100 + e) for e in range(E)])
