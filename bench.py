@@ -284,6 +284,25 @@ def suite(steps: int, warmup: int) -> list:
         del sets
         torch.cuda.empty_cache()
 
+    # quant variants on the dense M=4096 activations: per-token (G = K, one fp32 scale per
+    # row) and int8 output (G = 128, fp32 row-major scales)
+    w = synth.dense(4096)
+    M, K = w.M, w.K
+    x = torch.from_numpy(synth.quant_input(w)).to(dev).view(torch.bfloat16)
+    ns = _nsets(x.numel() * 3)
+    sets = [dict(x=x.clone(), q=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                 s=torch.empty((M, 1), dtype=torch.float32, device=dev),
+                 s8=torch.empty((M, K // 128), dtype=torch.float32, device=dev)) for _ in range(ns)]
+    ms = run(lambda i: fq.fp8q_group_quant(sets[i % ns]["x"], sets[i % ns]["q"], sets[i % ns]["s"], K), ns)
+    report("dense_m4096_per_token", "token_quant", ms, nbytes=quant_bytes(M, K, K, 2, 4, False),
+           extra={"scales": "f32 [M, 1]"})
+    ms = run(lambda i: fq.fp8q_group_quant_int8(sets[i % ns]["x"], sets[i % ns]["q"].view(torch.int8),
+                                                sets[i % ns]["s8"], 128), ns)
+    report("dense_m4096_int8", "group_quant_int8", ms, nbytes=quant_bytes(M, K, 128, 2, 4, False),
+           extra={"scales": "f32 row-major"})
+    del sets, x
+    torch.cuda.empty_cache()
+
     # masked MoE: masked quant then masked grouped GEMM
     w = synth.MASKED
     E, cap, K, N, G = w.E, w.M, w.K, w.N, w.G

@@ -39,6 +39,8 @@ _SIGNATURES = {
                          _I64, _INT, _P, _I64, _P],
     "fp8q_silu_mul_group_quant": [_P, _INT, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _INT, _I64,
                                   _I64, _I64, _INT, _P, _I64, _P],
+    "fp8q_group_quant_int8": [_P, _INT, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _INT, _I64,
+                              _I64, _I64, _INT, _P, _I64, _P],
     "fp8q_gemm_blockscaled": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _P, _INT, _I64, _I64, _P, _I64,
                               _I64, _I64, _I64, _INT, _P],
     "fp8q_grouped_gemm_masked": [_P, _I64, _I64, _P, _INT, _I64, _I64, _I64, _P, _I64, _I64, _P, _INT,
@@ -159,8 +161,19 @@ def fp8q_group_quant(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, group_si
                      masked_m: torch.Tensor | None = None, expected_m: int = 0, stream=None) -> None:
     """x [M, K] or [E, M, K] (bf16/f16/f32) -> q (uint8 or float8_e4m3fn, same shape) and
     s: a [.., M, K/G] view (float32 = fp32 scales, uint8 = UE8M0); its strides choose the
-    row- or column-major layout."""
+    row- or column-major layout. group_size == K is per-token quantization (s [.., M, 1])."""
     _quant("fp8q_group_quant", x, q, s, group_size, masked_m, expected_m, stream, False)
+
+
+def fp8q_group_quant_int8(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, group_size: int = 128,
+                          masked_m: torch.Tensor | None = None, expected_m: int = 0, stream=None) -> None:
+    """As fp8q_group_quant with int8 codes in q (torch.int8) and float32 scales
+    s = amax / 127."""
+    if q.dtype != torch.int8:
+        raise ValueError("q must be an int8 tensor")
+    if s.dtype != torch.float32:
+        raise ValueError("int8 output takes float32 scales")
+    _quant("fp8q_group_quant_int8", x, q, s, group_size, masked_m, expected_m, stream, False)
 
 
 def fp8q_silu_mul_group_quant(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, group_size: int = 128,
@@ -187,15 +200,20 @@ def alloc_scales(E: int | None, M: int, ng: int, scale_fmt: str, layout: str, de
 
 def group_quant(x: torch.Tensor, group_size: int = 128, scale_fmt: str = "ue8m0", layout: str = "col",
                 silu: bool = False, masked_m: torch.Tensor | None = None, expected_m: int = 0,
-                stream=None) -> tuple[torch.Tensor, torch.Tensor]:
-    """Allocating form: returns (q uint8 [.., M, K], scales viewed as [.., M, K/G])."""
+                stream=None, int8: bool = False) -> tuple[torch.Tensor, torch.Tensor]:
+    """Allocating form: returns (q uint8 [.., M, K] of e4m3 bytes, or int8 codes with
+    int8=True (fp32 scales), scales viewed as [.., M, K/G]). group_size == K is per-token."""
     W = x.shape[-1]
     K = W // 2 if silu else W
     lead = tuple(x.shape[:-2])
     M = x.shape[-2]
-    q = torch.empty(*lead, M, K, dtype=torch.uint8, device=x.device)
+    q = torch.empty(*lead, M, K, dtype=torch.int8 if int8 else torch.uint8, device=x.device)
     s = alloc_scales(lead[0] if lead else None, M, K // group_size, scale_fmt, layout, x.device)
-    if silu:
+    if int8:
+        if silu:
+            raise ValueError("int8 output has no fused silu variant")
+        fp8q_group_quant_int8(x, q, s, group_size, masked_m, expected_m, stream)
+    elif silu:
         fp8q_silu_mul_group_quant(x, q, s, group_size, masked_m, expected_m, stream)
     else:
         fp8q_group_quant(x, q, s, group_size, masked_m, expected_m, stream)

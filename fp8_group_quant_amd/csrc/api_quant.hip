@@ -12,17 +12,21 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int quant_entry(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K, int64_t x_se,
                 int64_t x_sm, uint8_t* q, int64_t q_se, int64_t q_sm, void* s, int scale_fmt,
                 int64_t s_se, int64_t s_sm, int64_t s_sg, int group_size, const int32_t* masked_m,
-                int64_t expected_m, void* stream, bool silu) {
+                int64_t expected_m, void* stream, bool silu, bool i8) {
   set_error("");
-  const char* fn = silu ? "fp8q_silu_mul_group_quant" : "fp8q_group_quant";
+  const char* fn = i8 ? "fp8q_group_quant_int8" : (silu ? "fp8q_silu_mul_group_quant" : "fp8q_group_quant");
   const std::string pre = std::string(fn) + ": ";
   if (in_dtype != FP8Q_DTYPE_BF16 && in_dtype != FP8Q_DTYPE_F16 && in_dtype != FP8Q_DTYPE_F32)
     return fail(FP8Q_EUNSUPPORTED, pre + "in_dtype must be BF16, F16 or F32");
   if (scale_fmt != FP8Q_SCALE_F32 && scale_fmt != FP8Q_SCALE_UE8M0 && scale_fmt != FP8Q_SCALE_UE8M0_PACKED)
     return fail(FP8Q_EUNSUPPORTED, pre + "scale_fmt must be F32, UE8M0 or UE8M0_PACKED");
-  if (group_size != 32 && group_size != 64 && group_size != 128)
-    return fail(FP8Q_EUNSUPPORTED, pre + "group_size must be 32, 64 or 128");
+  if (i8 && scale_fmt != FP8Q_SCALE_F32) return fail(FP8Q_EUNSUPPORTED, pre + "int8 output takes F32 scales");
   if (E < 0 || M < 0 || K < 0) return fail(FP8Q_EINVAL, pre + "negative size");
+  const bool per_token = group_size > 0 && group_size == K && group_size != 32 && group_size != 64 && group_size != 128;
+  if (group_size != 32 && group_size != 64 && group_size != 128 && !per_token)
+    return fail(FP8Q_EUNSUPPORTED, pre + "group_size must be 32, 64, 128 or K (per-token)");
+  if (per_token && K % 16 != 0) return fail(FP8Q_EINVAL, pre + "per-token quantization needs K % 16 == 0");
+  if (per_token && K > (int64_t(1) << 30)) return fail(FP8Q_EUNSUPPORTED, pre + "per-token rows are limited to 2^30 elements");
   if (x_se < 0 || x_sm < 0 || q_se < 0 || q_sm < 0 || s_se < 0 || s_sm < 0 || s_sg < 0)
     return fail(FP8Q_EINVAL, pre + "negative stride");
   if (expected_m < 0) return fail(FP8Q_EINVAL, pre + "expected_m must be >= 0");
@@ -76,7 +80,7 @@ int quant_entry(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K, in
   p.s_sm = s_sm;
   p.s_sg = s_sg;
   p.packed = packed ? 1 : 0;
-  return launch_group_quant(in_dtype, packed ? FP8Q_SCALE_UE8M0 : scale_fmt, group_size, silu, p, expected_m,
+  return launch_group_quant(in_dtype, packed ? FP8Q_SCALE_UE8M0 : scale_fmt, group_size, silu, i8, p, expected_m,
                             static_cast<hipStream_t>(stream));
 }
 
@@ -90,7 +94,7 @@ int fp8q_group_quant(const void* x, int in_dtype, int64_t E, int64_t M, int64_t 
                      int64_t s_se, int64_t s_sm, int64_t s_sg, int group_size,
                      const int32_t* masked_m, int64_t expected_m, void* stream) {
   return fp8q::quant_entry(x, in_dtype, E, M, K, x_se, x_sm, q, q_se, q_sm, s, scale_fmt, s_se, s_sm,
-                           s_sg, group_size, masked_m, expected_m, stream, false);
+                           s_sg, group_size, masked_m, expected_m, stream, false, false);
 }
 
 int fp8q_silu_mul_group_quant(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K,
@@ -99,7 +103,15 @@ int fp8q_silu_mul_group_quant(const void* x, int in_dtype, int64_t E, int64_t M,
                               int group_size, const int32_t* masked_m, int64_t expected_m,
                               void* stream) {
   return fp8q::quant_entry(x, in_dtype, E, M, K, x_se, x_sm, q, q_se, q_sm, s, scale_fmt, s_se, s_sm,
-                           s_sg, group_size, masked_m, expected_m, stream, true);
+                           s_sg, group_size, masked_m, expected_m, stream, true, false);
+}
+
+int fp8q_group_quant_int8(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K, int64_t x_se,
+                          int64_t x_sm, int8_t* q, int64_t q_se, int64_t q_sm, float* s, int scale_fmt,
+                          int64_t s_se, int64_t s_sm, int64_t s_sg, int group_size,
+                          const int32_t* masked_m, int64_t expected_m, void* stream) {
+  return fp8q::quant_entry(x, in_dtype, E, M, K, x_se, x_sm, reinterpret_cast<uint8_t*>(q), q_se, q_sm, s,
+                           scale_fmt, s_se, s_sm, s_sg, group_size, masked_m, expected_m, stream, false, true);
 }
 
 }  // extern "C"

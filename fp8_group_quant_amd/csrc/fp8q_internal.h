@@ -30,11 +30,12 @@ struct QuantParams {
   int64_t s_se, s_sm, s_sg; // scale strides (scale elements; packed UE8M0: 32-bit words of 4 groups)
   int32_t packed;           // UE8M0 exponents packed 4 per word (group g in byte g % 4 of word g / 4)
   int64_t nseg;             // segments per row
-  int32_t chunks_per_seg;   // 512-element chunks per segment (1..8)
-  int32_t chunks_per_row;   // ceil(K / 512)
+  int32_t chunks_per_seg;   // 1024-element chunks per segment
+  int32_t chunks_per_row;   // ceil(K / 1024)
 };
 
-int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu,
+// group_size 32, 64 or 128, or K (per-token: one group per row); i8 = int8 output
+int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, bool i8,
                        QuantParams p, int64_t expected_m, hipStream_t stream);
 
 // ------------------------------------------------------------------ GEMM launchers

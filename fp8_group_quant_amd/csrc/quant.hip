@@ -8,6 +8,11 @@
 // the two halves of each input row (TeleFuser "tf-kernel 安装与使用", silu_and_mul
 // example; the PR's fuse_silu_and_mul trait).
 //
+// Two variants share that rule. int8 output (the PR's ref_int8 reference) uses 127 in place
+// of 448: s = amax/127 in fp32, multiplier 1/s, clamp to +-127, nearest integer with ties
+// to even. Per-token quantization (TeleFuser's per-token FP8 example, scale [M, 1]) is the
+// rule with one group per row (G = K), run by a whole-row kernel below.
+//
 // Mapping to CDNA4:
 //   - one wavefront (64 lanes) streams a segment of one row; each lane owns 16
 //     consecutive elements (32 bytes of bf16) of every 1024-element chunk: two adjacent
@@ -37,6 +42,7 @@ constexpr int kPerLane = 16;    // consecutive elements owned by one lane per ch
 constexpr int kChunk = 64 * kPerLane;  // elements per wave-wide chunk
 constexpr int kMaxChunks = 1;   // chunks per wave item (one: see launch_group_quant)
 constexpr float kFmax = 448.0f;
+constexpr float kImax = 127.0f;  // int8 output: largest code used
 constexpr float kEps = 0x1.b7cdfep-34f;  // 1e-10f, the amax floor
 
 // ------------------------------------------------------------------ wave helpers
@@ -158,9 +164,10 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // ------------------------------------------------------------------ scale rules
-template <int FMT>
+template <int FMT, bool I8>
 __device__ __forceinline__ float group_multiplier(float amax, uint32_t& scale_bits) {
-  const float r = amax / kFmax;  // correctly rounded
+  static_assert(!I8 || FMT == FP8Q_SCALE_F32, "int8 output takes fp32 scales");
+  const float r = amax / (I8 ? kImax : kFmax);  // correctly rounded
   if constexpr (FMT == FP8Q_SCALE_UE8M0) {
     const uint32_t bits = __float_as_uint(r);
     const uint32_t ex = ((bits >> 23) & 0xFFu) + ((bits & 0x7FFFFFu) != 0u ? 1u : 0u);
@@ -180,49 +187,93 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -kFmax), kFmax); }
 
-// ------------------------------------------------------------------ the kernel
-template <int DT, int G, int FMT, bool SILU>
+// int8: clamp to +-127, round to nearest even (v_rndne_f32), exact conversion, 4 bytes
+// packed little-endian
+__device__ __forceinline__ uint32_t i8_code(float v) {
+  return static_cast<uint32_t>(static_cast<int>(__builtin_rintf(fminf(fmaxf(v, -kImax), kImax)))) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t cvt4_i8(float a, float b, float c, float d) {
+  return i8_code(a) | (i8_code(b) << 8) | (i8_code(c) << 16) | (i8_code(d) << 24);
+}
+
+// 16 values times the multiplier, as 16 output codes (e4m3 after the clamp to +-448, or
+// int8)
+template <bool I8>
+__device__ __forceinline__ u32x4 encode16(const float (&v)[16], float inv) {
+  u32x4 w;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    if constexpr (I8)
+      w[q] = cvt4_i8(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
+    else
+      w[q] = cvt4(clamp448(v[4 * q] * inv), clamp448(v[4 * q + 1] * inv), clamp448(v[4 * q + 2] * inv),
+                  clamp448(v[4 * q + 3] * inv));
+  }
+  return w;
+}
+
+// ------------------------------------------------------------------ row dispatch
+// Masked dispatch: exclusive prefix sum of clamp(masked_m[e], 0, M) over experts into
+// lds_pref[0..E] (lds_pref[E] = total), one block-wide scan over kThreads partials stored
+// after it. Returns the number of valid rows. Every thread of the block must call it.
+__device__ int64_t masked_prefix(const QuantParams& p, int32_t* lds_pref) {
+  const int E = static_cast<int>(p.E);
+  int32_t* part = lds_pref + E + 1;
+  const int tid = threadIdx.x;
+  const int per = (E + kThreads - 1) / kThreads;
+  const int beg = min(tid * per, E), end = min(beg + per, E);
+  int32_t local = 0;
+  for (int i = beg; i < end; i++) {
+    int32_t c = p.masked_m[i];
+    c = c < 0 ? 0 : (c > p.M ? static_cast<int32_t>(p.M) : c);
+    local += c;
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int32_t add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - local;  // exclusive start of this thread's slice
+  for (int i = beg; i < end; i++) {
+    lds_pref[i] = run;
+    int32_t c = p.masked_m[i];
+    c = c < 0 ? 0 : (c > p.M ? static_cast<int32_t>(p.M) : c);
+    run += c;
+  }
+  if (tid == kThreads - 1) lds_pref[E] = part[kThreads - 1];
+  __syncthreads();
+  return lds_pref[E];
+}
+
+// (expert, row) of the row-th processed row: a binary search of the prefix when masked,
+// else row-major over [E][M].
+__device__ __forceinline__ void row_at(const QuantParams& p, const int32_t* lds_pref, bool masked, int64_t row,
+                                       int64_t& e, int64_t& m) {
+  if (masked) {
+    int lo = 0, hi = static_cast<int>(p.E);  // lds_pref[lo] <= row < lds_pref[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (lds_pref[mid] <= row) lo = mid; else hi = mid;
+    }
+    e = lo;
+    m = row - lds_pref[lo];
+  } else {
+    e = row / p.M;
+    m = row - e * p.M;
+  }
+}
+
+// ------------------------------------------------------------------ the group kernel
+template <int DT, int G, int FMT, bool SILU, bool I8>
 __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
   extern __shared__ int32_t lds_pref[];  // masked only: E+1 exclusive prefix + 256 partials
   constexpr int LANES = G / kPerLane;
   const int lane = threadIdx.x & 63;
   const bool masked = p.masked_m != nullptr;
-
-  int64_t total_rows;
-  if (masked) {
-    // prefix sum of clamp(masked_m[e], 0, M) over experts, one block-wide scan
-    const int E = static_cast<int>(p.E);
-    int32_t* part = lds_pref + E + 1;
-    const int tid = threadIdx.x;
-    const int per = (E + kThreads - 1) / kThreads;
-    const int beg = min(tid * per, E), end = min(beg + per, E);
-    int32_t local = 0;
-    for (int i = beg; i < end; i++) {
-      int32_t c = p.masked_m[i];
-      c = c < 0 ? 0 : (c > p.M ? static_cast<int32_t>(p.M) : c);
-      local += c;
-    }
-    part[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int32_t add = tid >= off ? part[tid - off] : 0;
-      __syncthreads();
-      part[tid] += add;
-      __syncthreads();
-    }
-    int32_t run = part[tid] - local;  // exclusive start of this thread's slice
-    for (int i = beg; i < end; i++) {
-      lds_pref[i] = run;
-      int32_t c = p.masked_m[i];
-      c = c < 0 ? 0 : (c > p.M ? static_cast<int32_t>(p.M) : c);
-      run += c;
-    }
-    if (tid == kThreads - 1) lds_pref[E] = part[kThreads - 1];
-    __syncthreads();
-    total_rows = lds_pref[E];
-  } else {
-    total_rows = p.E * p.M;
-  }
+  const int64_t total_rows = masked ? masked_prefix(p, lds_pref) : p.E * p.M;
 
   const int64_t items = total_rows * p.nseg;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
@@ -231,18 +282,7 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
     const int64_t row = t / p.nseg;
     const int seg = static_cast<int>(t - row * p.nseg);
     int64_t e, m;
-    if (masked) {
-      int lo = 0, hi = static_cast<int>(p.E);  // lds_pref[lo] <= row < lds_pref[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (lds_pref[mid] <= row) lo = mid; else hi = mid;
-      }
-      e = lo;
-      m = row - lds_pref[lo];
-    } else {
-      e = row / p.M;
-      m = row - e * p.M;
-    }
+    row_at(p, lds_pref, masked, row, e, m);
     const int64_t xrow = e * p.x_se + m * p.x_sm;
     uint8_t* qrow = p.q + e * p.q_se + m * p.q_sm;
     const int64_t srow = e * p.s_se + m * p.s_sm;
@@ -282,16 +322,11 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
         amax = group_max<LANES>(amax);  // all lanes active here
         amax = fmaxf(amax, kEps);
         uint32_t sbits;
-        const float inv = group_multiplier<FMT>(amax, sbits);
+        const float inv = group_multiplier<FMT, I8>(amax, sbits);
         if (k < p.K) {
-          u32x4 w;
-#pragma unroll
-          for (int q = 0; q < 4; q++)
-            w[q] = cvt4(clamp448(v[4 * q] * inv), clamp448(v[4 * q + 1] * inv), clamp448(v[4 * q + 2] * inv),
-                        clamp448(v[4 * q + 3] * inv));
           // default cache policy: the codes stay in the Infinity Cache for the GEMM that
           // reads them next (quant + GEMM measured ~3% faster than with non-temporal stores)
-          *reinterpret_cast<u32x4*>(qrow + k) = w;
+          *reinterpret_cast<u32x4*>(qrow + k) = encode16<I8>(v, inv);
           if ((lane & (LANES - 1)) == 0) {
             const int64_t g = k / G;
             // packed: group g is byte g % 4 of word g / 4 (little-endian), strides in words
@@ -307,28 +342,146 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
   }
 }
 
-template <int DT, int G, int FMT, bool SILU>
-void launch_one(const QuantParams& p, int grid, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((group_quant_kernel<DT, G, FMT, SILU>), dim3(grid), dim3(kThreads), lds, stream, p);
+// ------------------------------------------------------------------ the per-token kernel
+// Max over all 64 lanes, returned wave-uniform: 8-lane DPP butterfly, row_mirror for 16
+// lanes, then the four 16-lane rows through readlane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<8>(v);
+  v = fmaxf(v, dpp<0x140>(v));  // row_mirror: lane i with lane 15 - i of its row
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-template <int DT, int G, int FMT>
-void launch_silu(bool silu, const QuantParams& p, int grid, size_t lds, hipStream_t s) {
-  if (silu) launch_one<DT, G, FMT, true>(p, grid, lds, s);
-  else launch_one<DT, G, FMT, false>(p, grid, lds, s);
+// One wave per row, the whole row one group. The row is read in batches of kReg chunks
+// (each lane: 16 elements per chunk). A row of at most kReg chunks stays in registers
+// between the amax pass and the quantize pass; a longer row is read twice (the second
+// read is normally served by the L2 / Infinity Cache). K % 16 == 0, so every lane's 16
+// elements are either all inside the row or all outside.
+template <int DT, int FMT, bool SILU, bool I8>
+__global__ __launch_bounds__(kThreads) void token_quant_kernel(QuantParams p) {
+  extern __shared__ int32_t lds_pref[];
+  constexpr int kReg = (DT == FP8Q_DTYPE_F32 ? 4 : 8) / (SILU ? 2 : 1);
+  const int lane = threadIdx.x & 63;
+  const bool masked = p.masked_m != nullptr;
+  const int64_t total_rows = masked ? masked_prefix(p, lds_pref) : p.E * p.M;
+  const int nc = p.chunks_per_row;
+  const bool resident = nc <= kReg;
+
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6); row < total_rows;
+       row += nwaves) {
+    int64_t e, m;
+    row_at(p, lds_pref, masked, row, e, m);
+    const int64_t xrow = e * p.x_se + m * p.x_sm;
+    uint8_t* qrow = p.q + e * p.q_se + m * p.q_sm;
+
+    Raw16<DT> ra[kReg];
+    Raw16<DT> rb[SILU ? kReg : 1];
+    float keep[SILU ? kReg : 1][16];  // silu values of a resident row
+    auto load_batch = [&](int c0) {
+#pragma unroll
+      for (int c = 0; c < kReg; c++) {
+        zero_raw<DT>(ra[c]);
+        if constexpr (SILU) zero_raw<DT>(rb[c]);
+        const int64_t k = static_cast<int64_t>(c0 + c) * kChunk + lane * kPerLane;
+        if (c0 + c < nc && k < p.K) {
+          load_raw<DT>(p.x, xrow + k, ra[c]);
+          if constexpr (SILU) load_raw<DT>(p.x, xrow + p.K + k, rb[c]);
+        }
+      }
+    };
+    auto values = [&](int c, float (&v)[16]) {
+      widen<DT>(ra[c], v);
+      if constexpr (SILU) {
+        float u[16];
+        widen<DT>(rb[c], u);
+#pragma unroll
+        for (int j = 0; j < 16; j++) v[j] = silu_mul(v[j], u[j]);
+      }
+    };
+
+    // pass 1: row amax (lanes past K hold zeros)
+    float amax = 0.0f;
+    for (int c0 = 0; c0 < nc; c0 += kReg) {
+      load_batch(c0);
+#pragma unroll
+      for (int c = 0; c < kReg; c++) {
+        if (c0 + c < nc) {
+          float v[16];
+          values(c, v);
+#pragma unroll
+          for (int j = 0; j < 16; j++) amax = fmaxf(amax, fabsf(v[j]));
+          if constexpr (SILU) {
+#pragma unroll
+            for (int j = 0; j < 16; j++) keep[c][j] = v[j];
+          }
+        }
+      }
+    }
+    amax = fmaxf(wave_max(amax), kEps);
+    uint32_t sbits;
+    const float inv = group_multiplier<FMT, I8>(amax, sbits);
+    if (lane == 0) {
+      const int64_t sidx = e * p.s_se + m * p.s_sm;
+      if constexpr (FMT == FP8Q_SCALE_UE8M0)
+        static_cast<uint8_t*>(p.s)[sidx] = static_cast<uint8_t>(sbits);
+      else
+        static_cast<uint32_t*>(p.s)[sidx] = sbits;
+    }
+
+    // pass 2: quantize (a resident row reuses its registers)
+    for (int c0 = 0; c0 < nc; c0 += kReg) {
+      if (!resident) load_batch(c0);
+#pragma unroll
+      for (int c = 0; c < kReg; c++) {
+        const int64_t k = static_cast<int64_t>(c0 + c) * kChunk + lane * kPerLane;
+        if (c0 + c < nc && k < p.K) {
+          float v[16];
+          if constexpr (SILU) {
+            if (resident) {
+#pragma unroll
+              for (int j = 0; j < 16; j++) v[j] = keep[c][j];
+            } else {
+              values(c, v);
+            }
+          } else {
+            values(c, v);
+          }
+          *reinterpret_cast<u32x4*>(qrow + k) = encode16<I8>(v, inv);
+        }
+      }
+    }
+  }
+}
+
+// Instantiated combinations: e4m3 output with fp32 or UE8M0 scales, with or without silu;
+// int8 output with fp32 scales, without silu. G == 0 selects the per-token kernel.
+template <int DT, int G, int FMT, bool SILU, bool I8>
+void launch_one(const QuantParams& p, int grid, size_t lds, hipStream_t stream) {
+  if constexpr (G == 0)
+    hipLaunchKernelGGL((token_quant_kernel<DT, FMT, SILU, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
+  else
+    hipLaunchKernelGGL((group_quant_kernel<DT, G, FMT, SILU, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
 }
 
 template <int DT, int G>
-void launch_fmt(int fmt, bool silu, const QuantParams& p, int grid, size_t lds, hipStream_t s) {
-  if (fmt == FP8Q_SCALE_UE8M0) launch_silu<DT, G, FP8Q_SCALE_UE8M0>(silu, p, grid, lds, s);
-  else launch_silu<DT, G, FP8Q_SCALE_F32>(silu, p, grid, lds, s);
+void launch_variant(int fmt, bool silu, bool i8, const QuantParams& p, int grid, size_t lds, hipStream_t s) {
+  if (i8) launch_one<DT, G, FP8Q_SCALE_F32, false, true>(p, grid, lds, s);
+  else if (fmt == FP8Q_SCALE_UE8M0 && silu) launch_one<DT, G, FP8Q_SCALE_UE8M0, true, false>(p, grid, lds, s);
+  else if (fmt == FP8Q_SCALE_UE8M0) launch_one<DT, G, FP8Q_SCALE_UE8M0, false, false>(p, grid, lds, s);
+  else if (silu) launch_one<DT, G, FP8Q_SCALE_F32, true, false>(p, grid, lds, s);
+  else launch_one<DT, G, FP8Q_SCALE_F32, false, false>(p, grid, lds, s);
 }
 
 template <int DT>
-void launch_g(int g, int fmt, bool silu, const QuantParams& p, int grid, size_t lds, hipStream_t s) {
-  if (g == 32) launch_fmt<DT, 32>(fmt, silu, p, grid, lds, s);
-  else if (g == 64) launch_fmt<DT, 64>(fmt, silu, p, grid, lds, s);
-  else launch_fmt<DT, 128>(fmt, silu, p, grid, lds, s);
+void launch_g(int g, int fmt, bool silu, bool i8, const QuantParams& p, int grid, size_t lds, hipStream_t s) {
+  if (g == 32) launch_variant<DT, 32>(fmt, silu, i8, p, grid, lds, s);
+  else if (g == 64) launch_variant<DT, 64>(fmt, silu, i8, p, grid, lds, s);
+  else if (g == 128) launch_variant<DT, 128>(fmt, silu, i8, p, grid, lds, s);
+  else launch_variant<DT, 0>(fmt, silu, i8, p, grid, lds, s);
 }
 
 }  // namespace
@@ -336,25 +489,29 @@ void launch_g(int g, int fmt, bool silu, const QuantParams& p, int grid, size_t 
 // Picks the segment length and the grid, then launches. Measured on MI355X: one chunk per
 // wave item and one wave per item (as many waves as the problem has chunks) streams best;
 // the hardware's own wave scheduling keeps HBM busier than longer per-wave segments.
-int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, QuantParams p,
+// group_size 32/64/128 runs the group kernel; any other value is G = K (per-token), run
+// with one wave per row.
+int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, bool i8, QuantParams p,
                        int64_t expected_m, hipStream_t stream) {
+  const bool per_token = group_size != 32 && group_size != 64 && group_size != 128;
   const int chunks = static_cast<int>((p.K + kChunk - 1) / kChunk);
   int64_t rows_est = p.E * p.M;
   if (p.masked_m) rows_est = p.E * (expected_m > 0 ? std::min<int64_t>(expected_m, p.M) : p.M);
   if (rows_est < 1) rows_est = 1;
-  p.chunks_per_seg = 1;
+  p.chunks_per_seg = per_token ? chunks : 1;
   p.chunks_per_row = chunks;
-  p.nseg = chunks;
+  p.nseg = per_token ? 1 : chunks;
   const int64_t items = rows_est * p.nseg;
   int64_t grid = (items + kWavesPerBlock - 1) / kWavesPerBlock;
   // masked launches rebuild the expert prefix sum in every block: cap the grid there so each
   // wave walks several rows instead
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, p.masked_m ? 2048 : 65535));
   const size_t lds = p.masked_m ? static_cast<size_t>(p.E + 1 + kThreads) * sizeof(int32_t) : 0;
+  const int g = per_token ? 0 : group_size;
   switch (in_dtype) {
-    case FP8Q_DTYPE_BF16: launch_g<FP8Q_DTYPE_BF16>(group_size, scale_fmt, silu, p, (int)grid, lds, stream); break;
-    case FP8Q_DTYPE_F16: launch_g<FP8Q_DTYPE_F16>(group_size, scale_fmt, silu, p, (int)grid, lds, stream); break;
-    default: launch_g<FP8Q_DTYPE_F32>(group_size, scale_fmt, silu, p, (int)grid, lds, stream); break;
+    case FP8Q_DTYPE_BF16: launch_g<FP8Q_DTYPE_BF16>(g, scale_fmt, silu, i8, p, (int)grid, lds, stream); break;
+    case FP8Q_DTYPE_F16: launch_g<FP8Q_DTYPE_F16>(g, scale_fmt, silu, i8, p, (int)grid, lds, stream); break;
+    default: launch_g<FP8Q_DTYPE_F32>(g, scale_fmt, silu, i8, p, (int)grid, lds, stream); break;
   }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(FP8Q_ELAUNCH, std::string("group quant launch: ") + hipGetErrorString(err));

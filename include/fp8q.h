@@ -97,8 +97,12 @@ extern "C" {
  *     expected_m >= 0 is a host-side hint of the typical rows per expert used to size
  *     the launch; it never changes the result (0 = no hint).
  *
+ * Per-token quantization [TF per-token FP8 example: scale [M, 1]]: group_size == K
+ * makes the whole row one group (one scale per row, at s + e*s_se + m*s_sm; s_sg is
+ * not used). It requires K % 16 == 0 and K <= 2^30.
+ *
  * Requirements (else the status in brackets):
- *   in_dtype in {BF16, F16, F32} and group_size in {32, 64, 128}       [EUNSUPPORTED]
+ *   in_dtype in {BF16, F16, F32}; group_size in {32, 64, 128} or == K   [EUNSUPPORTED]
  *   K % group_size == 0, E, M, K >= 0, strides non-negative             [EINVAL]
  *   x and q 16-byte aligned; x_sm, x_se (in bytes) and q_sm, q_se
  *   multiples of 16 bytes; F32 scales and packed words 4-byte aligned   [EALIGN]
@@ -134,6 +138,26 @@ int fp8q_silu_mul_group_quant(const void* x, int in_dtype, int64_t E, int64_t M,
                               void* s, int scale_fmt, int64_t s_se, int64_t s_sm, int64_t s_sg,
                               int group_size, const int32_t* masked_m, int64_t expected_m,
                               void* stream);
+
+/*
+ * fp8q_group_quant_int8 — per-token-group quantization to int8
+ * [PR30924 关键文件 (the ref_int8 reference; out_dtype int8 among the trait axes),
+ *  风险与影响 (int8 codes move by one under approximate division, so the division here is
+ *  IEEE)]
+ *
+ * Same arguments, layouts, dispatch and requirements as fp8q_group_quant (group_size
+ * 32, 64, 128 or K), with int8 codes in q and fp32 scales only. For every group:
+ *   amax = max(max |x_i|, 1e-10f)                                  (fp32)
+ *   s = amax / 127 (IEEE fp32 division), stored as float; inv = 1 / s (IEEE fp32 division)
+ *   q_i = round_to_nearest_even( clamp(x_i * inv, -127, 127) ), a two's-complement byte
+ * scale_fmt other than FP8Q_SCALE_F32 is FP8Q_EUNSUPPORTED. No fused silu variant.
+ */
+int fp8q_group_quant_int8(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K,
+                          int64_t x_se, int64_t x_sm,
+                          int8_t* q, int64_t q_se, int64_t q_sm,
+                          float* s, int scale_fmt, int64_t s_se, int64_t s_sm, int64_t s_sg,
+                          int group_size, const int32_t* masked_m, int64_t expected_m,
+                          void* stream);
 
 /*
  * fp8q_gemm_blockscaled — Y = dequant(A) * dequant(B)^T, bf16 output  [FI sections 6-7]

@@ -28,8 +28,9 @@ def _lib():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ("fp8q_group_quant", "fp8q_silu_mul_group_quant", "fp8q_gemm_blockscaled",
-              "fp8q_grouped_gemm_masked", "fp8q_status_string", "fp8q_last_error", "fp8q_device_check"):
+    for n in ("fp8q_group_quant", "fp8q_silu_mul_group_quant", "fp8q_group_quant_int8", "fp8q_gemm_blockscaled",
+              "fp8q_grouped_gemm_masked", "fp8q_grouped_gemm_segments", "fp8q_grouped_gemm_contiguous",
+              "fp8q_status_string", "fp8q_last_error", "fp8q_device_check"):
         assert n in names
 
 
@@ -69,6 +70,33 @@ def test_device_check_refuses_without_gpu():
     lib = _lib()
     lib.fp8q_device_check.argtypes = [ctypes.c_int]
     assert lib.fp8q_device_check(0) == 4  # FP8Q_EDEVICE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks host validation on a machine without a GPU")
+@pytest.mark.parametrize("entry,K,G,fmt,status", [
+    ("fp8q_group_quant_int8", 512, 128, 1, 2),   # int8 with UE8M0 scales: EUNSUPPORTED
+    ("fp8q_group_quant_int8", 512, 128, 2, 2),   # int8 with packed UE8M0: EUNSUPPORTED
+    ("fp8q_group_quant", 512, 256, 0, 2),        # G not in {32, 64, 128} and != K: EUNSUPPORTED
+    ("fp8q_group_quant", 1032, 1032, 0, 1),      # per-token with K % 16 != 0: EINVAL
+    ("fp8q_group_quant", 1024, 1024, 2, 1),      # per-token, packed: 1 group per row: EINVAL
+    ("fp8q_group_quant", 1024, 1024, 0, 4),      # valid per-token: passes validation, EDEVICE here
+    ("fp8q_group_quant_int8", 1024, 1024, 0, 4), # valid int8 per-token: EDEVICE here
+    ("fp8q_group_quant_int8", 512, 64, 0, 4),    # valid int8 groups: EDEVICE here
+])
+def test_quant_variant_validation_before_any_device_call(entry, K, G, fmt, status):
+    # Host validation returns before the library touches a pointer or the device; the
+    # addresses below are never dereferenced.
+    lib = _lib()
+    fn = getattr(lib, entry)
+    I64, P = ctypes.c_int64, ctypes.c_void_p
+    fn.argtypes = [P, ctypes.c_int, I64, I64, I64, I64, I64, P, I64, I64, P, ctypes.c_int, I64, I64, I64,
+                   ctypes.c_int, P, I64, P]
+    fn.restype = ctypes.c_int
+    M = 8
+    ng = max(K // G, 1)
+    s_sm = 1 if fmt == 2 else ng
+    rc = fn(0x10000, 0, 1, M, K, M * K, K, 0x20000, M * K, K, 0x30000, fmt, M * ng, s_sm, 1, G, None, 0, None)
+    assert rc == status, lib.fp8q_last_error()
 
 
 def test_binding_reads_scale_layout_from_strides():

@@ -32,9 +32,11 @@ def _to_dev(x: np.ndarray, in_dtype: int) -> torch.Tensor:
     return t
 
 
-def _gpu_quant(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, expected_m=0, stream=None):
+def _gpu_quant(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, expected_m=0, stream=None,
+               int8=False):
     """Runs the GPU quant on x ([M, W] or [E, M, W]); returns (q, scale storage) as numpy in
-    the oracle's storage layout ([.., M, ng] row-major or [.., ng, M] column-major)."""
+    the oracle's storage layout ([.., M, ng] row-major or [.., ng, M] column-major). q is
+    returned as bytes (int8 codes as their two's-complement bytes)."""
     f = fq()
     x = _to_dev(x_np, in_dtype)
     x3 = x if x.dim() == 3 else x[None]
@@ -42,14 +44,15 @@ def _gpu_quant(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, expect
     K = W // 2 if silu else W
     ng = K // G
     q = torch.full((E, M, K), FILL, dtype=torch.uint8, device="cuda")
+    qt = q.view(torch.int8) if int8 else q
     width = 4 if fmt == oracle.SCALE_F32 else 1
     shape = (E, M, ng * width) if layout == "row" else (E, ng, M * width)
     s_store = torch.full(shape, FILL, dtype=torch.uint8, device="cuda")
     s_typed = s_store.view(torch.float32) if fmt == oracle.SCALE_F32 else s_store
     s_view = s_typed if layout == "row" else s_typed.transpose(1, 2)
     mm = None if masked_m is None else torch.from_numpy(np.asarray(masked_m, dtype=np.int32)).cuda()
-    fn = f.fp8q_silu_mul_group_quant if silu else f.fp8q_group_quant
-    xin, qin, sin = (x3, q, s_view) if x.dim() == 3 else (x3[0], q[0], s_view[0])
+    fn = f.fp8q_group_quant_int8 if int8 else (f.fp8q_silu_mul_group_quant if silu else f.fp8q_group_quant)
+    xin, qin, sin = (x3, qt, s_view) if x.dim() == 3 else (x3[0], qt[0], s_view[0])
     fn(xin, qin, sin, G, masked_m=mm, expected_m=expected_m, stream=stream)
     torch.cuda.synchronize()
     qn = q.cpu().numpy()
@@ -59,9 +62,10 @@ def _gpu_quant(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, expect
     return qn, sn
 
 
-def _oracle(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, rows=None):
-    return oracle.group_quant(x_np, G, fmt, layout, in_dtype=in_dtype, silu=silu, masked_m=masked_m,
-                              rows=rows, fill=FILL)
+def _oracle(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, rows=None, int8=False):
+    q, sc = oracle.group_quant(x_np, G, fmt, layout, in_dtype=in_dtype, silu=silu, masked_m=masked_m,
+                               rows=rows, fill=FILL, out_int8=int8)
+    return q.view(np.uint8), sc
 
 
 def _assert_same(a, b, what):
@@ -71,9 +75,9 @@ def _assert_same(a, b, what):
         raise AssertionError(f"{what}: {len(bad)} mismatching entries, first at {i}: gpu={a[i]!r} oracle={b[i]!r}")
 
 
-def _full_case(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, expected_m=0):
-    qg, sg = _gpu_quant(x_np, in_dtype, G, fmt, layout, silu, masked_m, expected_m)
-    qo, so = _oracle(x_np, in_dtype, G, fmt, layout, silu, masked_m)
+def _full_case(x_np, in_dtype, G, fmt, layout, silu=False, masked_m=None, expected_m=0, int8=False):
+    qg, sg = _gpu_quant(x_np, in_dtype, G, fmt, layout, silu, masked_m, expected_m, int8=int8)
+    qo, so = _oracle(x_np, in_dtype, G, fmt, layout, silu, masked_m, int8=int8)
     _assert_same(qg, qo, "q")
     _assert_same(sg.view(np.uint8), so.view(np.uint8), "scales")
 
@@ -351,6 +355,128 @@ def test_device_check():
     f = fq()
     assert f.fp8q_device_check(0) == f.OK
     assert f.fp8q_device_check(1000) == f.EDEVICE
+
+
+# ----------------------------------------------------------------- int8 output
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_int8_group_sizes_and_layouts(G, layout):
+    x = synth.activations_bf16(41, 37, 1536, outlier_p=0.02)
+    _full_case(x, oracle.BF16, G, oracle.SCALE_F32, layout, int8=True)
+
+
+@pytest.mark.parametrize("in_dtype", [oracle.F16, oracle.F32])
+def test_int8_input_dtypes(in_dtype):
+    xb = synth.activations_bf16(42, 29, 1024, outlier_p=0.01)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    x = xf.astype(np.float16).view(np.uint16) if in_dtype == oracle.F16 else xf
+    _full_case(x, in_dtype, 128, oracle.SCALE_F32, "row", int8=True)
+
+
+def test_int8_ties_and_edges_through_unit_scale():
+    # each row starts with 127, so s = 1 and the multiplier is exactly 1: every half-integer
+    # tie, its neighbours, and values past +-127 reach the rounding unchanged
+    halves = np.arange(-254, 255, dtype=np.float64) / 2.0
+    v = np.concatenate([halves, np.nextafter(halves, 1e9), np.nextafter(halves, -1e9)]).astype(np.float32)
+    v = np.clip(v, -127, 127)
+    per = 127
+    n = -(-v.size // per)
+    body = np.zeros(n * per, dtype=np.float32)
+    body[:v.size] = v
+    x = np.concatenate([np.full((n, 1), 127.0, dtype=np.float32), body.reshape(n, per)], axis=1)
+    qg, sg = _gpu_quant(x, oracle.F32, 128, oracle.SCALE_F32, "row", int8=True)
+    assert np.all(sg == 1.0)
+    _assert_same(qg.view(np.int8), np.rint(x).astype(np.int8), "q vs numpy rint")
+
+
+def test_int8_masked_and_per_token():
+    E, M, K = 5, 24, 1024
+    x = _masked_input(E, M, K, 43)
+    mm = np.array([24, 0, 5, 23, 1], dtype=np.int32)
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_F32, "col", masked_m=mm, int8=True)
+    _full_case(x, oracle.BF16, K, oracle.SCALE_F32, "row", masked_m=mm, int8=True)
+    _full_case(synth.activations_bf16(44, 33, 9216), oracle.BF16, 9216, oracle.SCALE_F32, "col", int8=True)
+
+
+def test_int8_rejects_ue8m0_scales():
+    f = fq()
+    x = torch.ones((4, 256), dtype=torch.bfloat16, device="cuda")
+    q = torch.full((4, 256), FILL, dtype=torch.uint8, device="cuda").view(torch.int8)
+    s = torch.full((4, 2), FILL, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        f.fp8q_group_quant_int8(x, q, s, 128)
+    torch.cuda.synchronize()
+    assert torch.all(q.view(torch.uint8) == FILL)
+
+
+# ----------------------------------------------------------------- per-token (G = K)
+# K: one partial chunk, the per-token example's 1024, a ragged tail, the largest row held
+# in registers (8 chunks of bf16), rows read twice (9 and 20 chunks, the last ragged)
+@pytest.mark.parametrize("K", [48, 256, 1024, 1040, 7168, 8192, 9216, 20000])
+@pytest.mark.parametrize("fmt", [oracle.SCALE_F32, oracle.SCALE_UE8M0])
+def test_per_token_widths(K, fmt):
+    x = synth.activations_bf16(45, 19, K, outlier_p=0.005)
+    _full_case(x, oracle.BF16, K, fmt, "row" if fmt == oracle.SCALE_F32 else "col")
+
+
+def test_per_token_fp16_example_shape():
+    # the per-token FP8 example's shape: fp16 [128, 1024], fp32 scales [128, 1]
+    xb = synth.activations_bf16(46, 128, 1024)
+    x = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float16).view(np.uint16)
+    _full_case(x, oracle.F16, 1024, oracle.SCALE_F32, "row")
+
+
+@pytest.mark.parametrize("K", [2048, 4096, 5120])
+def test_per_token_fp32_input(K):
+    # fp32 rows: 4 chunks stay in registers, 5 are read twice
+    xb = synth.activations_bf16(47, 11, K, outlier_p=0.01)
+    x = (xb.astype(np.uint32) << 16).view(np.float32)
+    _full_case(x, oracle.F32, K, oracle.SCALE_F32, "row")
+
+
+@pytest.mark.parametrize("K", [2048, 4096, 6144])
+def test_per_token_silu(K):
+    # silu rows: 4 chunks of silu values stay in registers; 6 are recomputed on the second read
+    x = synth.activations_bf16(48, 13, 2 * K)
+    _full_case(x, oracle.BF16, K, oracle.SCALE_F32, "row", silu=True)
+    _full_case(x, oracle.BF16, K, oracle.SCALE_UE8M0, "col", silu=True)
+
+
+def test_per_token_masked():
+    E, M, K = 6, 40, 3072
+    x = _masked_input(E, M, K, 49)
+    mm = np.array([0, 1, 40, 39, 17, 3], dtype=np.int32)
+    _full_case(x, oracle.BF16, K, oracle.SCALE_UE8M0, "col", masked_m=mm)
+    _full_case(x, oracle.BF16, K, oracle.SCALE_F32, "row", masked_m=mm, expected_m=5)
+
+
+def test_per_token_dense_m4096_sampled():
+    M, K = 4096, 7168
+    x = synth.activations_bf16(50, M, K, outlier_p=0.001)
+    qg, sg = _gpu_quant(x, oracle.BF16, K, oracle.SCALE_F32, "col")
+    g = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([[0, 1, M - 1], g.integers(0, M, size=45)]))
+    qo, so = _oracle(x, oracle.BF16, K, oracle.SCALE_F32, "col", rows=(np.zeros_like(rows), rows))
+    for m in rows:
+        _assert_same(qg[m], qo[m], f"q row {m}")
+        _assert_same(sg[:, m].view(np.uint8), so[:, m].view(np.uint8), f"s row {m}")
+    # everywhere: no NaN code, each row's largest code is 448 (0x7E), the scale is amax/448
+    assert not np.any((qg & 0x7F) == 0x7F)
+    assert np.all((qg & 0x7F).max(-1) == 0x7E)
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(sg[0], np.abs(xf).max(-1) / np.float32(448))
+
+
+def test_per_token_needs_k_multiple_of_16():
+    f = fq()
+    x = torch.ones((4, 1032), dtype=torch.bfloat16, device="cuda")
+    q = torch.full((4, 1040), FILL, dtype=torch.uint8, device="cuda")[:, :1032]
+    s = torch.zeros((4, 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(f.Fp8qError) as ei:
+        f.fp8q_group_quant(x, q, s, 1032)
+    assert ei.value.status == f.EINVAL
+    torch.cuda.synchronize()
+    assert torch.all(q == FILL)
 
 
 # ----------------------------------------------------------------- packed UE8M0 scales
