@@ -401,7 +401,20 @@ def suite(steps: int, warmup: int) -> list:
     ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
                                                 sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32), ns)
     report(w.name, "gemm_mx32", ms, flops=2.0 * w.M * w.N * w.K,
-           nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2)
+           nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
+           extra={"scales": "E8M0 bytes, row-major [rows, K/32]"})
+    # the same operands with both scale tensors as column-major packed words [K/128, rows]
+    # (four E8M0 bytes of one 128-wide K step per 32-bit word)
+    def col_words(e):
+        wd = e.view(np.uint32) if e.flags.c_contiguous else np.ascontiguousarray(e).view(np.uint32)
+        return torch.from_numpy(np.ascontiguousarray(wd.T).view(np.int32)).to(dev).t()
+    for st in sets:
+        st["ea"], st["eb"] = col_words(ea), col_words(eb)
+    ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
+                                                sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32), ns)
+    report(w.name, "gemm_mx32", ms, flops=2.0 * w.M * w.N * w.K,
+           nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
+           extra={"scales": "E8M0 packed words, column-major [K/128, rows]"})
     return lines
 
 

@@ -228,8 +228,11 @@ def _u8(t: torch.Tensor) -> torch.Tensor:
 def fp8q_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
                           y: torch.Tensor, mode: int = GEMM_BLOCK128, stream=None) -> None:
     """Y[M, N] (bf16) = dequant(a [M, K]) @ dequant(b [N, K])^T.
-    BLOCK128: sa viewed as [M, K/128], sb as [ceil(N/128), K/128] (float32 or uint8 UE8M0).
-    MX32: sa [M, K/32], sb [N, K/32], uint8 E8M0."""
+    BLOCK128: sa viewed as [M, K/128], sb as [ceil(N/128), K/128] (float32 or uint8 UE8M0;
+    sa may be int32 packed UE8M0 words [M, K/512]).
+    MX32: sa [M, K/32], sb [N, K/32], uint8 E8M0; or either as int32 packed words [rows, K/128]
+    (the four E8M0 bytes of one 128-wide K step per word; a [K/128, rows] storage viewed
+    transposed gives the column-major words that load fastest)."""
     a8, b8 = _u8(a), _u8(b)
     M, K = a8.shape
     N = b8.shape[0]

@@ -19,14 +19,17 @@ int check_operands(const std::string& pre, const uint8_t* a, int64_t lda, const 
   if (mode != FP8Q_GEMM_BLOCK128 && mode != FP8Q_GEMM_MX32)
     return fail(FP8Q_EUNSUPPORTED, pre + "mode must be BLOCK128 or MX32");
   const bool packed = sa_fmt == FP8Q_SCALE_UE8M0_PACKED;
-  if (!(valid_fmt(sa_fmt) || (packed && mode == FP8Q_GEMM_BLOCK128)) || !valid_fmt(sb_fmt))
+  const bool b_packed = sb_fmt == FP8Q_SCALE_UE8M0_PACKED;
+  if (mode == FP8Q_GEMM_MX32) {
+    const bool e8 = (sa_fmt == FP8Q_SCALE_UE8M0 || packed) && (sb_fmt == FP8Q_SCALE_UE8M0 || b_packed);
+    if (!e8) return fail(FP8Q_EUNSUPPORTED, pre + "MX32 scales must be E8M0 bytes (UE8M0 or UE8M0_PACKED)");
+  } else if (!(valid_fmt(sa_fmt) || packed) || !valid_fmt(sb_fmt)) {
     return fail(FP8Q_EUNSUPPORTED, pre + "scale formats must be F32 or UE8M0 (activation scales also "
-                                         "UE8M0_PACKED in BLOCK128 mode)");
-  if (mode == FP8Q_GEMM_MX32 && (sa_fmt != FP8Q_SCALE_UE8M0 || sb_fmt != FP8Q_SCALE_UE8M0))
-    return fail(FP8Q_EUNSUPPORTED, pre + "MX32 scales must be E8M0 bytes (FP8Q_SCALE_UE8M0)");
+                                         "UE8M0_PACKED)");
+  }
   if (rows < 0 || N < 0 || K < 0) return fail(FP8Q_EINVAL, pre + "negative size");
   if (K % 128 != 0) return fail(FP8Q_EINVAL, pre + "K must be a multiple of 128");
-  if (packed && K % 512 != 0)
+  if (packed && mode == FP8Q_GEMM_BLOCK128 && K % 512 != 0)
     return fail(FP8Q_EINVAL, pre + "packed UE8M0 activation scales need K a multiple of 512");
   if (lda < 0 || ldb < 0 || ldy < 0 || sa_sm < 0 || sa_sk < 0 || sb_sn < 0 || sb_sk < 0)
     return fail(FP8Q_EINVAL, pre + "negative stride");
@@ -37,7 +40,7 @@ int check_operands(const std::string& pre, const uint8_t* a, int64_t lda, const 
   if (!aligned(a, 16) || !aligned(b, 16) || lda % 16 != 0 || ldb % 16 != 0)
     return fail(FP8Q_EALIGN, pre + "a, b and their row strides must be 16-byte aligned");
   if (!aligned(y, 4) || ldy % 2 != 0) return fail(FP8Q_EALIGN, pre + "y must be 4-byte aligned with an even ldy");
-  if ((sa_fmt != FP8Q_SCALE_UE8M0 && !aligned(sa, 4)) || (sb_fmt == FP8Q_SCALE_F32 && !aligned(sb, 4)))
+  if ((sa_fmt != FP8Q_SCALE_UE8M0 && !aligned(sa, 4)) || (sb_fmt != FP8Q_SCALE_UE8M0 && !aligned(sb, 4)))
     return fail(FP8Q_EALIGN, pre + "fp32 scales and packed UE8M0 words must be 4-byte aligned");
   return FP8Q_OK;
 }
@@ -129,7 +132,8 @@ int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda, const void* sa, int sa_
   p.sb_sk = sb_sk;
   p.sa_packed = sa_fmt == FP8Q_SCALE_UE8M0_PACKED ? 1 : 0;
   p.sa_fmt = p.sa_packed ? FP8Q_SCALE_UE8M0 : sa_fmt;
-  p.sb_fmt = sb_fmt;
+  p.sb_packed = sb_fmt == FP8Q_SCALE_UE8M0_PACKED ? 1 : 0;
+  p.sb_fmt = p.sb_packed ? FP8Q_SCALE_UE8M0 : sb_fmt;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return mode == FP8Q_GEMM_MX32 ? launch_gemm_mx32(p, s) : launch_gemm_block128(p, 0, s);
 }

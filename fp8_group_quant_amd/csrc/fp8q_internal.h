@@ -58,6 +58,7 @@ struct GemmParams {
   int64_t sb_sn, sb_sk, sb_se;
   int sa_fmt, sb_fmt;
   int sa_packed;  // UE8M0 activation scales packed 4 K blocks per 32-bit word (sa strides in words)
+  int sb_packed;  // MX32 only: E8M0 weight scales packed likewise (sb strides in words)
 };
 
 int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t stream);

@@ -220,15 +220,22 @@ struct ScaleStage {
     if constexpr (MX) {
       const uint8_t* s8;
       int64_t off, sk;
+      bool packed;
       if (tid < C::BM) {
         s8 = static_cast<const uint8_t*>(SA);
         off = min(m0 + tid, rmax) * p.sa_sm;
         sk = p.sa_sk;
+        packed = p.sa_packed;
       } else if (tid < C::BM + C::BN) {
         s8 = static_cast<const uint8_t*>(SB);
         off = min(n0 + (tid - C::BM), p.N - 1) * p.sb_sn;
         sk = p.sb_sk;
+        packed = p.sb_packed;
       } else {
+        return;
+      }
+      if (packed) {  // word (row, kb): the E8M0 bytes of K blocks 4kb..4kb+3, strides in words
+        v = reinterpret_cast<const uint32_t*>(s8)[off + static_cast<int64_t>(kb) * sk];
         return;
       }
       const int64_t k0 = static_cast<int64_t>(4 * kb) * sk;
@@ -969,19 +976,24 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_lds[q] = 0;
       }
     } else {
-      if (js < 4) {  // E8M0 word (K blocks 4kb..4kb+3) of A row 64 js + lane
+      // E8M0 word (K blocks 4kb..4kb+3) of a row: bytes 4kb.. of a row-major byte row, or
+      // word (row, kb) of packed scales (strides in words; with column-major words the 64
+      // lanes of a job read 256 contiguous bytes instead of 64 rows' worth of lines)
+      const int64_t a_row = p.sa_packed ? p.sa_sm * 4 : p.sa_sm, a_step = p.sa_packed ? p.sa_sk * 4 : 4;
+      const int64_t b_row = p.sb_packed ? p.sb_sn * 4 : p.sb_sn, b_step = p.sb_packed ? p.sb_sk * 4 : 4;
+      if (js < 4) {  // A row 64 js + lane
         const uint8_t* SA = static_cast<const uint8_t*>(p.sa);
         const int row = js * 64 + lane;
-        r.s_base[q] = SA + m0 * p.sa_sm;
-        r.s_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * p.sa_sm);
-        r.s_step[q] = 4;
+        r.s_base[q] = SA + m0 * a_row;
+        r.s_off[q] = static_cast<uint32_t>((min(m0 + row, rmax) - m0) * a_row);
+        r.s_step[q] = a_step;
         r.s_lds[q] = js * 256;
-      } else if (js < 4 + C::BN / 64) {  // and of B row 64 (js-4) + lane
+      } else if (js < 4 + C::BN / 64) {  // B row 64 (js-4) + lane
         const uint8_t* SB = static_cast<const uint8_t*>(p.sb);
         const int row = (js - 4) * 64 + lane;
-        r.s_base[q] = SB + n0 * p.sb_sn;
-        r.s_off[q] = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.sb_sn);
-        r.s_step[q] = 4;
+        r.s_base[q] = SB + n0 * b_row;
+        r.s_off[q] = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * b_row);
+        r.s_step[q] = b_step;
         r.s_lds[q] = 1024 + (js - 4) * 256;
       }
     }
@@ -1472,10 +1484,16 @@ int dma_mode(const GemmParams& p, bool mx) {
   if (p.lda >= (int64_t(1) << 24) || p.ldb >= (int64_t(1) << 24)) return -1;
   const bool k512 = p.K % 512 == 0;
   if (mx) {
-    if (p.sa_sk != 1 || p.sb_sk != 1 || p.sa_sm >= (int64_t(1) << 24) || p.sb_sn >= (int64_t(1) << 24)) return -1;
-    if (k512 && p.sa_sm % 16 == 0 && p.sb_sn % 16 == 0 && a16(p.sa) && a16(p.sb)) return kScMxGrp;
-    const bool ok = p.sa_sm % 4 == 0 && p.sb_sn % 4 == 0 && u32_ok(p.sa) && u32_ok(p.sb);
-    return ok ? kScMx : -1;
+    // per operand: a row-major byte layout (4-byte words per step) or packed words with
+    // any word strides; the 32-bit lane offsets of a 256-row tile must fit
+    auto operand_ok = [&](bool packed, int64_t sm, int64_t sk, const void* s) {
+      if (packed) return sm < (int64_t(1) << 22);
+      return sk == 1 && sm < (int64_t(1) << 24) && sm % 4 == 0 && u32_ok(s);
+    };
+    if (!operand_ok(p.sa_packed, p.sa_sm, p.sa_sk, p.sa) || !operand_ok(p.sb_packed, p.sb_sn, p.sb_sk, p.sb)) return -1;
+    if (!p.sa_packed && !p.sb_packed && k512 && p.sa_sm % 16 == 0 && p.sb_sn % 16 == 0 && a16(p.sa) && a16(p.sb))
+      return kScMxGrp;
+    return kScMx;
   }
   const int64_t E = (p.masked_m || p.seg_indptr) ? p.E : 1;  // groups in the device tile list
   if (p.sb_fmt != FP8Q_SCALE_F32) return -1;

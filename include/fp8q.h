@@ -172,8 +172,15 @@ int fp8q_group_quant_int8(const void* x, int in_dtype, int64_t E, int64_t M, int
  *     sb: one scale per (nb, kb), nb = n/128, at sb + nb*sb_sn + kb*sb_sk; sb_fmt F32 or UE8M0.
  *     Y[m][n] = bf16_rne( sum_kb sa(m,kb) * sb(n/128,kb) * sum_{k in kb} dec(A[m][k]) * dec(B[n][k]) )
  *   mode FP8Q_GEMM_MX32:
- *     sa: one E8M0 byte per (m, k/32) at sa + m*sa_sm + (k/32)*sa_sk; sb likewise per (n, k/32).
- *     sa_fmt and sb_fmt must be FP8Q_SCALE_UE8M0.
+ *     sa: one E8M0 byte per (m, k/32) at sa + m*sa_sm + (k/32)*sa_sk; sb likewise per (n, k/32)
+ *     (sa_fmt, sb_fmt = FP8Q_SCALE_UE8M0: the 2D non-swizzled layout of [FI] section 6).
+ *     Either operand may instead use FP8Q_SCALE_UE8M0_PACKED: the four bytes of K blocks
+ *     4j..4j+3 (one 128-wide K step) of a row in one 32-bit word, byte k/32 % 4 of the word
+ *     at s + 4*(row*s_sm + (k/128)*s_sk) bytes (strides in words, s 4-byte aligned [EALIGN]).
+ *     Column-major words (s_sm == 1, s_sk >= rows) are the layout this library reads
+ *     fastest: one K step's scales of consecutive rows are contiguous. The activation
+ *     layout is what fp8q_group_quant writes for group_size 32 with UE8M0_PACKED scales
+ *     in column-major words.
  *     Y[m][n] = bf16_rne( sum_k 2^(sa-127) dec(A[m][k]) * 2^(sb-127) dec(B[n][k]) )
  * Accumulation is fp32; the result is rounded to bf16 once, at the end.
  *

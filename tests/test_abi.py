@@ -99,6 +99,29 @@ def test_quant_variant_validation_before_any_device_call(entry, K, G, fmt, statu
     assert rc == status, lib.fp8q_last_error()
 
 
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks host validation on a machine without a GPU")
+@pytest.mark.parametrize("mode,sa_fmt,sb_fmt,sa_ptr,status", [
+    (1, 2, 2, 0x30000, 4),   # MX32, both packed words: passes validation, EDEVICE here
+    (1, 2, 1, 0x30000, 4),   # MX32, packed activation words and E8M0 weight bytes
+    (1, 2, 2, 0x30002, 3),   # packed words not 4-byte aligned: EALIGN
+    (1, 0, 1, 0x30000, 2),   # MX32 with fp32 scales: EUNSUPPORTED
+    (0, 0, 2, 0x30000, 2),   # BLOCK128 with packed weight scales: EUNSUPPORTED
+    (0, 2, 0, 0x30000, 4),   # BLOCK128 with packed activation words (K % 512 == 0)
+])
+def test_gemm_scale_format_validation_before_any_device_call(mode, sa_fmt, sb_fmt, sa_ptr, status):
+    # Host validation returns before the library touches a pointer or the device; the
+    # addresses below are never dereferenced.
+    lib = _lib()
+    I64, P = ctypes.c_int64, ctypes.c_void_p
+    fn = lib.fp8q_gemm_blockscaled
+    fn.argtypes = [P, I64, P, ctypes.c_int, I64, I64, P, I64, P, ctypes.c_int, I64, I64, P, I64, I64, I64, I64,
+                   ctypes.c_int, P]
+    fn.restype = ctypes.c_int
+    M, N, K = 256, 256, 1024
+    rc = fn(0x10000, K, sa_ptr, sa_fmt, 1, M, 0x20000, K, 0x40000, sb_fmt, 1, N, 0x50000, N, M, N, K, mode, None)
+    assert rc == status
+
+
 def test_binding_reads_scale_layout_from_strides():
     import fp8_group_quant_amd as fq
     row = fq.alloc_scales(None, 6, 4, "f32", "row", "cpu")

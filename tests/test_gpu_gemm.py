@@ -323,6 +323,95 @@ def test_mx_workload_sampled():
     assert not np.any(y == SENT)
 
 
+# ------------------------------------------------------------ MX32 with packed E8M0 words
+def _mx_scales_dev(e, layout):
+    """E8M0 bytes [rows, K/32] on the device as: "bytes" (row-major), "bytes_t" (stored
+    [K/32, rows], K stride != 1), or packed int32 words [rows, K/128] stored row-major
+    ("row") or column-major ("col")."""
+    if layout == "bytes":
+        return _dev(e)
+    if layout == "bytes_t":
+        return _dev(np.ascontiguousarray(e.T)).t()
+    return _packed_words(e, layout)
+
+
+def _gpu_mx_layouts(a, ea, b, eb, la, lb):
+    f = fq()
+    M, K = a.shape
+    N = b.shape[0]
+    y = torch.full((M, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_gemm_blockscaled(_dev(a), _mx_scales_dev(ea, la), _dev(b), _mx_scales_dev(eb, lb),
+                            y.view(torch.bfloat16), f.GEMM_MX32)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16)
+
+
+# Packed words on the direct-to-LDS kernel (256x128 tiles), one operand packed and the other
+# row-major bytes, and on the register-staged kernel (the other operand's bytes have a K
+# stride != 1).
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (130, 96, 256), (300, 260, 1024)])
+@pytest.mark.parametrize("la,lb", [("col", "col"), ("row", "row"), ("col", "bytes"), ("bytes", "col"),
+                                   ("col", "bytes_t"), ("bytes_t", "row")])
+def test_mx_packed_words_full(M, N, K, la, lb):
+    a = synth.weight_codes(72, M, K, tensor_id=1)
+    b = synth.weight_codes(72, N, K, tensor_id=2)
+    ea = synth.e8m0_exponents(72, M, K // 32, tensor_id=3)
+    eb = synth.e8m0_exponents(72, N, K // 32, tensor_id=4)
+    y = _gpu_mx_layouts(a, ea, b, eb, la, lb)
+    ys, ss = oracle.gemm_mx32(a, ea, b, eb)
+    check(y, ys, ss, K, f"mx packed {la}/{lb} {M}x{N}x{K}")
+
+
+# 256x256 tiles (at least 256 of them) with packed words, ragged in both directions
+@pytest.mark.parametrize("la,lb", [("col", "col"), ("row", "bytes")])
+def test_mx_packed_words_wide_sampled(la, lb):
+    M, N, K = 4000, 4200, 1024
+    a = synth.weight_codes(73, M, K, tensor_id=1)
+    b = synth.weight_codes(73, N, K, tensor_id=2)
+    ea = synth.e8m0_exponents(73, M, K // 32, tensor_id=3)
+    eb = synth.e8m0_exponents(73, N, K // 32, tensor_id=4)
+    y = _gpu_mx_layouts(a, ea, b, eb, la, lb)
+    assert not np.any(y == SENT)
+    g = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 3839, 3840, 3999], g.integers(0, M, 40)]))
+    cols = np.unique(np.concatenate([[0, 63, 64, 255, 256, 4095, 4096, 4199], g.integers(0, N, 40)]))
+    ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
+    ys, ss = oracle.gemm_mx32(a, ea, b, eb, at=(ms, ns))
+    check(y[ms, ns], ys, ss, K, f"mx packed wide {la}/{lb}")
+
+
+def test_mx_packed_words_workload_sampled():
+    w = synth.MX
+    a, b, ea, eb = synth.mx_operands(w)
+    y = _gpu_mx_layouts(a, ea, b, eb, "col", "col")
+    ms, ns = _sample(w.M, w.N, 4000, 6)
+    ys, ss = oracle.gemm_mx32(a, ea, b, eb, at=(ms, ns))
+    check(y[ms, ns], ys, ss, w.K, "mxfp8 8192^3, column-major packed words")
+    assert not np.any(y == SENT)
+
+
+def test_quant_g32_packed_words_feed_the_mx_gemm():
+    """group_size 32 with UE8M0 scales in column-major packed words is the MX activation
+    layout: quantize bf16 activations on the GPU, then run the MXFP8 GEMM on its outputs
+    directly; the oracle chain is its quantization (row-major bytes) then its MX32 GEMM."""
+    f = fq()
+    M, N, K = 300, 520, 2048
+    xb = synth.activations_bf16(74, M, K, outlier_p=0.01)
+    b = synth.weight_codes(74, N, K, tensor_id=2)
+    eb = synth.e8m0_exponents(74, N, K // 32, tensor_id=4)
+    x = _dev(xb).view(torch.bfloat16)
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sw = f.alloc_scales(None, M, K // 32, "ue8m0_packed", "col", "cuda")
+    f.fp8q_group_quant(x, q, sw, 32)
+    y = torch.full((M, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_gemm_blockscaled(q, sw, _dev(b), _dev(eb), y.view(torch.bfloat16), f.GEMM_MX32)
+    torch.cuda.synchronize()
+    qo, so = oracle.group_quant(xb, 32, oracle.SCALE_UE8M0, "row")
+    assert np.array_equal(q.cpu().numpy(), qo)
+    ys, ss = oracle.gemm_mx32(qo, so, b, eb)
+    check(y.cpu().numpy().view(np.uint16), ys, ss, K, "quant G=32 packed -> MX32")
+
+
 # ----------------------------------------------------------------------------- API behaviour
 def test_invalid_arguments_write_nothing():
     f = fq()
@@ -341,6 +430,10 @@ def test_invalid_arguments_write_nothing():
         f.fp8q_gemm_blockscaled(a.view(-1)[8:8 + 15 * 256].view(15, 256), sa[:15], b, sb,
                                 y[:15].view(torch.bfloat16))
     assert ei.value.status == f.EALIGN
+    words = torch.zeros((32, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(f.Fp8qError) as ei:  # packed weight scales are an MX32 layout only
+        f.fp8q_gemm_blockscaled(a, sa, b, words[:1], y.view(torch.bfloat16))
+    assert ei.value.status == f.EUNSUPPORTED
     torch.cuda.synchronize()
     assert torch.all(y == SENT_I16)
 
