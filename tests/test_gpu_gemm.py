@@ -116,6 +116,27 @@ def test_wide_tiles_ragged_sampled(K, sa_kind):
     check(y[ms, ns], ys, ss, K, f"wide {M}x{N}x{K} {sa_kind}")
 
 
+# 4000 x 4000 is exactly one round of 256 tiles of 256x256: one launch, ragged in both
+# directions. (4000 x 4200 above takes two: columns [0, 4096) as 256x256 tiles, the last
+# 104 as 128x256 tiles that fill the second round.)
+@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col"])
+def test_wide_tiles_one_round_ragged_sampled(sa_kind):
+    M, N, K = 4000, 4000, 512
+    w = synth.Workload("t", seed=66, M=M, K=K, N=N, scale_fmt=sa_kind.split("-")[0])
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    layout = sa_kind.split("-")[1]
+    sa_store = sa if layout == "row" else np.ascontiguousarray(sa.T)
+    y = _gpu_block(a, sa_store, b, sb, layout)
+    assert not np.any(y == SENT)
+    g = np.random.default_rng(66)
+    rows = np.unique(np.concatenate([[0, 255, 256, 3839, 3840, 3999], g.integers(0, M, 40)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, 3839, 3840, 3999], g.integers(0, N, 40)]))
+    ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
+    ys, ss = oracle.gemm_block128(a, sa_store, b, sb, _fmt(sa), layout, oracle.SCALE_F32, at=(ms, ns))
+    check(y[ms, ns], ys, ss, K, f"wide one round {sa_kind}")
+
+
 def test_padded_output_rows_untouched():
     w = synth.Workload("t", seed=50, M=70, K=256, N=130, scale_fmt="f32")
     a, sa = synth.gemm_activation(w)
