@@ -196,6 +196,46 @@ def test_fp32_sweep_through_unit_scale():
     _assert_same(qg[:2048], qo, "q vs oracle encoder")
 
 
+# Every fp32 bit pattern of magnitude <= 448 (both signs, subnormals and zeros included)
+# through the kernel's fp32 -> e4m3 step: rows of one 448 (UE8M0 byte 127, multiplier exactly
+# 1) and 127 patterns, so each pattern reaches the clamp and the conversion unchanged
+# (anything larger would change the group's scale; the clamp itself is covered by the
+# silu and sweep tests). The reference is torch's CPU cast (a library routine).
+# 2 x (0x43E00000 + 1) patterns in 8 parts, streamed in chunks of 2^25 magnitudes.
+_MAG_END = 0x43E00000 + 1  # bits of 448, plus one
+
+
+@pytest.mark.parametrize("part", range(8))
+def test_fp32_to_e4m3_every_pattern_up_to_448(part):
+    f = fq()
+    chunk = 1 << 25
+    per = 127
+    lo = part * (_MAG_END // 8)
+    hi = _MAG_END if part == 7 else (part + 1) * (_MAG_END // 8)
+    for start in range(lo, hi, chunk):
+        mags = np.arange(start, min(start + chunk, hi), dtype=np.uint32)
+        v = np.concatenate([mags, mags | np.uint32(0x80000000)]).view(np.float32)
+        n = -(-v.size // per)
+        body = np.zeros(n * per, dtype=np.float32)
+        body[:v.size] = v
+        x = np.empty((n, 128), dtype=np.float32)
+        x[:, 0] = 448.0
+        x[:, 1:] = body.reshape(n, per)
+        xd = torch.from_numpy(x).cuda()
+        q = torch.empty((n, 128), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((n, 1), dtype=torch.uint8, device="cuda")
+        f.fp8q_group_quant(xd, q, sc, 128)
+        torch.cuda.synchronize()
+        assert bool(torch.all(sc == 127)), f"chunk {start:#x}: scale byte is not 127"
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8)
+        got = q.cpu()
+        if not torch.equal(got, ref):
+            i, j = (got != ref).nonzero()[0].tolist()
+            raise AssertionError(f"chunk {start:#x}: input bits {x.view(np.uint32)[i, j]:#010x} "
+                                 f"gpu {int(got[i, j]):#04x} torch {int(ref[i, j]):#04x}")
+        del xd, q
+
+
 # ----------------------------------------------------------------------------- masked
 def _masked_input(E, M, K, seed):
     return np.stack([synth.activations_bf16(seed, M, K, tensor_id=(synth.T_X << 12) | e) for e in range(E)])
