@@ -430,8 +430,8 @@ def main(argv=None) -> int:
                     help="print per-kernel lines for every named workload instead of the step line")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no multi-GPU "
-              f"component in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
+              f"multi-GPU path", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
