@@ -244,6 +244,33 @@ def test_masked_f32_row_scales():
         assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
 
 
+# Masked counts on both sides of every 128-row tile boundary up to the capacity, ragged N,
+# both per-step activation scale layouts.
+@pytest.mark.parametrize("sa_kind", ["ue8m0-col", "f32-row"])
+def test_masked_counts_across_tile_boundaries(sa_kind):
+    E, cap, N, K = 10, 700, 320, 256
+    fmt, layout = sa_kind.split("-")
+    w = synth.Workload("m", seed=63, M=cap, K=K, N=N, E=E, scale_fmt=fmt, layout=layout, masked=True)
+    ops = [synth.gemm_activation(w, e) + synth.weights(w, e) for e in range(E)]
+    a, sa, b, sb = (np.stack([o[i] for o in ops]) for i in range(4))
+    mm = np.array([128, 384, 385, 512, 513, 640, 641, 257, 700, 127], dtype=np.int32)
+    f = fq()
+    y = torch.full((E, cap, N), SENT_I16, dtype=torch.int16, device="cuda")
+    if layout == "col":
+        sa_dev = _dev(np.ascontiguousarray(sa.transpose(0, 2, 1))).transpose(1, 2)
+    else:
+        sa_dev = _dev(sa)
+    f.fp8q_grouped_gemm_masked(_dev(a), sa_dev, _dev(b), _dev(sb), y.view(torch.bfloat16), _dev(mm), 0)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().view(np.uint16)
+    sfmt = oracle.SCALE_UE8M0 if fmt == "ue8m0" else oracle.SCALE_F32
+    for e in range(E):
+        r = int(mm[e])
+        ys, ss = oracle.gemm_block128(a[e, :r], np.ascontiguousarray(sa[e, :r]), b[e], sb[e], sfmt, "row")
+        check(y[e, :r], ys, ss, K, f"expert {e} ({r} rows)")
+        assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
+
+
 def test_masked_result_independent_of_expected_m():
     E, cap, N, K = 6, 300, 384, 256
     a, sa, b, sb = _masked_operands(E, cap, N, K, 61)
