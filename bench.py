@@ -36,9 +36,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def _kernel_source_tag(name: str) -> str:
+    """Hash of a kernel source and the shared internal header, with // comments and blank
+    lines removed: a comment edit keeps the tag, any code change breaks it."""
     import hashlib
-    with open(os.path.join(ROOT, "fp8_group_quant_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    h = hashlib.sha256()
+    for fn in (name, "fp8q_internal.h"):
+        with open(os.path.join(ROOT, "fp8_group_quant_amd", "csrc", fn), encoding="utf-8") as f:
+            for line in f:
+                line = re.sub(r"//.*$", "", line).rstrip()
+                if line.strip():
+                    h.update(line.encode() + b"\n")
+    return h.hexdigest()[:16]
 
 
 def _measured_traffic(kernel_file: str, workload: str):

@@ -1,10 +1,12 @@
-// gemm.hip — block-scaled FP8 GEMMs for gfx950: the 1x128 x 128x128 groupwise GEMM (dense
-// and masked grouped per expert) and the MXFP8 GEMM with 1x32 E8M0 scales.
+// gemm.hip — block-scaled FP8 GEMMs for gfx950: the 1x128 x 128x128 groupwise GEMM (dense,
+// masked grouped per expert, and grouped over packed rows by segments or by m_indices) and
+// the MXFP8 GEMM with 1x32 E8M0 scales.
 //
 // What is computed follows "FlashInfer GEMM 学习笔记", section 6 (block-scaled FP8 and
 // MXFP8 with block size 32, plain 2D scale tensors) and section 7 (DeepGEMM's NT groupwise
-// GEMM, grouped masked with expected_m + masked_m), with the activation-side scales that
-// the per-token-group quantizer produces (sglang PR #30924 report, prhub, "实现拆解"):
+// GEMM: grouped masked with expected_m + masked_m, grouped contiguous with m_indices, and
+// SegmentGEMM over seg_indptr), with the activation-side scales that the per-token-group
+// quantizer produces (sglang PR #30924 report, prhub, "实现拆解"):
 //   BLOCK128: Y[m][n] = bf16( sum_kb sa(m,kb) * sb(n/128,kb) * sum_{k in kb} A[m][k] B[n][k] )
 //   MX32:     Y[m][n] = bf16( sum_k 2^(ea(m,k/32)-127) A[m][k] * 2^(eb(n,k/32)-127) B[n][k] )
 //
@@ -22,24 +24,27 @@
 //   - K layout inside a lane (measured on gfx950): lane l of a 16x16x128 operand holds row
 //     l%16 and two 16-byte runs of K, at 16*(l/16) and 64 + 16*(l/16); the E8M0 scale for
 //     (row i, 32-wide block b) comes from lane i + 16*b.
-//   - 256x128 output tiles, 8 wavefronts of 64(m) x 64(n), K step 128; large flat
-//     problems use 256x256 tiles, 8 wavefronts of 128(m) x 64(n), which load a third fewer
-//     operand bytes per output. LDS rows are 128 bytes with the 16-byte chunk index
-//     XOR-swizzled by (row/2)%8, which keeps the 16 rows read by one fragment load on
-//     distinct banks without padding.
+//   - Tile shapes, all with 8 wavefronts and K steps of 128: 256x256 (wave tiles 128x64,
+//     two LDS stages) for large flat problems and MXFP8; 128x256 (wave tiles 64x64, three
+//     stages) for grouped launches, whose groups pad rows to 128, and for the columns that
+//     fill a flat problem's last round of tiles; 256x128 otherwise. LDS rows are 128 bytes
+//     with the 16-byte chunk index XOR-swizzled by (row/2)%8, which keeps the 16 rows read
+//     by one fragment load on distinct banks without padding.
 //   - Two ways to fill LDS. The main kernel loads operand tiles and scales straight into
-//     LDS (global_load_lds) through three stages with one barrier per step, so loads have
-//     two steps to land and the next step's first operands are read during the current
-//     step's last row (see "direct-to-LDS pipeline" below). Scale layouts it cannot move
-//     in aligned 4-byte pieces go to a register-staged kernel: loads issued two steps
-//     ahead into one of two register sets, written to one of two LDS stages.
-//   - BLOCK128 fold pipeline: the MFMAs of subtile row i are interleaved with the fold of
-//     row i-1 (the last row's fold moves into the next step), so no fold waits on the
-//     MFMA it consumes and the fold's VALU work co-issues with the matrix core.
+//     LDS (global_load_lds), one barrier per step, loads issued one or two steps ahead and
+//     the next step's first operands read during the current step's last row (see
+//     "direct-to-LDS pipeline" below). Scale layouts it cannot move in aligned 4-byte
+//     pieces go to a register-staged kernel: loads issued two steps ahead into one of two
+//     register sets, written to one of two LDS stages.
+//   - BLOCK128 fold pipeline: each MFMA product goes to a four-slot register ring and is
+//     folded three MFMAs later, so no fold waits on the MFMA it consumes and the fold's
+//     VALU work co-issues with the matrix core.
 //   - persistent workgroups (one per CU); the tile list is split into 8 contiguous ranges,
 //     one per XCD (workgroup w runs on XCD w % 8), and dense tiles are ordered in groups of
-//     4 m-tiles so one XCD's tiles share operand rows in its L2. Masked grouped launches
-//     build the tile list on device from masked_m, so the work scales with the valid rows.
+//     4 m-tiles so one XCD's tiles share operand rows in its L2. Grouped launches build the
+//     tile list on device (from masked_m or seg_indptr; m_indices per 128-row block), so
+//     the work scales with the valid rows.
+//   - M <= 128: a split-K kernel streams 16 rows of B per workgroup through LDS.
 #include "fp8q_internal.h"
 
 #include <utility>
