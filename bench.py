@@ -245,9 +245,13 @@ def _nsets(set_bytes: int, cap: int = 8) -> int:
     return max(1, min(cap, -(-(1 << 30) // max(set_bytes, 1))))
 
 
-def suite(steps: int, warmup: int) -> list:
+SUITE_SECTIONS = ("flat", "variants", "masked", "moe_down", "mxfp8")
+
+
+def suite(steps: int, warmup: int, only=None) -> list:
     """Per-kernel figures for every named workload (quant GB/s, GEMM TFLOP/s and HBM GB/s),
-    each timed over `steps` launches rotating over >= 1 GiB of buffers where memory allows."""
+    each timed over `steps` launches rotating over >= 1 GiB of buffers where memory allows.
+    `only`: a subset of SUITE_SECTIONS to run (all when None)."""
     import torch
     import fp8_group_quant_amd as fq
     import synth
@@ -271,159 +275,167 @@ def suite(steps: int, warmup: int) -> list:
     def run(fn, n_sets):
         return _timed(fn, steps, max(warmup, 10))
 
-    # flat workloads: quant then block-scaled GEMM
-    for w in (synth.TINY, synth.dense(1), synth.dense(16), synth.dense(128), synth.dense(4096), synth.SILU):
-        M, K, N, G = w.M, w.K, w.N, w.G
+    def want(section):
+        return only is None or section in only
+
+    if want("flat"):
+        # flat workloads: quant then block-scaled GEMM
+        for w in (synth.TINY, synth.dense(1), synth.dense(16), synth.dense(128), synth.dense(4096), synth.SILU):
+            M, K, N, G = w.M, w.K, w.N, w.G
+            x = torch.from_numpy(synth.quant_input(w)).to(dev).view(torch.bfloat16)
+            wq, ws = synth.weights(w)
+            wd, wsd = torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)
+            set_bytes = x.numel() * 2 + M * K + wd.numel() + M * N * 2
+            ns = _nsets(set_bytes)
+            sets = [dict(x=x.clone(), q=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                         s=fq.alloc_scales(None, M, K // G, w.scale_fmt, w.layout, dev), w=wd.clone(), sw=wsd.clone(),
+                         y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(ns)]
+            qf = fq.fp8q_silu_mul_group_quant if w.silu else fq.fp8q_group_quant
+            ms = run(lambda i: qf(sets[i % ns]["x"], sets[i % ns]["q"], sets[i % ns]["s"], G), ns)
+            report(w.name, "silu_mul_group_quant" if w.silu else "group_quant", ms,
+                   nbytes=quant_bytes(M, K, G, 2, 1 if w.scale_fmt == "ue8m0" else 4, w.silu))
+            ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["q"], sets[i % ns]["s"], sets[i % ns]["w"],
+                                                        sets[i % ns]["sw"], sets[i % ns]["y"]), ns)
+            sbytes = M * (K // 128) * (1 if w.scale_fmt == "ue8m0" else 4) + ws.nbytes
+            report(w.name, "gemm_blockscaled", ms, flops=2.0 * M * N * K, nbytes=M * K + N * K + sbytes + M * N * 2)
+            del sets
+            torch.cuda.empty_cache()
+
+    if want("variants"):
+        # quant variants on the dense M=4096 activations: per-token (G = K, one fp32 scale per
+        # row) and int8 output (G = 128, fp32 row-major scales)
+        w = synth.dense(4096)
+        M, K = w.M, w.K
         x = torch.from_numpy(synth.quant_input(w)).to(dev).view(torch.bfloat16)
-        wq, ws = synth.weights(w)
-        wd, wsd = torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)
-        set_bytes = x.numel() * 2 + M * K + wd.numel() + M * N * 2
-        ns = _nsets(set_bytes)
+        ns = _nsets(x.numel() * 3)
         sets = [dict(x=x.clone(), q=torch.empty((M, K), dtype=torch.uint8, device=dev),
-                     s=fq.alloc_scales(None, M, K // G, w.scale_fmt, w.layout, dev), w=wd.clone(), sw=wsd.clone(),
-                     y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(ns)]
-        qf = fq.fp8q_silu_mul_group_quant if w.silu else fq.fp8q_group_quant
-        ms = run(lambda i: qf(sets[i % ns]["x"], sets[i % ns]["q"], sets[i % ns]["s"], G), ns)
-        report(w.name, "silu_mul_group_quant" if w.silu else "group_quant", ms,
-               nbytes=quant_bytes(M, K, G, 2, 1 if w.scale_fmt == "ue8m0" else 4, w.silu))
-        ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["q"], sets[i % ns]["s"], sets[i % ns]["w"],
-                                                    sets[i % ns]["sw"], sets[i % ns]["y"]), ns)
-        sbytes = M * (K // 128) * (1 if w.scale_fmt == "ue8m0" else 4) + ws.nbytes
-        report(w.name, "gemm_blockscaled", ms, flops=2.0 * M * N * K, nbytes=M * K + N * K + sbytes + M * N * 2)
-        del sets
+                     s=torch.empty((M, 1), dtype=torch.float32, device=dev),
+                     s8=torch.empty((M, K // 128), dtype=torch.float32, device=dev)) for _ in range(ns)]
+        ms = run(lambda i: fq.fp8q_group_quant(sets[i % ns]["x"], sets[i % ns]["q"], sets[i % ns]["s"], K), ns)
+        report("dense_m4096_per_token", "token_quant", ms, nbytes=quant_bytes(M, K, K, 2, 4, False),
+               extra={"scales": "f32 [M, 1]"})
+        ms = run(lambda i: fq.fp8q_group_quant_int8(sets[i % ns]["x"], sets[i % ns]["q"].view(torch.int8),
+                                                    sets[i % ns]["s8"], 128), ns)
+        report("dense_m4096_int8", "group_quant_int8", ms, nbytes=quant_bytes(M, K, 128, 2, 4, False),
+               extra={"scales": "f32 row-major"})
+        del sets, x
         torch.cuda.empty_cache()
 
-    # quant variants on the dense M=4096 activations: per-token (G = K, one fp32 scale per
-    # row) and int8 output (G = 128, fp32 row-major scales)
-    w = synth.dense(4096)
-    M, K = w.M, w.K
-    x = torch.from_numpy(synth.quant_input(w)).to(dev).view(torch.bfloat16)
-    ns = _nsets(x.numel() * 3)
-    sets = [dict(x=x.clone(), q=torch.empty((M, K), dtype=torch.uint8, device=dev),
-                 s=torch.empty((M, 1), dtype=torch.float32, device=dev),
-                 s8=torch.empty((M, K // 128), dtype=torch.float32, device=dev)) for _ in range(ns)]
-    ms = run(lambda i: fq.fp8q_group_quant(sets[i % ns]["x"], sets[i % ns]["q"], sets[i % ns]["s"], K), ns)
-    report("dense_m4096_per_token", "token_quant", ms, nbytes=quant_bytes(M, K, K, 2, 4, False),
-           extra={"scales": "f32 [M, 1]"})
-    ms = run(lambda i: fq.fp8q_group_quant_int8(sets[i % ns]["x"], sets[i % ns]["q"].view(torch.int8),
-                                                sets[i % ns]["s8"], 128), ns)
-    report("dense_m4096_int8", "group_quant_int8", ms, nbytes=quant_bytes(M, K, 128, 2, 4, False),
-           extra={"scales": "f32 row-major"})
-    del sets, x
-    torch.cuda.empty_cache()
+    if want("masked"):
+        # masked MoE: masked quant then masked grouped GEMM
+        w = synth.MASKED
+        E, cap, K, N, G = w.E, w.M, w.K, w.N, w.G
+        mm = synth.masked_rows(w.seed, E, cap)
+        rows = int(mm.sum())
+        x = torch.from_numpy(np.stack([synth.quant_input(w, e) for e in range(E)])).to(dev).view(torch.bfloat16)
+        mmd = torch.from_numpy(mm).to(dev)
+        q = torch.empty((E, cap, K), dtype=torch.uint8, device=dev)
+        sq = fq.alloc_scales(E, cap, K // G, "ue8m0", "col", dev)
+        ms = run(lambda i: fq.fp8q_group_quant(x, q, sq, G, masked_m=mmd, expected_m=cap // 2), 1)
+        report(w.name, "group_quant_masked", ms, nbytes=quant_bytes(rows, K, G, 2, 1, False), extra={"sum_masked_m": rows})
+        del x
+        wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+        ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+        for e in range(E):
+            a, b = synth.weights(w, e)
+            wq[e].copy_(torch.from_numpy(a))
+            ws[e].copy_(torch.from_numpy(b))
+        y = torch.empty((E, cap, N), dtype=torch.bfloat16, device=dev)
+        ms = run(lambda i: fq.fp8q_grouped_gemm_masked(q, sq, wq, ws, y, mmd, cap // 2), 1)
+        active = int((mm > 0).sum())
+        gemm_bytes = rows * K + active * N * K + rows * (K // 128) + active * ws[0].numel() * 4 + rows * N * 2
+        report(w.name, "grouped_gemm_masked", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
+               extra={"sum_masked_m": rows})
+        del y
+        # the same experts' rows packed one after another: the contiguous layout (each expert at a
+        # 128-aligned offset, padded with m_indices = -1; UE8M0 column-major scales) and segments
+        # (no padding; packed UE8M0 words, which are the row-major bytes read as int32)
+        sq_store = sq.transpose(1, 2)  # [E, K/128, cap] storage
+        blocks = (mm.astype(np.int64) + 127) // 128
+        offs = np.concatenate([[0], np.cumsum(blocks * 128)])
+        Tc = int(offs[-1])
+        ac = torch.zeros((Tc, K), dtype=torch.uint8, device=dev)
+        sc = torch.zeros((K // G, Tc), dtype=torch.uint8, device=dev)
+        mi = torch.full((Tc,), -1, dtype=torch.int32, device=dev)
+        seg = np.concatenate([[0], np.cumsum(mm.astype(np.int64))])
+        asg = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+        ssg = torch.empty((rows, K // G), dtype=torch.uint8, device=dev)
+        for e in range(E):
+            m, o, so = int(mm[e]), int(offs[e]), int(seg[e])
+            ac[o:o + m] = q[e, :m]
+            sc[:, o:o + m] = sq_store[e, :, :m]
+            mi[o:o + m] = e
+            asg[so:so + m] = q[e, :m]
+            ssg[so:so + m] = sq_store[e, :, :m].t()
+        yc = torch.empty((Tc, N), dtype=torch.bfloat16, device=dev)
+        ms = run(lambda i: fq.fp8q_grouped_gemm_contiguous(ac, sc.t(), wq, ws, yc, mi), 1)
+        report("contiguous_moe", "grouped_gemm_contiguous", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
+               extra={"rows": rows, "padded_rows": Tc, "layout": "masked_moe experts, 128-aligned, m_indices"})
+        del yc, ac, sc, mi
+        ys = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+        sid = torch.from_numpy(seg.astype(np.int32)).to(dev)
+        ms = run(lambda i: fq.fp8q_grouped_gemm_segments(asg, ssg.view(torch.int32), wq, ws, ys, sid,
+                                                         expected_rows=rows), 1)
+        report("segments_moe", "grouped_gemm_segments", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
+               extra={"rows": rows, "layout": "masked_moe experts, seg_indptr, packed UE8M0 words"})
+        del ys, asg, ssg, wq, q
+        torch.cuda.empty_cache()
 
-    # masked MoE: masked quant then masked grouped GEMM
-    w = synth.MASKED
-    E, cap, K, N, G = w.E, w.M, w.K, w.N, w.G
-    mm = synth.masked_rows(w.seed, E, cap)
-    rows = int(mm.sum())
-    x = torch.from_numpy(np.stack([synth.quant_input(w, e) for e in range(E)])).to(dev).view(torch.bfloat16)
-    mmd = torch.from_numpy(mm).to(dev)
-    q = torch.empty((E, cap, K), dtype=torch.uint8, device=dev)
-    sq = fq.alloc_scales(E, cap, K // G, "ue8m0", "col", dev)
-    ms = run(lambda i: fq.fp8q_group_quant(x, q, sq, G, masked_m=mmd, expected_m=cap // 2), 1)
-    report(w.name, "group_quant_masked", ms, nbytes=quant_bytes(rows, K, G, 2, 1, False), extra={"sum_masked_m": rows})
-    del x
-    wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
-    ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
-    for e in range(E):
-        a, b = synth.weights(w, e)
-        wq[e].copy_(torch.from_numpy(a))
-        ws[e].copy_(torch.from_numpy(b))
-    y = torch.empty((E, cap, N), dtype=torch.bfloat16, device=dev)
-    ms = run(lambda i: fq.fp8q_grouped_gemm_masked(q, sq, wq, ws, y, mmd, cap // 2), 1)
-    active = int((mm > 0).sum())
-    gemm_bytes = rows * K + active * N * K + rows * (K // 128) + active * ws[0].numel() * 4 + rows * N * 2
-    report(w.name, "grouped_gemm_masked", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
-           extra={"sum_masked_m": rows})
-    del y
-    # the same experts' rows packed one after another: the contiguous layout (each expert at a
-    # 128-aligned offset, padded with m_indices = -1; UE8M0 column-major scales) and segments
-    # (no padding; packed UE8M0 words, which are the row-major bytes read as int32)
-    sq_store = sq.transpose(1, 2)  # [E, K/128, cap] storage
-    blocks = (mm.astype(np.int64) + 127) // 128
-    offs = np.concatenate([[0], np.cumsum(blocks * 128)])
-    Tc = int(offs[-1])
-    ac = torch.zeros((Tc, K), dtype=torch.uint8, device=dev)
-    sc = torch.zeros((K // G, Tc), dtype=torch.uint8, device=dev)
-    mi = torch.full((Tc,), -1, dtype=torch.int32, device=dev)
-    seg = np.concatenate([[0], np.cumsum(mm.astype(np.int64))])
-    asg = torch.empty((rows, K), dtype=torch.uint8, device=dev)
-    ssg = torch.empty((rows, K // G), dtype=torch.uint8, device=dev)
-    for e in range(E):
-        m, o, so = int(mm[e]), int(offs[e]), int(seg[e])
-        ac[o:o + m] = q[e, :m]
-        sc[:, o:o + m] = sq_store[e, :, :m]
-        mi[o:o + m] = e
-        asg[so:so + m] = q[e, :m]
-        ssg[so:so + m] = sq_store[e, :, :m].t()
-    yc = torch.empty((Tc, N), dtype=torch.bfloat16, device=dev)
-    ms = run(lambda i: fq.fp8q_grouped_gemm_contiguous(ac, sc.t(), wq, ws, yc, mi), 1)
-    report("contiguous_moe", "grouped_gemm_contiguous", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
-           extra={"rows": rows, "padded_rows": Tc, "layout": "masked_moe experts, 128-aligned, m_indices"})
-    del yc, ac, sc, mi
-    ys = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
-    sid = torch.from_numpy(seg.astype(np.int32)).to(dev)
-    ms = run(lambda i: fq.fp8q_grouped_gemm_segments(asg, ssg.view(torch.int32), wq, ws, ys, sid,
-                                                     expected_rows=rows), 1)
-    report("segments_moe", "grouped_gemm_segments", ms, flops=2.0 * rows * N * K, nbytes=gemm_bytes,
-           extra={"rows": rows, "layout": "masked_moe experts, seg_indptr, packed UE8M0 words"})
-    del ys, asg, ssg, wq, q
-    torch.cuda.empty_cache()
+    if want("moe_down"):
+        # MoE second stage: masked silu_and_mul + quant into packed UE8M0 words (column-major,
+        # four groups per word), then the masked grouped down-projection GEMM
+        w = synth.MASKED_DOWN
+        E, cap, K, N, G = w.E, w.M, w.K, w.N, w.G
+        mm = synth.masked_rows(w.seed, E, cap)
+        rows = int(mm.sum())
+        h = torch.from_numpy(np.stack([synth.quant_input(w, e) for e in range(E)])).to(dev).view(torch.bfloat16)
+        mmd = torch.from_numpy(mm).to(dev)
+        q = torch.empty((E, cap, K), dtype=torch.uint8, device=dev)
+        sq = fq.alloc_scales(E, cap, K // G, "ue8m0_packed", "col", dev)
+        ms = run(lambda i: fq.fp8q_silu_mul_group_quant(h, q, sq, G, masked_m=mmd, expected_m=cap // 2), 1)
+        report(w.name, "silu_mul_group_quant_masked", ms, nbytes=quant_bytes(rows, K, G, 2, 1, True),
+               extra={"sum_masked_m": rows, "scales": "ue8m0 packed, column-major words"})
+        del h
+        wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+        ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+        for e in range(E):
+            a, b = synth.weights(w, e)
+            wq[e].copy_(torch.from_numpy(a))
+            ws[e].copy_(torch.from_numpy(b))
+        y = torch.empty((E, cap, N), dtype=torch.bfloat16, device=dev)
+        ms = run(lambda i: fq.fp8q_grouped_gemm_masked(q, sq, wq, ws, y, mmd, cap // 2), 1)
+        active = int((mm > 0).sum())
+        report(w.name, "grouped_gemm_masked", ms, flops=2.0 * rows * N * K,
+               nbytes=rows * K + active * N * K + rows * (K // 128) + active * ws[0].numel() * 4 + rows * N * 2,
+               extra={"sum_masked_m": rows})
+        del wq, q, y
+        torch.cuda.empty_cache()
 
-    # MoE second stage: masked silu_and_mul + quant into packed UE8M0 words (column-major,
-    # four groups per word), then the masked grouped down-projection GEMM
-    w = synth.MASKED_DOWN
-    E, cap, K, N, G = w.E, w.M, w.K, w.N, w.G
-    mm = synth.masked_rows(w.seed, E, cap)
-    rows = int(mm.sum())
-    h = torch.from_numpy(np.stack([synth.quant_input(w, e) for e in range(E)])).to(dev).view(torch.bfloat16)
-    mmd = torch.from_numpy(mm).to(dev)
-    q = torch.empty((E, cap, K), dtype=torch.uint8, device=dev)
-    sq = fq.alloc_scales(E, cap, K // G, "ue8m0_packed", "col", dev)
-    ms = run(lambda i: fq.fp8q_silu_mul_group_quant(h, q, sq, G, masked_m=mmd, expected_m=cap // 2), 1)
-    report(w.name, "silu_mul_group_quant_masked", ms, nbytes=quant_bytes(rows, K, G, 2, 1, True),
-           extra={"sum_masked_m": rows, "scales": "ue8m0 packed, column-major words"})
-    del h
-    wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
-    ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
-    for e in range(E):
-        a, b = synth.weights(w, e)
-        wq[e].copy_(torch.from_numpy(a))
-        ws[e].copy_(torch.from_numpy(b))
-    y = torch.empty((E, cap, N), dtype=torch.bfloat16, device=dev)
-    ms = run(lambda i: fq.fp8q_grouped_gemm_masked(q, sq, wq, ws, y, mmd, cap // 2), 1)
-    active = int((mm > 0).sum())
-    report(w.name, "grouped_gemm_masked", ms, flops=2.0 * rows * N * K,
-           nbytes=rows * K + active * N * K + rows * (K // 128) + active * ws[0].numel() * 4 + rows * N * 2,
-           extra={"sum_masked_m": rows})
-    del wq, q, y
-    torch.cuda.empty_cache()
-
-    # MXFP8
-    w = synth.MX
-    a, b, ea, eb = synth.mx_operands(w)
-    ad, bd, ead, ebd = (torch.from_numpy(t).to(dev) for t in (a, b, ea, eb))
-    ns = _nsets(a.nbytes + b.nbytes + w.M * w.N * 2, 4)
-    sets = [dict(a=ad.clone(), b=bd.clone(), ea=ead.clone(), eb=ebd.clone(),
-                 y=torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)) for _ in range(ns)]
-    ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
-                                                sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32), ns)
-    report(w.name, "gemm_mx32", ms, flops=2.0 * w.M * w.N * w.K,
-           nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
-           extra={"scales": "E8M0 bytes, row-major [rows, K/32]"})
-    # the same operands with both scale tensors as column-major packed words [K/128, rows]
-    # (four E8M0 bytes of one 128-wide K step per 32-bit word)
-    def col_words(e):
-        wd = e.view(np.uint32) if e.flags.c_contiguous else np.ascontiguousarray(e).view(np.uint32)
-        return torch.from_numpy(np.ascontiguousarray(wd.T).view(np.int32)).to(dev).t()
-    for st in sets:
-        st["ea"], st["eb"] = col_words(ea), col_words(eb)
-    ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
-                                                sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32), ns)
-    report(w.name, "gemm_mx32", ms, flops=2.0 * w.M * w.N * w.K,
-           nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
-           extra={"scales": "E8M0 packed words, column-major [K/128, rows]"})
+    if want("mxfp8"):
+        # MXFP8
+        w = synth.MX
+        a, b, ea, eb = synth.mx_operands(w)
+        ad, bd, ead, ebd = (torch.from_numpy(t).to(dev) for t in (a, b, ea, eb))
+        ns = _nsets(a.nbytes + b.nbytes + w.M * w.N * 2, 4)
+        sets = [dict(a=ad.clone(), b=bd.clone(), ea=ead.clone(), eb=ebd.clone(),
+                     y=torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)) for _ in range(ns)]
+        ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
+                                                    sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32), ns)
+        report(w.name, "gemm_mx32", ms, flops=2.0 * w.M * w.N * w.K,
+               nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
+               extra={"scales": "E8M0 bytes, row-major [rows, K/32]"})
+        # the same operands with both scale tensors as column-major packed words [K/128, rows]
+        # (four E8M0 bytes of one 128-wide K step per 32-bit word)
+        def col_words(e):
+            wd = e.view(np.uint32) if e.flags.c_contiguous else np.ascontiguousarray(e).view(np.uint32)
+            return torch.from_numpy(np.ascontiguousarray(wd.T).view(np.int32)).to(dev).t()
+        for st in sets:
+            st["ea"], st["eb"] = col_words(ea), col_words(eb)
+        ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
+                                                    sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32), ns)
+        report(w.name, "gemm_mx32", ms, flops=2.0 * w.M * w.N * w.K,
+               nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
+               extra={"scales": "E8M0 packed words, column-major [K/128, rows]"})
     return lines
 
 
@@ -435,6 +447,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="dense_m4096")
     ap.add_argument("--cpu-rows", type=int, default=384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="with --suite: comma-separated sections to run (" + ",".join(SUITE_SECTIONS) + ")")
     ap.add_argument("--suite", action="store_true",
                     help="print per-kernel lines for every named workload instead of the step line")
     args = ap.parse_args(argv)
@@ -445,7 +459,13 @@ def main(argv=None) -> int:
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
     if args.suite:
-        suite(args.steps, args.warmup)
+        only = None
+        if args.only:
+            only = set(args.only.split(","))
+            bad = only - set(SUITE_SECTIONS)
+            if bad:
+                raise SystemExit(f"unknown suite sections: {sorted(bad)}")
+        suite(args.steps, args.warmup, only)
         return 0
     print(json.dumps(run(args)), flush=True)
     return 0
