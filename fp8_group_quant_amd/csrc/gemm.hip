@@ -708,11 +708,9 @@ struct DmaRun {
   uint32_t ea[SM], eb[SN];
   v4f acc[SM][SN];
   // BLOCK128 fold pipeline: the product of MFMA t of a step from stage S sits in
-  // pr[(kSlot0 * S + t) % 3] and is folded two MFMAs later; the last two of a step are
-  // folded at the start of the next one with that step's last-row factor pend_s. With
-  // three stages the numbering runs on across steps (3 steps hold a multiple of 3 MFMAs);
-  // with two, each step starts at slot 0 and first moves the two pending products to
-  // the slots of MFMAs -2 and -1.
+  // pr[(kSlot0 * S + t) % kRingN] and is folded kLag MFMAs later; the last kLag of a step
+  // are folded at the start of the next one with that step's last-row factor pend_s. The
+  // slot numbering runs on across steps (a step holds a multiple of kRingN MFMAs).
   static constexpr int kLag = 3;  // MFMAs between a product and its fold
   static constexpr int kRingN = kLag + 1;
   static_assert(kLag == 2 || kPerStep % kRingN == 0, "ring numbering must run on across steps");
