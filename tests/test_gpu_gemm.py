@@ -684,6 +684,73 @@ def test_contiguous_full(kind):
     _check_rows(yg, Y, S, K, f"contiguous {kind}")
 
 
+# The suite's packed-row MoE workloads at full expert shape (K=7168, N=4096) for the first 8
+# experts of masked_moe with their row counts: each expert's rows placed at a 128-aligned
+# offset with -1 padding (contiguous, UE8M0 column-major bytes) or back to back (segments,
+# packed UE8M0 words). Sampled outputs of every expert are compared with the oracle run on
+# that expert's own operands; padding rows must stay untouched.
+def _moe_experts(n_exp):
+    w = synth.MASKED
+    mm = synth.masked_rows(w.seed, w.E, w.M)[:n_exp].astype(np.int64)
+    mm[0] = 0  # an empty expert
+    acts = [synth.gemm_activation(w, e) for e in range(n_exp)]
+    wts = [synth.weights(w, e) for e in range(n_exp)]
+    return w, mm, acts, wts
+
+
+def _moe_samples(mm, N, seed):
+    g = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([[0, 127, 128, 255, 256, N - 1], g.integers(0, N, 58)]))
+    out = []
+    for e, r in enumerate(mm):
+        if r == 0:
+            continue
+        rows = np.unique(np.concatenate([[0, r - 1], g.integers(0, r, 3)]))
+        ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
+        out.append((e, ms, ns))
+    return out
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "segments"])
+def test_moe_packed_rows_workload_sampled(layout):
+    f = fq()
+    n_exp = 8
+    w, mm, acts, wts = _moe_experts(n_exp)
+    K, N = w.K, w.N
+    if layout == "contiguous":
+        offs = np.concatenate([[0], np.cumsum((mm + 127) // 128 * 128)])
+    else:
+        offs = np.concatenate([[0], np.cumsum(mm)])
+    T = int(offs[-1])
+    A = np.zeros((T, K), dtype=np.uint8)
+    SA = np.zeros((T, K // 128), dtype=np.uint8)
+    mi = np.full(T, -1, dtype=np.int32)
+    for e in range(n_exp):
+        r, o = int(mm[e]), int(offs[e])
+        A[o:o + r] = acts[e][0][:r]
+        SA[o:o + r] = acts[e][1][:r]
+        mi[o:o + r] = e
+    B = np.stack([x[0] for x in wts])
+    SB = np.stack([x[1] for x in wts])
+    y = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
+    if layout == "contiguous":
+        f.fp8q_grouped_gemm_contiguous(_dev(A), _dev(np.ascontiguousarray(SA.T)).t(), _dev(B), _dev(SB),
+                                       y.view(torch.bfloat16), _dev(mi))
+    else:
+        f.fp8q_grouped_gemm_segments(_dev(A), _dev(oracle.pack_ue8m0(SA)), _dev(B), _dev(SB), y.view(torch.bfloat16),
+                                     _dev(offs.astype(np.int32)), expected_rows=T)
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy().view(np.uint16)
+    y_all, ys_all, s_all = [], [], []
+    for e, ms, ns in _moe_samples(mm, N, 11):
+        a_e, sa_e = acts[e]
+        ys, ss = oracle.gemm_block128(a_e, sa_e, wts[e][0], wts[e][1], oracle.SCALE_UE8M0, "row", at=(ms, ns))
+        y_all.append(yg[int(offs[e]) + ms, ns]); ys_all.append(ys); s_all.append(ss)
+    check(np.concatenate(y_all), np.concatenate(ys_all), np.concatenate(s_all), K, f"{layout} moe experts")
+    if layout == "contiguous":
+        assert np.all(yg[mi < 0] == SENT), "padding rows were written"
+
+
 def test_contiguous_unsupported_scale_layout_writes_nothing():
     T, N, K, W = 256, 128, 512, 2
     a, sa, b, sb = _grouped_operands(T, N, K, W, 72, "ue8m0")

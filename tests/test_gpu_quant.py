@@ -438,6 +438,22 @@ def test_int8_masked_and_per_token():
     _full_case(synth.activations_bf16(44, 33, 9216), oracle.BF16, 9216, oracle.SCALE_F32, "col", int8=True)
 
 
+def test_int8_dense_m4096_sampled():
+    w = synth.dense(4096)
+    x = synth.quant_input(w)
+    qg, sg = _gpu_quant(x, oracle.BF16, 128, oracle.SCALE_F32, "row", int8=True)
+    g = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, 1, 4095], g.integers(0, 4096, size=45)]))
+    qo, so = _oracle(x, oracle.BF16, 128, oracle.SCALE_F32, "row", rows=(np.zeros_like(rows), rows), int8=True)
+    for m in rows:
+        _assert_same(qg[m], qo[m], f"q row {m}")
+        _assert_same(sg[m].view(np.uint8), so[m].view(np.uint8), f"s row {m}")
+    # everywhere: codes in [-127, 127] and each group's largest magnitude at 127
+    c = qg.view(np.int8).astype(np.int16)
+    assert c.min() >= -127 and c.max() <= 127
+    assert np.all(np.abs(c).reshape(4096, 56, 128).max(-1) == 127)
+
+
 def test_int8_rejects_ue8m0_scales():
     f = fq()
     x = torch.ones((4, 256), dtype=torch.bfloat16, device="cuda")
