@@ -318,6 +318,22 @@ def suite(steps: int, warmup: int, only=None) -> list:
                                                     sets[i % ns]["s8"], 128), ns)
         report("dense_m4096_int8", "group_quant_int8", ms, nbytes=quant_bytes(M, K, 128, 2, 4, False),
                extra={"scales": "f32 row-major"})
+        # the dense GEMM with UE8M0 weight-block scales (powers of two on both sides: applied by
+        # the matrix core, no fold)
+        N = w.N
+        wq, ws = synth.weights(w)
+        ws8 = synth.e8m0_exponents(w.seed, ws.shape[0], ws.shape[1], lo=-4, hi=4, tensor_id=synth.T_SW + 1)
+        for st in sets:
+            qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            sa_col = fq.alloc_scales(None, M, K // 128, "ue8m0", "col", dev)
+            fq.fp8q_group_quant(st["x"], qa, sa_col, 128)
+            st.update(qa=qa, sa_col=sa_col, w=torch.from_numpy(wq).to(dev), sw8=torch.from_numpy(ws8).to(dev),
+                      y=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+        ms = run(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["qa"], sets[i % ns]["sa_col"], sets[i % ns]["w"],
+                                                    sets[i % ns]["sw8"], sets[i % ns]["y"]), ns)
+        report("dense_m4096_ue8m0_weights", "gemm_blockscaled", ms, flops=2.0 * M * N * K,
+               nbytes=M * K + N * K + M * (K // 128) + ws8.nbytes + M * N * 2,
+               extra={"weight_scale": "ue8m0 128x128"})
         del sets, x
         torch.cuda.empty_cache()
 

@@ -606,7 +606,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 // first read four steps later. The scale load of the other steps (and of the wavefronts
 // without a scale to move) rereads group 0 into a 1 KB area nobody reads, so every step
 // still issues the same loads.
-enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp = 4, kScE8Pk = 5 };
+// kScE8E8: UE8M0 column-major activation scales and UE8M0 weight-block scales, both applied
+// by the scaled MFMA, so BLOCK128 needs no fold (accumulation runs in the matrix core)
+enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp = 4, kScE8Pk = 5, kScE8E8 = 6 };
 
 // LDS layout of the direct-to-LDS kernel for tile shape C: kStages stages, each holding
 // both operand tiles of one K step and (per-step scale modes) the step's scales, followed
@@ -672,6 +674,10 @@ struct DmaRun {
   // weight-block scale alone, the same for every lane. P * 2^e * sb rounds exactly like
   // P * (2^e * sb), so the result is the same as folding the product of both scales.
   static constexpr bool E8 = SCM == kScE8Col || SCM == kScE8Pk;
+  // UE8M0 scales on both sides: the weight-block byte (one per wave and step) goes to the
+  // matrix core with the activation bytes, and the products accumulate with no fold
+  static constexpr bool E8W = SCM == kScE8E8;
+  static constexpr bool NOFOLD = MX || E8W;
   static constexpr int SM = C::SM, SN = C::SN;
   static_assert((C::BM == 256 || C::BM == 128) && SN == 4 && C::WTN == 64, "64-wide wave tiles");
   static constexpr int kW = C::kWaves;
@@ -760,7 +766,14 @@ struct DmaRun {
       return;
     }
     const uint8_t* sc = stage(st) + L::kScOff;
-    if constexpr (MX) {
+    if constexpr (E8W) {
+#pragma unroll
+      for (int i = 0; i < SM; i++) ea[i] = sc[wm * C::WTM + i * 16 + (lane & 15)];
+      // the weight block's word of K blocks 4(kb/4) .. +3 (the same for every lane)
+      const uint32_t w = sc[1024 + ((wn * C::WTN) / 128) * 256 + (kb & 3)];
+#pragma unroll
+      for (int j = 0; j < SN; j++) eb[j] = w;
+    } else if constexpr (MX) {
 #pragma unroll
       for (int i = 0; i < SM; i++) ea[i] = sc[4 * (wm * C::WTM + i * 16 + (lane & 15)) + (lane >> 4)];
 #pragma unroll
@@ -801,7 +814,7 @@ struct DmaRun {
   __device__ __forceinline__ void mf(const v8i& xf, const float (&f)[SM], const uint32_t (&eas)[SM],
                                      const uint32_t (&ebs)[SN]) {
     constexpr int i = T / 4, j = T % 4;
-    if constexpr (MX) {
+    if constexpr (NOFOLD) {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 0, 0, 0,
                                                                    static_cast<int>(ebs[j]), 0,
                                                                    static_cast<int>(eas[i]));
@@ -865,7 +878,7 @@ struct DmaRun {
   __device__ __forceinline__ void step(int kb) {
     constexpr int NX = (S + 1) % kStages;
     float f[SM];
-    if constexpr (!MX) {
+    if constexpr (!NOFOLD) {
       // two stages: the previous step's last two products move to the slots of MFMAs -2 and -1
       constexpr int s0 = (kPerStep - 2) % 3, s1 = (kPerStep - 1) % 3;
       if constexpr (kLag == 2 && kStages == 2 && (s0 != 1 || s1 != 2)) {
@@ -893,11 +906,11 @@ struct DmaRun {
     // and every step keeps the same load count and no branch.
     issue(S, min(kb + kStages, nkb - 1));
     uint32_t ea_c[SM], eb_c[SN];
-    if constexpr (MX || E8) {
+    if constexpr (MX || E8 || E8W) {
 #pragma unroll
       for (int i = 0; i < SM; i++) ea_c[i] = ea[i];
     }
-    if constexpr (MX) {
+    if constexpr (NOFOLD) {
 #pragma unroll
       for (int j = 0; j < SN; j++) eb_c[j] = eb[j];
     }
@@ -908,7 +921,7 @@ struct DmaRun {
     load_scales(NX, kb + 1);
     __builtin_amdgcn_sched_barrier(0);
     row<S, NX, SM - 1>(xs[SM - 1], f, ea_c, eb_c);
-    if constexpr (!MX) pend_s = f[SM - 1];
+    if constexpr (!NOFOLD) pend_s = f[SM - 1];
   }
 };
 
@@ -970,7 +983,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_step[q] = p.sa_sk * 4;
         r.s_lds[q] = js * 256;
       }
-    } else if constexpr (SCM == kScE8Col) {
+    } else if constexpr (SCM == kScE8Col || SCM == kScE8E8) {
       if (js == 0) {  // the 4 bytes of tile rows 4*lane .. 4*lane + 3 (clamped to the last full word)
         const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + t.e * p.sa_se + t.row0;  // (row0 % 4 == 0)
         r.s_base[q] = SA + m0;
@@ -978,7 +991,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_step[q] = p.sa_sk;
         r.s_lds[q] = 0;
       }
-    } else {
+    } else if constexpr (SCM == kScMx || SCM == kScMxGrp) {
       // E8M0 word (K blocks 4kb..4kb+3) of a row: bytes 4kb.. of a row-major byte row, or
       // word (row, kb) of packed scales (strides in words; with column-major words the 64
       // lanes of a job read 256 contiguous bytes instead of 64 rows' worth of lines)
@@ -998,6 +1011,19 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_off[q] = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * b_row);
         r.s_step[q] = b_step;
         r.s_lds[q] = 1024 + (js - 4) * 256;
+      }
+    }
+    if constexpr (SCM == kScE8E8) {
+      // UE8M0 weight block nb of the tile: the word of its K blocks 4(kb/4) .. +3, moved
+      // every fourth step (every lane loads it) to [1024 + 256 nb, +256)
+      const int nb = js - 1;
+      if (nb >= 0 && nb < kNb) {
+        const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.we * p.sb_se;
+        r.s_base[q] = SB + min(n0 / 128 + nb, nmax / 128) * p.sb_sn;
+        r.s_off[q] = 0;
+        r.s_step[q] = 4;
+        r.s_shift[q] = 2;
+        r.s_lds[q] = 1024 + 256 * nb;
       }
     }
     if constexpr (SCM == kScF32Row || SCM == kScE8Col || SCM == kScE8Pk) {
@@ -1089,7 +1115,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
       if (kb + 1 < nkb) r.template step<1>(kb + 1);
     }
   }
-  if constexpr (!R::MX) {  // the last step's last two folds are still pending
+  if constexpr (!R::NOFOLD) {  // the last step's last folds are still pending
     const int s_last = (nkb - 1) % R::kStages;
     if (s_last == 0) r.template drain<0>();
     else if (s_last == 1) r.template drain<1>();
@@ -1499,7 +1525,16 @@ int dma_mode(const GemmParams& p, bool mx) {
     return kScMx;
   }
   const int64_t E = (p.masked_m || p.seg_indptr) ? p.E : 1;  // groups in the device tile list
-  if (p.sb_fmt != FP8Q_SCALE_F32) return -1;
+  if (p.sb_fmt != FP8Q_SCALE_F32) {
+    // UE8M0 weight-block bytes, row-major [N/128][K/128] in whole 4-byte words (per weight),
+    // with UE8M0 column-major activation scales: both go to the matrix core
+    const bool w8 = p.sb_fmt == FP8Q_SCALE_UE8M0 && !p.sa_packed && p.sa_fmt == FP8Q_SCALE_UE8M0 && p.sb_sk == 1 &&
+                    p.sb_sn % 4 == 0 && p.sb_sn < (int64_t(1) << 30) && (p.K / BK) % 4 == 0 && u32_ok(p.sb) &&
+                    (E == 1 || p.sb_se % 4 == 0);
+    const bool col = p.sa_sm == 1 && p.sa_sk % 4 == 0 && p.M % 4 == 0 && u32_ok(p.sa) && !p.seg_indptr &&
+                     (p.masked_m == nullptr || p.sa_se % 4 == 0) && E <= DmaLayout<kScE8E8, DmaCfg>::kMaxPrefix;
+    return w8 && col ? kScE8E8 : -1;
+  }
   if (p.sa_packed)
     return p.sa_sm < (int64_t(1) << 22) && E <= DmaLayout<kScE8Pk, DmaCfg>::kMaxPrefix ? kScE8Pk : -1;
   if (p.sa_fmt == FP8Q_SCALE_F32) {
@@ -1569,20 +1604,22 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   const int dm = dma_mode(p, false);
   if (p.m_indices && dm < 0)
     return fail(FP8Q_EUNSUPPORTED, "block-scaled contiguous grouped GEMM: activation scales must be fp32, UE8M0 "
-                                   "column-major (rows a multiple of 4) or packed UE8M0 words, weight scales fp32");
-  if ((p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScE8Pk)) || (p.seg_indptr && dm >= 0) ||
-      p.m_indices) {
+                                   "column-major (rows a multiple of 4) or packed UE8M0 words with fp32 weight "
+                                   "scales, or UE8M0 column-major with UE8M0 weight scales in whole 4-byte words");
+  if ((p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScE8Pk || dm == kScE8E8)) ||
+      (p.seg_indptr && dm >= 0) || p.m_indices) {
     // grouped: 128-row tiles pad a group's rows to a multiple of 128 instead of 256 (and
     // are the aligned blocks of the contiguous layout)
     using T = DmaCfgT;
     const int g = grid_for(tiles_for(T::BM, T::BN));
     if (dm == kScE8Col) launch_dma<kScE8Col, T>(p, g, stream);
+    else if (dm == kScE8E8) launch_dma<kScE8E8, T>(p, g, stream);
     else if (dm == kScE8Pk) launch_dma<kScE8Pk, T>(p, g, stream);
     else if (dm == kScF32Grp) launch_dma<kScF32Grp, T>(p, g, stream);
     else launch_dma<kScF32Row, T>(p, g, stream);
     return finish("block-scaled grouped GEMM launch");
   }
-  if (!grouped && (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp || dm == kScE8Pk)) {
+  if (!grouped && (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp || dm == kScE8Pk || dm == kScE8E8)) {
     // 256x256 tiles halve the operand bytes each tile loads per output; used when they
     // still give every CU a tile
     using W = DmaCfgW;
@@ -1590,6 +1627,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
     if (wt >= kCUs) {
       auto wide = [&](const GemmParams& q, int64_t tiles) {
         if (dm == kScE8Col) launch_dma<kScE8Col, W>(q, grid_for(tiles), stream);
+        else if (dm == kScE8E8) launch_dma<kScE8E8, W>(q, grid_for(tiles), stream);
         else if (dm == kScE8Pk) launch_dma<kScE8Pk, W>(q, grid_for(tiles), stream);
         else if (dm == kScF32Grp) launch_dma<kScF32Grp, W>(q, grid_for(tiles), stream);
         else launch_dma<kScF32Row, W>(q, grid_for(tiles), stream);
@@ -1611,6 +1649,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
       using T = DmaCfgT;
       const int g = grid_for(((p.M + T::BM - 1) / T::BM) * ((p2.N + T::BN - 1) / T::BN));
       if (dm == kScE8Col) launch_dma<kScE8Col, T>(p2, g, stream);
+      else if (dm == kScE8E8) launch_dma<kScE8E8, T>(p2, g, stream);
       else if (dm == kScE8Pk) launch_dma<kScE8Pk, T>(p2, g, stream);
       else if (dm == kScF32Grp) launch_dma<kScF32Grp, T>(p2, g, stream);
       else launch_dma<kScF32Row, T>(p2, g, stream);
@@ -1620,6 +1659,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   if (dm == kScF32Row) launch_dma<kScF32Row>(p, grid, stream);
   else if (dm == kScF32Grp) launch_dma<kScF32Grp>(p, grid, stream);
   else if (dm == kScE8Col) launch_dma<kScE8Col>(p, grid, stream);
+  else if (dm == kScE8E8) launch_dma<kScE8E8>(p, grid, stream);
   else if (dm == kScE8Pk) launch_dma<kScE8Pk>(p, grid, stream);
   else if (a8 && b8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid, stream);
   else if (a8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, grid, stream);

@@ -137,6 +137,58 @@ def test_wide_tiles_one_round_ragged_sampled(sa_kind):
     check(y[ms, ns], ys, ss, K, f"wide one round {sa_kind}")
 
 
+# UE8M0 weight-block scales with UE8M0 column-major activation scales (K a multiple of 512)
+# go to the matrix core on both sides with no fold: narrow tiles, 256x256 tiles with the
+# column split of a partly empty last round, masked experts; K = 640 keeps the
+# register-staged kernel.
+def _ue8m0_weights(w, seed):
+    b, sbf = synth.weights(w)
+    return b, synth.e8m0_exponents(seed, sbf.shape[0], sbf.shape[1], lo=-4, hi=4, tensor_id=98)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 512), (4000, 4200, 1024), (136, 1000, 2048), (260, 384, 640)])
+def test_ue8m0_weight_scales(M, N, K):
+    w = synth.Workload("e8", seed=64, M=M, K=K, N=N, scale_fmt="ue8m0")
+    a, sa = synth.gemm_activation(w)
+    b, sb = _ue8m0_weights(w, 64)
+    sa_col = np.ascontiguousarray(sa.T)
+    y = _gpu_block(a, sa_col, b, sb, "col")
+    assert not np.any(y == SENT)
+    g = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(0, M, 127), g.integers(0, M, 30)]))
+    cols = np.unique(np.concatenate([[0, N - 1], np.arange(0, N, 127), g.integers(0, N, 30)]))
+    ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
+    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", oracle.SCALE_UE8M0, at=(ms, ns))
+    check(y[ms, ns], ys, ss, K, f"ue8m0 weights {M}x{N}x{K}")
+
+
+def test_ue8m0_weight_scales_masked():
+    E, cap, N, K = 5, 300, 384, 1024
+    a, sa, b, _ = _masked_operands(E, cap, N, K, 65)
+    sb = synth.e8m0_exponents(65, E * (N // 128), K // 128, lo=-4, hi=4, tensor_id=97).reshape(E, N // 128, K // 128)
+    mm = np.array([300, 0, 129, 7, 256], dtype=np.int32)
+    y = _gpu_masked(a, sa, b, sb, mm)
+    for e in range(E):
+        r = mm[e]
+        if r > 0:
+            ys, ss = oracle.gemm_block128(a[e, :r], np.ascontiguousarray(sa[e][:, :r]), b[e], sb[e],
+                                          oracle.SCALE_UE8M0, "col", oracle.SCALE_UE8M0)
+            check(y[e, :r], ys, ss, K, f"expert {e}")
+        assert np.all(y[e, r:] == SENT), f"expert {e}: rows past masked_m written"
+
+
+def test_ue8m0_weight_scales_dense_m4096_sampled():
+    w = synth.dense(4096)
+    a, sa = synth.gemm_activation(w)
+    b, sb = _ue8m0_weights(w, 66)
+    sa_col = np.ascontiguousarray(sa.T)
+    y = _gpu_block(a, sa_col, b, sb, "col")
+    ms, ns = _sample(w.M, w.N, 3000, 12)
+    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", oracle.SCALE_UE8M0, at=(ms, ns))
+    check(y[ms, ns], ys, ss, w.K, "dense M=4096, UE8M0 weight scales")
+    assert not np.any(y == SENT)
+
+
 def test_padded_output_rows_untouched():
     w = synth.Workload("t", seed=50, M=70, K=256, N=130, scale_fmt="f32")
     a, sa = synth.gemm_activation(w)
@@ -749,6 +801,21 @@ def test_moe_packed_rows_workload_sampled(layout):
     check(np.concatenate(y_all), np.concatenate(ys_all), np.concatenate(s_all), K, f"{layout} moe experts")
     if layout == "contiguous":
         assert np.all(yg[mi < 0] == SENT), "padding rows were written"
+
+
+def test_contiguous_ue8m0_weight_scales():
+    T, N, K, W = 640, 300, 1024, 3
+    a, sa, b, sbf = _grouped_operands(T, N, K, W, 72, "ue8m0")
+    sb = synth.e8m0_exponents(72, W * sbf.shape[1], sbf.shape[2], lo=-4, hi=4, tensor_id=96).reshape(sbf.shape)
+    mi = _contiguous_indices()
+    f = fq()
+    y = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
+    f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, "ue8m0-col"), _dev(b), _dev(sb), y.view(torch.bfloat16),
+                                   _dev(mi))
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy().view(np.uint16)
+    Y, S = oracle.gemm_contiguous(a, sa, oracle.SCALE_UE8M0, b, sb, mi, sb_fmt=oracle.SCALE_UE8M0)
+    _check_rows(yg, Y, S, K, "contiguous, UE8M0 weight scales")
 
 
 def test_contiguous_unsupported_scale_layout_writes_nothing():
