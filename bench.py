@@ -202,9 +202,10 @@ def run(args) -> dict:
         "config": {"workload": w.name, "M": M, "K": K, "N": N, "group_size": G,
                    "act_scale": f"{w.scale_fmt} {w.layout}-major", "weight_scale": "fp32 128x128",
                    "buffer_sets": nsets, "silu": w.silu},
-        # the GEMM's average launch duration inside the step loop
-        "roofline": {"bound": "mfma", "achieved": round(gemm_step_tflops, 2), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_step_tflops / PEAK_FP8_TFLOPS, 4),
+        # the GEMM's average launch duration in its own loop of K back-to-back launches (no
+        # events between launches; this is the figure that matches the kernel trace)
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic},
         "kernels": {
             "group_quant": {"avg_ms_in_steps": round(quant_in_step, 5), "avg_ms": round(quant_ms, 5),
@@ -213,6 +214,7 @@ def run(args) -> dict:
                             "traffic": _measured_traffic("quant.hip", w.name)},
             "gemm_blockscaled": {"avg_ms_in_steps": round(gemm_in_step, 5), "avg_ms": round(gemm_ms, 5),
                                  "flops": flops, "TFLOP/s": round(gemm_tflops, 2),
+                                 "TFLOP/s_in_steps": round(gemm_step_tflops, 2),
                                  "frac_mfma": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)},
         },
     }
