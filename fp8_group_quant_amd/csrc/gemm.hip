@@ -1530,7 +1530,7 @@ int dma_mode(const GemmParams& p, bool mx) {
     // with UE8M0 column-major activation scales: both go to the matrix core
     const bool w8 = p.sb_fmt == FP8Q_SCALE_UE8M0 && !p.sa_packed && p.sa_fmt == FP8Q_SCALE_UE8M0 && p.sb_sk == 1 &&
                     p.sb_sn % 4 == 0 && p.sb_sn < (int64_t(1) << 30) && (p.K / BK) % 4 == 0 && u32_ok(p.sb) &&
-                    (E == 1 || p.sb_se % 4 == 0);
+                    ((E == 1 && p.W <= 1) || p.sb_se % 4 == 0);
     const bool col = p.sa_sm == 1 && p.sa_sk % 4 == 0 && p.M % 4 == 0 && u32_ok(p.sa) && !p.seg_indptr &&
                      (p.masked_m == nullptr || p.sa_se % 4 == 0) && E <= DmaLayout<kScE8E8, DmaCfg>::kMaxPrefix;
     return w8 && col ? kScE8E8 : -1;

@@ -816,6 +816,17 @@ def test_contiguous_ue8m0_weight_scales():
     yg = y.cpu().numpy().view(np.uint16)
     Y, S = oracle.gemm_contiguous(a, sa, oracle.SCALE_UE8M0, b, sb, mi, sb_fmt=oracle.SCALE_UE8M0)
     _check_rows(yg, Y, S, K, "contiguous, UE8M0 weight scales")
+    # a weight stride of the UE8M0 scales that is not a whole number of words is refused
+    Wn, nb, kb = sb.shape
+    store = torch.zeros(Wn * (nb * kb + 2), dtype=torch.uint8, device="cuda")
+    sb_odd = store.as_strided((Wn, nb, kb), (nb * kb + 2, kb, 1))
+    y2 = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
+    with pytest.raises(f.Fp8qError) as ei:
+        f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, "ue8m0-col"), _dev(b), sb_odd, y2.view(torch.bfloat16),
+                                       _dev(mi))
+    assert ei.value.status == f.EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(y2 == SENT_I16)
 
 
 def test_contiguous_unsupported_scale_layout_writes_nothing():
