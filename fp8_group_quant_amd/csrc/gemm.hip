@@ -608,7 +608,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 // still issues the same loads.
 // kScE8E8: UE8M0 column-major activation scales and UE8M0 weight-block scales, both applied
 // by the scaled MFMA, so BLOCK128 needs no fold (accumulation runs in the matrix core)
-enum ScaleMode { kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp = 4, kScE8Pk = 5, kScE8E8 = 6 };
+// kScPkE8: the same with the activation scales as packed UE8M0 words
+enum ScaleMode {
+  kScF32Row = 0, kScE8Col = 1, kScMx = 2, kScF32Grp = 3, kScMxGrp = 4, kScE8Pk = 5, kScE8E8 = 6, kScPkE8 = 7
+};
 
 // LDS layout of the direct-to-LDS kernel for tile shape C: kStages stages, each holding
 // both operand tiles of one K step and (per-step scale modes) the step's scales, followed
@@ -676,7 +679,7 @@ struct DmaRun {
   static constexpr bool E8 = SCM == kScE8Col || SCM == kScE8Pk;
   // UE8M0 scales on both sides: the weight-block byte (one per wave and step) goes to the
   // matrix core with the activation bytes, and the products accumulate with no fold
-  static constexpr bool E8W = SCM == kScE8E8;
+  static constexpr bool E8W = SCM == kScE8E8 || SCM == kScPkE8;
   static constexpr bool NOFOLD = MX || E8W;
   static constexpr int SM = C::SM, SN = C::SN;
   static_assert((C::BM == 256 || C::BM == 128) && SN == 4 && C::WTN == 64, "64-wide wave tiles");
@@ -768,7 +771,10 @@ struct DmaRun {
     const uint8_t* sc = stage(st) + L::kScOff;
     if constexpr (E8W) {
 #pragma unroll
-      for (int i = 0; i < SM; i++) ea[i] = sc[wm * C::WTM + i * 16 + (lane & 15)];
+      for (int i = 0; i < SM; i++) {
+        const int row = wm * C::WTM + i * 16 + (lane & 15);
+        ea[i] = SCM == kScPkE8 ? sc[4 * row + (kb & 3)] : sc[row];  // packed: the row's word of 4 K blocks
+      }
       // the weight block's word of K blocks 4(kb/4) .. +3 (the same for every lane)
       const uint32_t w = sc[1024 + ((wn * C::WTN) / 128) * 256 + (kb & 3)];
 #pragma unroll
@@ -964,7 +970,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
     r.s_step[q] = 0;
     r.s_shift[q] = 0;
     r.s_lds[q] = R::L::kSpare;
-    if constexpr (SCM == kScE8Pk) {
+    if constexpr (SCM == kScE8Pk || SCM == kScPkE8) {
       if (js < 4) {  // packed word (K blocks 4(kb/4)..+3) of tile row 64 js + lane
         const uint8_t* SA = static_cast<const uint8_t*>(p.sa) + (t.e * p.sa_se + t.row0 * p.sa_sm) * 4;
         const int row = js * 64 + lane;
@@ -1013,10 +1019,10 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
         r.s_lds[q] = 1024 + (js - 4) * 256;
       }
     }
-    if constexpr (SCM == kScE8E8) {
+    if constexpr (SCM == kScE8E8 || SCM == kScPkE8) {
       // UE8M0 weight block nb of the tile: the word of its K blocks 4(kb/4) .. +3, moved
       // every fourth step (every lane loads it) to [1024 + 256 nb, +256)
-      const int nb = js - 1;
+      const int nb = js - (SCM == kScE8E8 ? 1 : 4);
       if (nb >= 0 && nb < kNb) {
         const uint8_t* SB = static_cast<const uint8_t*>(p.sb) + t.we * p.sb_se;
         r.s_base[q] = SB + min(n0 / 128 + nb, nmax / 128) * p.sb_sn;
@@ -1531,6 +1537,12 @@ int dma_mode(const GemmParams& p, bool mx) {
     const bool w8 = p.sb_fmt == FP8Q_SCALE_UE8M0 && !p.sa_packed && p.sa_fmt == FP8Q_SCALE_UE8M0 && p.sb_sk == 1 &&
                     p.sb_sn % 4 == 0 && p.sb_sn < (int64_t(1) << 30) && (p.K / BK) % 4 == 0 && u32_ok(p.sb) &&
                     ((E == 1 && p.W <= 1) || p.sb_se % 4 == 0);
+    if (p.sa_packed) {
+      const bool w8p = p.sb_fmt == FP8Q_SCALE_UE8M0 && p.sb_sk == 1 && p.sb_sn % 4 == 0 &&
+                       p.sb_sn < (int64_t(1) << 30) && (p.K / BK) % 4 == 0 && u32_ok(p.sb) &&
+                       ((E == 1 && p.W <= 1) || p.sb_se % 4 == 0);
+      return w8p && p.sa_sm < (int64_t(1) << 22) && E <= DmaLayout<kScPkE8, DmaCfg>::kMaxPrefix ? kScPkE8 : -1;
+    }
     const bool col = p.sa_sm == 1 && p.sa_sk % 4 == 0 && p.M % 4 == 0 && u32_ok(p.sa) && !p.seg_indptr &&
                      (p.masked_m == nullptr || p.sa_se % 4 == 0) && E <= DmaLayout<kScE8E8, DmaCfg>::kMaxPrefix;
     return w8 && col ? kScE8E8 : -1;
@@ -1605,8 +1617,9 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   if (p.m_indices && dm < 0)
     return fail(FP8Q_EUNSUPPORTED, "block-scaled contiguous grouped GEMM: activation scales must be fp32, UE8M0 "
                                    "column-major (rows a multiple of 4) or packed UE8M0 words with fp32 weight "
-                                   "scales, or UE8M0 column-major with UE8M0 weight scales in whole 4-byte words");
-  if ((p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScE8Pk || dm == kScE8E8)) ||
+                                   "scales, or UE8M0 column-major or packed with UE8M0 weight scales in whole "
+                                   "4-byte words");
+  if ((p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScE8Pk || dm == kScE8E8 || dm == kScPkE8)) ||
       (p.seg_indptr && dm >= 0) || p.m_indices) {
     // grouped: 128-row tiles pad a group's rows to a multiple of 128 instead of 256 (and
     // are the aligned blocks of the contiguous layout)
@@ -1614,12 +1627,14 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
     const int g = grid_for(tiles_for(T::BM, T::BN));
     if (dm == kScE8Col) launch_dma<kScE8Col, T>(p, g, stream);
     else if (dm == kScE8E8) launch_dma<kScE8E8, T>(p, g, stream);
+    else if (dm == kScPkE8) launch_dma<kScPkE8, T>(p, g, stream);
     else if (dm == kScE8Pk) launch_dma<kScE8Pk, T>(p, g, stream);
     else if (dm == kScF32Grp) launch_dma<kScF32Grp, T>(p, g, stream);
     else launch_dma<kScF32Row, T>(p, g, stream);
     return finish("block-scaled grouped GEMM launch");
   }
-  if (!grouped && (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp || dm == kScE8Pk || dm == kScE8E8)) {
+  if (!grouped &&
+      (dm == kScE8Col || dm == kScF32Row || dm == kScF32Grp || dm == kScE8Pk || dm == kScE8E8 || dm == kScPkE8)) {
     // 256x256 tiles halve the operand bytes each tile loads per output; used when they
     // still give every CU a tile
     using W = DmaCfgW;
@@ -1628,6 +1643,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
       auto wide = [&](const GemmParams& q, int64_t tiles) {
         if (dm == kScE8Col) launch_dma<kScE8Col, W>(q, grid_for(tiles), stream);
         else if (dm == kScE8E8) launch_dma<kScE8E8, W>(q, grid_for(tiles), stream);
+        else if (dm == kScPkE8) launch_dma<kScPkE8, W>(q, grid_for(tiles), stream);
         else if (dm == kScE8Pk) launch_dma<kScE8Pk, W>(q, grid_for(tiles), stream);
         else if (dm == kScF32Grp) launch_dma<kScF32Grp, W>(q, grid_for(tiles), stream);
         else launch_dma<kScF32Row, W>(q, grid_for(tiles), stream);
@@ -1650,6 +1666,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
       const int g = grid_for(((p.M + T::BM - 1) / T::BM) * ((p2.N + T::BN - 1) / T::BN));
       if (dm == kScE8Col) launch_dma<kScE8Col, T>(p2, g, stream);
       else if (dm == kScE8E8) launch_dma<kScE8E8, T>(p2, g, stream);
+      else if (dm == kScPkE8) launch_dma<kScPkE8, T>(p2, g, stream);
       else if (dm == kScE8Pk) launch_dma<kScE8Pk, T>(p2, g, stream);
       else if (dm == kScF32Grp) launch_dma<kScF32Grp, T>(p2, g, stream);
       else launch_dma<kScF32Row, T>(p2, g, stream);
@@ -1660,6 +1677,7 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   else if (dm == kScF32Grp) launch_dma<kScF32Grp>(p, grid, stream);
   else if (dm == kScE8Col) launch_dma<kScE8Col>(p, grid, stream);
   else if (dm == kScE8E8) launch_dma<kScE8E8>(p, grid, stream);
+  else if (dm == kScPkE8) launch_dma<kScPkE8>(p, grid, stream);
   else if (dm == kScE8Pk) launch_dma<kScE8Pk>(p, grid, stream);
   else if (a8 && b8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid, stream);
   else if (a8) launch<C, false, FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, grid, stream);

@@ -254,10 +254,10 @@ int fp8q_grouped_gemm_segments(const uint8_t* a, int64_t lda,
  * (The layout this serves puts each expert's rows at a 128-aligned offset and pads them
  * with -1 to a multiple of 128.)
  * Activation scales: fp32 (any strides), UE8M0 column-major with T % 4 == 0, or
- * UE8M0_PACKED, with fp32 weight scales; or UE8M0 column-major activation scales with UE8M0
- * weight scales in row-major [N/128][K/128] rows of whole 4-byte words (K % 512 == 0,
- * sb_sn % 4 == 0, sb_se % 4 == 0, sb 4-byte aligned) [EUNSUPPORTED otherwise]. Other
- * requirements as above.
+ * UE8M0_PACKED, with fp32 weight scales; or UE8M0 column-major (T % 4 == 0) or UE8M0_PACKED
+ * activation scales with UE8M0 weight scales in row-major [N/128][K/128] rows of whole
+ * 4-byte words (K % 512 == 0, sb_sn % 4 == 0, sb_se % 4 == 0, sb 4-byte aligned)
+ * [EUNSUPPORTED otherwise]. Other requirements as above.
  */
 int fp8q_grouped_gemm_contiguous(const uint8_t* a, int64_t lda,
                                  const void* sa, int sa_fmt, int64_t sa_sm, int64_t sa_sk,

@@ -162,6 +162,24 @@ def test_ue8m0_weight_scales(M, N, K):
     check(y[ms, ns], ys, ss, K, f"ue8m0 weights {M}x{N}x{K}")
 
 
+# The same with packed UE8M0 activation words (row- or column-major words): narrow tiles, the
+# 256x256 tiles with the column split, and the full dense shape
+@pytest.mark.parametrize("M,N,K", [(300, 260, 512), (4000, 4200, 1024), (136, 1000, 2048), (4096, 7168, 7168)])
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_packed_activation_ue8m0_weight_scales(M, N, K, layout):
+    w = synth.Workload("pe8", seed=67, M=M, K=K, N=N, scale_fmt="ue8m0")
+    a, sa = synth.gemm_activation(w)
+    b, sb = _ue8m0_weights(w, 67)
+    y = _gpu_block_packed(a, sa, b, sb, layout)
+    assert not np.any(y == SENT)
+    g = np.random.default_rng(M + N + K)
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(0, M, 127), g.integers(0, M, 30)]))
+    cols = np.unique(np.concatenate([[0, N - 1], np.arange(0, N, 127), g.integers(0, N, 30)]))
+    ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
+    ys, ss = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_UE8M0, "row", oracle.SCALE_UE8M0, at=(ms, ns))
+    check(y[ms, ns], ys, ss, K, f"packed {layout} words, ue8m0 weights {M}x{N}x{K}")
+
+
 def test_ue8m0_weight_scales_masked():
     E, cap, N, K = 5, 300, 384, 1024
     a, sa, b, _ = _masked_operands(E, cap, N, K, 65)
@@ -570,8 +588,8 @@ def _gpu_block_packed(a, sa_bytes, b, sb, layout):
 
 
 # Packed activation scales (four K blocks per word; K a multiple of 512) on every path: the
-# small-M kernel (M <= 128), the register-staged kernel (UE8M0 weight scales), the
-# direct-to-LDS 256x128 kernel with ragged M, N.
+# small-M kernel (M <= 128) and the direct-to-LDS 256x128 kernel with ragged M, N (fp32
+# weight scales folded, UE8M0 weight scales on the matrix core).
 @pytest.mark.parametrize("M,N,K", [(1, 256, 512), (100, 200, 1024), (130, 136, 512), (260, 300, 1024)])
 @pytest.mark.parametrize("layout", ["row", "col"])
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
@@ -600,8 +618,8 @@ def test_packed_activation_scales_wide_sampled():
     check(y[ms, ns], ys, ss, K, "packed wide")
 
 
-# fp32 weight scales: the 128x256 kernel; UE8M0 weight scales: the register-staged kernel,
-# whose expert offset into packed words counts 4 bytes per word
+# The 128x256 kernel with fp32 (folded) or UE8M0 (matrix-core) weight scales; the expert
+# offset into packed words counts 4 bytes per word
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
 def test_packed_activation_scales_masked(sb_kind):
     E, cap, N, K = 5, 200, 384, 512
@@ -690,8 +708,8 @@ def _check_rows(yg, Y, S, K, what):
 
 
 # fp32 row scales with K % 512 == 0 take the 128x256 kernel with four-step scale groups, fp32
-# column scales its per-step loads, packed words their per-step word loads; UE8M0 bytes and
-# UE8M0 weight scales the register-staged kernel (segments start at any row).
+# column scales its per-step loads, packed words their per-step word loads (with either
+# weight-scale format); UE8M0 bytes the register-staged kernel (segments start at any row).
 @pytest.mark.parametrize("kind", ["f32-row", "f32-col", "packed-col", "packed-row", "ue8m0-col"])
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
 def test_segments_full(kind, sb_kind):
@@ -803,26 +821,27 @@ def test_moe_packed_rows_workload_sampled(layout):
         assert np.all(yg[mi < 0] == SENT), "padding rows were written"
 
 
-def test_contiguous_ue8m0_weight_scales():
+@pytest.mark.parametrize("kind", ["ue8m0-col", "packed-col", "packed-row"])
+def test_contiguous_ue8m0_weight_scales(kind):
     T, N, K, W = 640, 300, 1024, 3
     a, sa, b, sbf = _grouped_operands(T, N, K, W, 72, "ue8m0")
     sb = synth.e8m0_exponents(72, W * sbf.shape[1], sbf.shape[2], lo=-4, hi=4, tensor_id=96).reshape(sbf.shape)
     mi = _contiguous_indices()
     f = fq()
     y = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
-    f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, "ue8m0-col"), _dev(b), _dev(sb), y.view(torch.bfloat16),
+    f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, kind), _dev(b), _dev(sb), y.view(torch.bfloat16),
                                    _dev(mi))
     torch.cuda.synchronize()
     yg = y.cpu().numpy().view(np.uint16)
     Y, S = oracle.gemm_contiguous(a, sa, oracle.SCALE_UE8M0, b, sb, mi, sb_fmt=oracle.SCALE_UE8M0)
-    _check_rows(yg, Y, S, K, "contiguous, UE8M0 weight scales")
+    _check_rows(yg, Y, S, K, f"contiguous {kind}, UE8M0 weight scales")
     # a weight stride of the UE8M0 scales that is not a whole number of words is refused
     Wn, nb, kb = sb.shape
     store = torch.zeros(Wn * (nb * kb + 2), dtype=torch.uint8, device="cuda")
     sb_odd = store.as_strided((Wn, nb, kb), (nb * kb + 2, kb, 1))
     y2 = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
     with pytest.raises(f.Fp8qError) as ei:
-        f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, "ue8m0-col"), _dev(b), sb_odd, y2.view(torch.bfloat16),
+        f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, kind), _dev(b), sb_odd, y2.view(torch.bfloat16),
                                        _dev(mi))
     assert ei.value.status == f.EUNSUPPORTED
     torch.cuda.synchronize()
