@@ -1178,7 +1178,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_dma_kernel(GemmParams p) 
 // goes to wave kb % 4) and the four partial sums are added through LDS at the end.
 // BLOCK128 only. Two variants: the kernel below loads MFMA fragments straight from global
 // memory into registers, U blocks ahead (any scale layout); the LDS-staged one after it
-// (fp32 weight-block scales) moves whole cache lines and is about twice as fast.
+// moves whole cache lines and is about twice as fast (used whenever its tables fit LDS).
 constexpr int kSkinnyThreads = 256;
 constexpr int64_t kSkinnyMaxM = 128;  // at most 8 m subtiles
 
@@ -1286,7 +1286,7 @@ __global__ __launch_bounds__(kSkinnyThreads) void gemm_skinny_kernel(GemmParams 
 // A wave only reads its own stages, so the K loop needs no barrier: the wave's own
 // vmcnt wait makes a stage readable, and its own LDS reads complete before it refills
 // the stage. The activation scales of the workgroup ([K/128][MR]) and the weight-block
-// scales ([K/128]) are read into LDS tables before the loop, so the loop issues no other
+// scales ([K/128], as fp32) are read into LDS tables before the loop, so the loop issues no other
 // vector-memory instruction and the vmcnt counts are exact. Fragment reads use the same
 // XOR swizzle as the large kernels. The result equals the register-loading kernel's bit
 // for bit (same per-wave block order and reduction order).
@@ -1389,7 +1389,11 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void gemm_skinny_dma_kernel(Gemm
       }
     }
     const int64_t nb = n0 / 128;
-    for (int kb = tid; kb < nkb; kb += kSkinnyThreads) sb_tab[kb] = static_cast<const float*>(p.sb)[nb * p.sb_sn + kb * p.sb_sk];
+    for (int kb = tid; kb < nkb; kb += kSkinnyThreads) {
+      const int64_t bi = nb * p.sb_sn + kb * p.sb_sk;
+      sb_tab[kb] = p.sb_fmt == FP8Q_SCALE_F32 ? static_cast<const float*>(p.sb)[bi]
+                                              : scale_value<FP8Q_SCALE_UE8M0>(static_cast<const uint8_t*>(p.sb)[bi]);
+    }
   }
   __syncthreads();
   const uint8_t* ring_p = smem + wave * KS * D::kStage;
@@ -1474,10 +1478,11 @@ int launch_skinny_dma(const GemmParams& p, size_t lds, hipStream_t s) {
   return 0;
 }
 
-// The LDS-staged small-M kernel when its scale tables and rings fit (fp32 weight-block
-// scales; any activation-scale layout); returns false to use the register-loading one.
+// The LDS-staged small-M kernel when its scale tables and rings fit (any BLOCK128 scale
+// layout; weight-block scales decoded to fp32 in its table); returns false to use the
+// register-loading one.
 bool try_skinny_dma(const GemmParams& p, hipStream_t s) {
-  if (p.sb_fmt != FP8Q_SCALE_F32 || p.lda >= (int64_t(1) << 25) || p.ldb >= (int64_t(1) << 28)) return false;
+  if (p.lda >= (int64_t(1) << 25) || p.ldb >= (int64_t(1) << 28)) return false;
   const int sm = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : (p.M <= 64 ? 4 : 8));
   const size_t lds = skinny_dma_lds(sm, p.sa_fmt, p.K / BK);
   if (lds > 160 * 1024) return false;

@@ -180,6 +180,25 @@ def test_packed_activation_ue8m0_weight_scales(M, N, K, layout):
     check(y[ms, ns], ys, ss, K, f"packed {layout} words, ue8m0 weights {M}x{N}x{K}")
 
 
+# Small M (the LDS-staged split-K kernel) with UE8M0 weight-block scales, decoded to fp32 in
+# its table, under each activation-scale layout; N ragged
+@pytest.mark.parametrize("M", [1, 16, 33, 100, 128])
+@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-row", "ue8m0-col", "packed-col"])
+def test_small_m_ue8m0_weight_scales(M, sa_kind):
+    N, K = 300, 1024
+    w = synth.Workload("sm8", seed=68 + M, M=M, K=K, N=N, scale_fmt="f32" if sa_kind.startswith("f32") else "ue8m0")
+    a, sa = synth.gemm_activation(w)
+    b, sb = _ue8m0_weights(w, 68)
+    if sa_kind.startswith("packed"):
+        y = _gpu_block_packed(a, sa, b, sb, "col")
+    elif sa_kind.endswith("col"):
+        y = _gpu_block(a, np.ascontiguousarray(sa.T), b, sb, "col")
+    else:
+        y = _gpu_block(a, sa, b, sb)
+    ys, ss = oracle.gemm_block128(a, sa, b, sb, _fmt(sa), "row", oracle.SCALE_UE8M0)
+    check(y, ys, ss, K, f"small M={M} {sa_kind}, ue8m0 weights")
+
+
 def test_ue8m0_weight_scales_masked():
     E, cap, N, K = 5, 300, 384, 1024
     a, sa, b, _ = _masked_operands(E, cap, N, K, 65)
