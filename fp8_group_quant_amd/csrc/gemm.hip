@@ -1596,8 +1596,24 @@ int64_t wide_split_columns(const GemmParams& p) {
   return best < 0.97 * whole ? best_n1 : 0;
 }
 
-int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t stream) {
+// UE8M0 activation scales stored row-major ([rows][K/128] bytes, K % 512 == 0) whose rows
+// and expert blocks start on 4-byte boundaries are packed words under another name: byte kb
+// of row m is byte kb % 4 of word m * (sa_sm / 4) + kb / 4. They are read as such, which
+// gives them the direct-to-LDS kernel's per-row word loads.
+GemmParams rows_as_words(const GemmParams& p) {
+  GemmParams q = p;
+  if (!p.sa_packed && p.sa_fmt == FP8Q_SCALE_UE8M0 && p.sa_sk == 1 && p.sa_sm % 4 == 0 && p.sa_se % 4 == 0 &&
+      p.K % 512 == 0 && (reinterpret_cast<uintptr_t>(p.sa) & 3) == 0) {
+    q.sa_packed = 1;
+    q.sa_sm = p.sa_sm / 4;
+    q.sa_se = p.sa_se / 4;
+  }
+  return q;
+}
+
+int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t stream) {
   using C = Large;
+  const GemmParams p = rows_as_words(p_in);
   // launch sizing only (the device tile list decides the work): masked and segment launches
   // use the row hint; a segment adds at most one partial tile
   auto tiles_for = [&](int64_t bm, int64_t bn) -> int64_t {
@@ -1621,7 +1637,8 @@ int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t st
   const int dm = dma_mode(p, false);
   if (p.m_indices && dm < 0)
     return fail(FP8Q_EUNSUPPORTED, "block-scaled contiguous grouped GEMM: activation scales must be fp32, UE8M0 "
-                                   "column-major (rows a multiple of 4) or packed UE8M0 words with fp32 weight "
+                                   "column-major (rows a multiple of 4) or packed UE8M0 words (or row-major UE8M0 "
+                                   "rows of whole words) with fp32 weight "
                                    "scales, or UE8M0 column-major or packed with UE8M0 weight scales in whole "
                                    "4-byte words");
   if ((p.masked_m && (dm == kScE8Col || dm == kScF32Row || dm == kScE8Pk || dm == kScE8E8 || dm == kScPkE8)) ||

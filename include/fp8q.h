@@ -256,7 +256,9 @@ int fp8q_grouped_gemm_segments(const uint8_t* a, int64_t lda,
  * Activation scales: fp32 (any strides), UE8M0 column-major with T % 4 == 0, or
  * UE8M0_PACKED, with fp32 weight scales; or UE8M0 column-major (T % 4 == 0) or UE8M0_PACKED
  * activation scales with UE8M0 weight scales in row-major [N/128][K/128] rows of whole
- * 4-byte words (K % 512 == 0, sb_sn % 4 == 0, sb_se % 4 == 0, sb 4-byte aligned)
+ * 4-byte words (K % 512 == 0, sb_sn % 4 == 0, sb_se % 4 == 0, sb 4-byte aligned). UE8M0
+ * activation scales stored row-major (sa_sk == 1) in rows of whole 4-byte words
+ * (K % 512 == 0, sa_sm % 4 == 0, sa 4-byte aligned) count as UE8M0_PACKED words.
  * [EUNSUPPORTED otherwise]. Other requirements as above.
  */
 int fp8q_grouped_gemm_contiguous(const uint8_t* a, int64_t lda,

@@ -74,7 +74,7 @@ def test_tiny_workload_full():
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 130, 256), (129, 200, 384), (257, 300, 640),
                                    (64, 1024, 1024), (132, 136, 128), (264, 128, 256),
                                    (260, 300, 640), (516, 136, 384), (132, 136, 512), (260, 300, 1024)])
-@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col"])
+@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col", "ue8m0-row"])
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
 def test_ragged_shapes_full(M, N, K, sa_kind, sb_kind):
     w = synth.Workload("t", seed=40 + M, M=M, K=K, N=N, scale_fmt=sa_kind.split("-")[0])
@@ -96,7 +96,7 @@ def test_ragged_shapes_full(M, N, K, sa_kind, sb_kind):
 # groups. Outputs on a grid of rows x columns through tile and wave-tile boundaries plus
 # random ones are compared; every output must be written.
 @pytest.mark.parametrize("K", [128, 256, 384, 512, 1024])
-@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col"])
+@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col", "ue8m0-row"])
 def test_wide_tiles_ragged_sampled(K, sa_kind):
     M, N = 4000, 4200
     w = synth.Workload("t", seed=60 + K, M=M, K=K, N=N, scale_fmt=sa_kind.split("-")[0])
@@ -334,10 +334,11 @@ def test_masked_f32_row_scales():
 
 
 # Masked counts on both sides of every 128-row tile boundary up to the capacity, ragged N,
-# both per-step activation scale layouts.
-@pytest.mark.parametrize("sa_kind", ["ue8m0-col", "f32-row"])
+# both per-step activation scale layouts; UE8M0 row-major bytes with K = 1024 (rows of whole
+# words: read as packed words, per expert).
+@pytest.mark.parametrize("sa_kind", ["ue8m0-col", "f32-row", "ue8m0-row"])
 def test_masked_counts_across_tile_boundaries(sa_kind):
-    E, cap, N, K = 10, 700, 320, 256
+    E, cap, N, K = 10, 700, 320, (1024 if sa_kind == "ue8m0-row" else 256)
     fmt, layout = sa_kind.split("-")
     w = synth.Workload("m", seed=63, M=cap, K=K, N=N, E=E, scale_fmt=fmt, layout=layout, masked=True)
     ops = [synth.gemm_activation(w, e) + synth.weights(w, e) for e in range(E)]
@@ -729,7 +730,7 @@ def _check_rows(yg, Y, S, K, what):
 # fp32 row scales with K % 512 == 0 take the 128x256 kernel with four-step scale groups, fp32
 # column scales its per-step loads, packed words their per-step word loads (with either
 # weight-scale format); UE8M0 bytes the register-staged kernel (segments start at any row).
-@pytest.mark.parametrize("kind", ["f32-row", "f32-col", "packed-col", "packed-row", "ue8m0-col"])
+@pytest.mark.parametrize("kind", ["f32-row", "f32-col", "packed-col", "packed-row", "ue8m0-col", "ue8m0-row"])
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
 def test_segments_full(kind, sb_kind):
     T, N, K, W = 720, 300, 1024, 3
@@ -759,7 +760,7 @@ def _contiguous_indices():
     return mi
 
 
-@pytest.mark.parametrize("kind", ["f32-row", "ue8m0-col", "packed-col"])
+@pytest.mark.parametrize("kind", ["f32-row", "ue8m0-col", "packed-col", "ue8m0-row"])
 def test_contiguous_full(kind):
     T, N, K, W = 640, 300, 1024, 3
     a, sa, b, sb = _grouped_operands(T, N, K, W, 71, "f32" if kind.startswith("f32") else "ue8m0")
@@ -868,11 +869,12 @@ def test_contiguous_ue8m0_weight_scales(kind):
 
 
 def test_contiguous_unsupported_scale_layout_writes_nothing():
-    T, N, K, W = 256, 128, 512, 2
+    T, N, K, W = 256, 128, 640, 2
     a, sa, b, sb = _grouped_operands(T, N, K, W, 72, "ue8m0")
     f = fq()
     y = torch.full((T, N), SENT_I16, dtype=torch.int16, device="cuda")
-    with pytest.raises(f.Fp8qError) as ei:  # UE8M0 bytes row-major: not moved by the 128-row kernel
+    # UE8M0 bytes row-major in rows of 5 bytes (K % 512 != 0): not moved by the 128-row kernel
+    with pytest.raises(f.Fp8qError) as ei:
         f.fp8q_grouped_gemm_contiguous(_dev(a), _sa_dev(sa, "ue8m0-row"), _dev(b), _dev(sb), y.view(torch.bfloat16),
                                        _dev(np.zeros(T, dtype=np.int32)))
     assert ei.value.status == f.EUNSUPPORTED
