@@ -20,7 +20,8 @@
 //     slice and 32-wide K block are applied by the matrix core, and accumulation runs
 //     across the whole K loop inside the MFMA with no fold. BLOCK128 with UE8M0 activation
 //     scales uses it too, for the activation side only: the fold then multiplies by the
-//     fp32 weight-block scale, one value per wavefront.
+//     fp32 weight-block scale, one value per wavefront. With UE8M0 weight-block scales
+//     as well, both sides go to the matrix core and BLOCK128 needs no fold either.
 //   - K layout inside a lane (measured on gfx950): lane l of a 16x16x128 operand holds row
 //     l%16 and two 16-byte runs of K, at 16*(l/16) and 64 + 16*(l/16); the E8M0 scale for
 //     (row i, 32-wide block b) comes from lane i + 16*b.
@@ -35,7 +36,8 @@
 //     the next step's first operands read during the current step's last row (see
 //     "direct-to-LDS pipeline" below). Scale layouts it cannot move in aligned 4-byte
 //     pieces go to a register-staged kernel: loads issued two steps ahead into one of two
-//     register sets, written to one of two LDS stages.
+//     register sets, written to one of two LDS stages. (UE8M0 row-major activation rows of
+//     whole 4-byte words are read as packed words, so they stay on the main kernel.)
 //   - BLOCK128 fold pipeline: each MFMA product goes to a four-slot register ring and is
 //     folded three MFMAs later, so no fold waits on the MFMA it consumes and the fold's
 //     VALU work co-issues with the matrix core.
