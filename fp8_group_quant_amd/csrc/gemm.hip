@@ -729,13 +729,13 @@ struct DmaRun {
   v4f pr[kRingN];
   float pend_s;
 
-  // Two-stage pipelines (not grouped): a step's loads go out in two parts, the activation
-  // blocks right after the barrier two steps earlier and the weight blocks and scale job
-  // during the first two rows of the step before, so the texture path sees no burst of
-  // every wave's loads at once (3-4% faster on the large flat GEMMs than one burst after
-  // the barrier). The stage they fill is free from that barrier on, and the barrier of
-  // the step before waits for all of them (vmcnt 0) either way.
-  static constexpr bool kSplit = kStages == 2 && !L::kGrouped;
+  // Per-step scale modes (not grouped): the loads of step kb + kStages go out in two parts,
+  // the activation blocks right after the barrier of step kb (which frees the stage) and
+  // the weight blocks and scale job before rows 0 and 1 of step kb + 1, so the texture
+  // path sees no burst of every wave's loads at once (3-8% faster than one burst after the
+  // barrier). The wait before each barrier is unchanged: the loads issued after those of
+  // the step it needs are exactly one step's worth (none with two stages).
+  static constexpr bool kSplit = !L::kGrouped;
   static_assert(!kSplit || SM >= 3, "the weight loads go out before rows 0 and 1");
   __device__ __forceinline__ void issue_a(int st, int kb) {
     const uint32_t base = smem_lds + st * L::kStage;
@@ -893,7 +893,7 @@ struct DmaRun {
   }
   template <int S, int I>
   __device__ __forceinline__ void spread(int kb) {
-    if constexpr (kSplit && I < 2) issue_b<I>((S + 1) % kStages, min(kb + 1, nkb - 1));
+    if constexpr (kSplit && I < 2) issue_b<I>((S + kStages - 1) % kStages, min(kb + kStages - 1, nkb - 1));
   }
   template <int S, int I>
   __device__ __forceinline__ void pre(v8i (&xs)[SM]) {
@@ -1136,11 +1136,14 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
 
   const int nkb = r.nkb;
   r.issue(0, 0);
-  if constexpr (R::kSplit)
+  if constexpr (R::kSplit && R::kStages == 2)
     r.issue_a(1, min(1, nkb - 1));  // the rest of step 1 goes out during step 0's first rows
   else
     r.issue(1, min(1, nkb - 1));
-  if constexpr (R::kStages == 3) {
+  if constexpr (R::kStages == 3 && R::kSplit) {
+    r.issue_a(2, min(2, nkb - 1));  // the rest of step 2 goes out during step 0's first rows
+    wait_vmcnt<R::kGroup + R::kLA>();  // step 0 has landed
+  } else if constexpr (R::kStages == 3) {
     r.issue(2, min(2, nkb - 1));
     wait_vmcnt<2 * R::kGroup>();  // step 0 has landed; steps 1 and 2 may be in flight
   } else if constexpr (R::kSplit) {
