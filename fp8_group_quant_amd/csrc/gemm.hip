@@ -729,13 +729,16 @@ struct DmaRun {
   v4f pr[kRingN];
   float pend_s;
 
-  // Per-step scale modes (not grouped): the loads of step kb + kStages go out in two parts,
-  // the activation blocks right after the barrier of step kb (which frees the stage) and
-  // the weight blocks and scale job before rows 0 and 1 of step kb + 1, so the texture
-  // path sees no burst of every wave's loads at once (3-8% faster than one burst after the
-  // barrier). The wait before each barrier is unchanged: the loads issued after those of
-  // the step it needs are exactly one step's worth (none with two stages).
-  static constexpr bool kSplit = !L::kGrouped;
+  // The loads of step kb + kStages go out in two parts: the activation blocks right after
+  // the barrier of step kb (which frees the stage) and the weight blocks and the scale load
+  // before rows 0 and 1 of step kb + 1, so the texture path sees no burst of every wave's
+  // loads at once (3-8% faster than one burst after the barrier). The wait before each
+  // barrier is unchanged: the loads issued after those of the step it needs are exactly
+  // one step's worth (none with two stages). A grouped mode's four-step scale group still
+  // goes out after the barrier of the same step as before (the ring slot it fills is free
+  // from there) and has landed before the step that carries it, two steps before the
+  // group's first read.
+  static constexpr bool kSplit = true;
   static_assert(!kSplit || SM >= 3, "the weight loads go out before rows 0 and 1");
   __device__ __forceinline__ void issue_a(int st, int kb) {
     const uint32_t base = smem_lds + st * L::kStage;
@@ -750,11 +753,7 @@ struct DmaRun {
     constexpr int h = kLB / 2;
 #pragma unroll
     for (int q = PART * h; q < (PART + 1) * h; q++) dma16(base + C::BM * BK + (wave * kLB + q) * 1024, bp, b_off[q]);
-    if constexpr (PART == 1) {
-#pragma unroll
-      for (int q = 0; q < kSc; q++)
-        dma4(base + L::kScOff + s_lds[q], s_base[q] + (kb >> s_shift[q]) * s_step[q], s_off[q]);
-    }
+    if constexpr (PART == 1) issue_scales(st, kb);
   }
 
   __device__ __forceinline__ void issue(int st, int kb) {
@@ -765,6 +764,11 @@ struct DmaRun {
     const uint8_t* bp = b_base + kb * BK;
 #pragma unroll
     for (int q = 0; q < kLB; q++) dma16(base + C::BM * BK + (wave * kLB + q) * 1024, bp, b_off[q]);
+    issue_scales(st, kb);
+  }
+  // the scale load of step kb (grouped modes: a four-step group or the dummy)
+  __device__ __forceinline__ void issue_scales(int st, int kb) {
+    const uint32_t base = smem_lds + st * L::kStage;
     if constexpr (L::kGrouped) {
       // tiles of step kb carry scale group (kb+2)/4 when kb%4 == 2 (groups 0 and 1 with
       // the first two steps); the group index is clamped (a reload writes equal bytes)
