@@ -586,6 +586,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
 //
 // 256x256 tiles need 64 KB per step, so only two stages fit: step kb+2 is loaded into
 // stage kb%2 after the barrier of step kb and has one (twice as long) step to land.
+// In both, a step's loads go out in two parts (activation blocks after the barrier,
+// weight blocks and scales before the next step's first two rows), not as one burst.
 //
 // The loads are written as inline assembly so that the compiler, which cannot tell LDS
 // stages apart, does not wait for them before unrelated LDS reads; the waits are explicit
