@@ -482,7 +482,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_m4096")
-    ap.add_argument("--cpu-rows", type=int, default=384)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="with --suite: comma-separated sections to run (" + ",".join(SUITE_SECTIONS) + ")")
