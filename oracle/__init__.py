@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchma
 CPU-baseline leg, never by the product path. It shares no code with the HIP library.
 
 The arithmetic lives in plain C (fp8q_oracle.c, built by build.py with IEEE semantics);
-this module only marshals numpy arrays into it. Function-level citations are in the C
+this module only marshals numpy arrays into it. The C loops over rows and output elements
+run on all host cores (OpenMP; `threads(n)` limits them); each row or output is computed
+whole by one thread, so results do not depend on the thread count. Function-level citations are in the C
 source; the arguments mirror the C ABI declared in include/fp8q.h, with host arrays in
 place of device pointers.
 
@@ -64,8 +66,38 @@ def _load():
         getattr(lib, name).argtypes = [_P, _P, _I64]
     lib.ora_silu_mul_array.restype = None
     lib.ora_silu_mul_array.argtypes = [_P, _P, _P, _I64]
+    lib.ora_set_threads.restype = None
+    lib.ora_set_threads.argtypes = [ctypes.c_int]
+    lib.ora_max_threads.restype = ctypes.c_int
+    lib.ora_max_threads.argtypes = []
     _lib = lib
     return lib
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's loops over rows / output elements (results do not depend
+    on it: every row or output is computed whole by one thread)."""
+    _load().ora_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().ora_max_threads())
+
+
+class threads:
+    """Context manager: run the oracle with n threads, then restore the previous count."""
+
+    def __init__(self, n: int):
+        self.n = n
+
+    def __enter__(self):
+        self.prev = max_threads()
+        set_threads(self.n)
+        return self
+
+    def __exit__(self, *exc):
+        set_threads(self.prev)
+        return False
 
 
 def _ptr(a: np.ndarray | None):

@@ -12,7 +12,7 @@ SRC = os.path.join(HERE, "fp8q_oracle.c")
 LIB = os.path.join(HERE, "libfp8q_oracle.so")
 
 # IEEE semantics: no fast-math, no implicit fused multiply-add.
-CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
           "-Wall", "-Wextra"]
 
 

@@ -7,9 +7,12 @@
  * constant with the HIP library: everything here is written out from the sources
  * cited below and from the definitions of the number formats.
  *
- * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared (see build.py).
- * All float arithmetic is IEEE-754 binary32/binary64 with round-to-nearest-even; no
- * contraction into fused multiply-add except where fmaf() is written explicitly.
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -fPIC -shared (see
+ * build.py). All float arithmetic is IEEE-754 binary32/binary64 with round-to-nearest-even;
+ * no contraction into fused multiply-add except where fmaf() is written explicitly.
+ * The only parallelism is an OpenMP loop over independent rows (quantization) or output
+ * elements (GEMM): each result is computed by one thread with the same sequential
+ * arithmetic, so results do not depend on the thread count (ora_set_threads).
  *
  * Sources:
  *   [PR30924] prhub report of sglang PR #30924 "[JIT] Trait-driven per_token_group_quant:
@@ -39,6 +42,7 @@
  *     even, stored as a two's-complement byte. fp32 scales only.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -261,31 +265,48 @@ int ora_group_quant(const void* x, int in_dtype, int64_t E, int64_t M, int64_t K
   if (G != 32 && G != 64 && G != 128 && G != K) return -1;
   if (G <= 0 || K % G != 0) return -1;
   if (out_int8 && scale_fmt != ORA_SCALE_F32) return -1;
-  float* vals = (float*)malloc((size_t)G * sizeof(float));
-  if (!vals) return -1;
-  if (rows_e && rows_m) {
-    for (int64_t i = 0; i < n_rows; i++) {
-      int64_t e = rows_e[i], m = rows_m[i];
-      quant_row(x, in_dtype, e * x_se + m * x_sm, K, silu, q + e * q_se + m * q_sm, s,
-                scale_fmt, e * s_se + m * s_sm, s_sg, G, out_int8, vals);
+  int failed = 0;
+  /* rows are independent: one thread quantizes a whole row */
+#pragma omp parallel
+  {
+    float* vals = (float*)malloc((size_t)G * sizeof(float));
+    if (!vals) {
+#pragma omp atomic write
+      failed = 1;
+    }
+    if (vals && rows_e && rows_m) {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t i = 0; i < n_rows; i++) {
+        int64_t e = rows_e[i], m = rows_m[i];
+        quant_row(x, in_dtype, e * x_se + m * x_sm, K, silu, q + e * q_se + m * q_sm, s,
+                  scale_fmt, e * s_se + m * s_sm, s_sg, G, out_int8, vals);
+      }
+    } else if (vals) {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < E * M; r++) {
+        int64_t e = r / M, m = r % M;
+        int64_t rows = M;
+        if (masked_m) {
+          rows = masked_m[e];
+          if (rows < 0) rows = 0;
+          if (rows > M) rows = M;
+        }
+        if (m < rows)
+          quant_row(x, in_dtype, e * x_se + m * x_sm, K, silu, q + e * q_se + m * q_sm, s,
+                    scale_fmt, e * s_se + m * s_sm, s_sg, G, out_int8, vals);
+      }
     }
     free(vals);
-    return 0;
   }
-  for (int64_t e = 0; e < E; e++) {
-    int64_t rows = M;
-    if (masked_m) {
-      rows = masked_m[e];
-      if (rows < 0) rows = 0;
-      if (rows > M) rows = M;
-    }
-    for (int64_t m = 0; m < rows; m++)
-      quant_row(x, in_dtype, e * x_se + m * x_sm, K, silu, q + e * q_se + m * q_sm, s,
-                scale_fmt, e * s_se + m * s_sm, s_sg, G, out_int8, vals);
-  }
-  free(vals);
-  return 0;
+  return failed ? -1 : 0;
 }
+
+/* Thread count of the OpenMP loops (n >= 1), and the count they will use. */
+void ora_set_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+}
+
+int ora_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------------------
  * block-scaled GEMM: dequantize, then multiply, in fp64  [FI sections 6-7]
@@ -335,12 +356,15 @@ int ora_gemm(const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t 
   double dec[256];
   for (int c = 0; c < 256; c++) dec[c] = ora_e4m3_decode((uint8_t)c);
   if (mode != ORA_GEMM_BLOCK128 && mode != ORA_GEMM_MX32) return -1;
+  /* output elements are independent: one thread computes each whole sum */
   if (ms && ns) {
+#pragma omp parallel for schedule(dynamic, 64)
     for (int64_t i = 0; i < count; i++)
       gemm_elem(a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, K, mode,
                 dec, ms[i], ns[i], &y_out[i], &s_out[i]);
     return 0;
   }
+#pragma omp parallel for schedule(dynamic, 1)
   for (int64_t m = 0; m < M; m++)
     for (int64_t n = 0; n < N; n++)
       gemm_elem(a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, K, mode,

@@ -358,3 +358,25 @@ def test_pack_ue8m0_round_trip_and_shape():
     assert np.array_equal(oracle.unpack_ue8m0(w), b)
     with pytest.raises(ValueError):
         oracle.pack_ue8m0(b[..., :6])
+
+
+# ----------------------------------------------------------------- thread-count independence
+def test_results_do_not_depend_on_the_thread_count():
+    """The oracle's OpenMP loops give each row (quant) and each output (GEMM) to one thread,
+    so one thread and all threads must agree bit for bit, masked and flat."""
+    x = synth.activations_bf16(30, 3 * 40, 2 * 384, outlier_p=0.01).reshape(3, 40, 768)
+    mm = np.array([40, 0, 17], dtype=np.int32)
+    a = synth.weight_codes(31, 37, 512, tensor_id=1, sigma=100.0)
+    b = synth.weight_codes(31, 50, 512, tensor_id=2)
+    sa = synth.block_scales(31, 37, 4, tensor_id=3)
+    sb = synth.block_scales(31, 1, 4, tensor_id=4)
+    outs = []
+    for n in (1, max(2, oracle.max_threads())):
+        with oracle.threads(n):
+            q, s = oracle.group_quant(x, 128, oracle.SCALE_UE8M0, "col", silu=True, masked_m=mm, fill=0x5A)
+            qf, sf = oracle.group_quant(x[0], 64, oracle.SCALE_F32, "row")
+            y, S = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_F32)
+            ys, Ss = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_F32, at=(np.arange(30) % 37, np.arange(30)))
+        outs.append((q, s, qf, sf, y, S, ys, Ss))
+    for u, v in zip(*outs):
+        assert np.array_equal(u, v)
