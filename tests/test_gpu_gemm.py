@@ -49,11 +49,17 @@ def _fmt(s):
     return oracle.SCALE_F32 if s.dtype == np.float32 else oracle.SCALE_UE8M0
 
 
-def _sample(M, N, count, seed):
+def _sample(M, N, count, seed, tile=256):
+    """Output elements to compare at full size: the corners, `count` seeded random ones and
+    one complete tile x tile block of outputs at a seeded tile position (ragged where it
+    meets the edge)."""
     g = np.random.default_rng(seed)
     ms = np.concatenate([[0, M - 1, 0, M - 1, min(127, M - 1), min(128, M - 1)], g.integers(0, M, count)])
     ns = np.concatenate([[0, N - 1, N - 1, 0, min(128, N - 1), min(127, N - 1)], g.integers(0, N, count)])
-    return ms, ns
+    m0 = int(g.integers(0, -(-M // tile))) * tile
+    n0 = int(g.integers(0, -(-N // tile))) * tile
+    tm, tn = np.meshgrid(np.arange(m0, min(M, m0 + tile)), np.arange(n0, min(N, n0 + tile)), indexing="ij")
+    return np.concatenate([ms, tm.ravel()]), np.concatenate([ns, tn.ravel()])
 
 
 # ----------------------------------------------------------------------------- BLOCK128 full
@@ -64,7 +70,7 @@ def test_tiny_workload_full():
     wq, ws = synth.weights(w)
     y = _gpu_block(q, s, wq, ws)
     ys, ss = oracle.gemm_block128(q, s, wq, ws, oracle.SCALE_F32)
-    check(y, ys, ss, w.K, "tiny")
+    check(y, ys, ss, w.K, "tiny", cls="outlier")
 
 
 # M > 128 with M % 4 == 0 reaches the direct-to-LDS kernel for fp32 weight scales (also
@@ -220,7 +226,7 @@ def test_ue8m0_weight_scales_dense_m4096_sampled():
     b, sb = _ue8m0_weights(w, 66)
     sa_col = np.ascontiguousarray(sa.T)
     y = _gpu_block(a, sa_col, b, sb, "col")
-    ms, ns = _sample(w.M, w.N, 3000, 12)
+    ms, ns = _sample(w.M, w.N, 5000, 12)
     ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", oracle.SCALE_UE8M0, at=(ms, ns))
     check(y[ms, ns], ys, ss, w.K, "dense M=4096, UE8M0 weight scales")
     assert not np.any(y == SENT)
@@ -244,11 +250,8 @@ def test_dense_small_m(M):
     b, sb = synth.weights(w)
     sa_col = np.ascontiguousarray(sa.T)
     y = _gpu_block(a, sa_col, b, sb, "col")
-    ns = np.unique(np.concatenate([np.arange(0, w.N, 16), np.arange(127, w.N, 128)]))
-    ms = np.repeat(np.arange(M), ns.size)
-    nn = np.tile(ns, M)
-    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", at=(ms, nn))
-    check(y[ms, nn], ys, ss, w.K, f"dense M={M}")
+    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col")  # every output
+    check(y, ys, ss, w.K, f"dense M={M} (c2)")
 
 
 def test_dense_m4096_sampled():
@@ -257,9 +260,9 @@ def test_dense_m4096_sampled():
     b, sb = synth.weights(w)
     sa_col = np.ascontiguousarray(sa.T)
     y = _gpu_block(a, sa_col, b, sb, "col")
-    ms, ns = _sample(w.M, w.N, 4000, 1)
+    ms, ns = _sample(w.M, w.N, 5000, 1)
     ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", at=(ms, ns))
-    check(y[ms, ns], ys, ss, w.K, "dense M=4096")
+    check(y[ms, ns], ys, ss, w.K, "dense M=4096 (c2)", cls="act")
     assert not np.any(y == SENT)
 
 
@@ -268,9 +271,9 @@ def test_silu_down_projection_sampled():
     a, sa = synth.gemm_activation(w)
     b, sb = synth.weights(w)
     y = _gpu_block(a, sa, b, sb, "row")
-    ms, ns = _sample(w.M, w.N, 4000, 2)
+    ms, ns = _sample(w.M, w.N, 5000, 2)
     ys, ss = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_F32, "row", at=(ms, ns))
-    check(y[ms, ns], ys, ss, w.K, "silu down-proj")
+    check(y[ms, ns], ys, ss, w.K, "silu down-proj (c3)", cls="act")
 
 
 # ----------------------------------------------------------------------------- masked grouped
@@ -397,11 +400,16 @@ def test_masked_moe_workload_sampled(forced):
             continue
         ms = np.concatenate([[0, r - 1], g.integers(0, r, 158)])
         ns = np.concatenate([[0, w.N - 1], g.integers(0, w.N, 158)])
+        if r == mm.max():  # one complete 128 x 256 output tile of the fullest expert
+            n0 = int(g.integers(0, w.N // 256)) * 256
+            tm, tn = np.meshgrid(np.arange(min(r, 128)), np.arange(n0, n0 + 256), indexing="ij")
+            ms, ns = np.concatenate([ms, tm.ravel()]), np.concatenate([ns, tn.ravel()])
         ys, ss = oracle.gemm_block128(a[e, :r], np.ascontiguousarray(sa[e][:, :r]), b[e], sb[e],
                                       oracle.SCALE_UE8M0, "col", at=(ms, ns))
         check(y[e][ms, ns], ys, ss, w.K, f"expert {e}")
         ys_all.append(ys); y_all.append(y[e][ms, ns]); s_all.append(ss)
-    check(np.concatenate(y_all), np.concatenate(ys_all), np.concatenate(s_all), w.K, "all experts")
+    check(np.concatenate(y_all), np.concatenate(ys_all), np.concatenate(s_all), w.K,
+          "masked MoE (c4)" + (", forced counts" if forced else ""))
 
 
 # ----------------------------------------------------------------------------- MX32
@@ -428,7 +436,7 @@ def test_mx_full(M, N, K, sk_stride):
     eb = synth.e8m0_exponents(70, N, K // 32, tensor_id=4)
     y = _gpu_mx(a, ea, b, eb, sk_stride)
     ys, ss = oracle.gemm_mx32(a, ea, b, eb)
-    check(y, ys, ss, K, f"mx {M}x{N}x{K}")
+    check(y, ys, ss, K, f"mx {M}x{N}x{K}", cls="wide")
 
 
 # At least 256 tiles of 256x256 take the two-stage kernel (per-step scale loads); ragged in
@@ -448,16 +456,16 @@ def test_mx_wide_ragged_sampled(K, sk_stride):
     cols = np.unique(np.concatenate([[0, 63, 64, 191, 192, 255, 256, 4095, 4096, 4199], g.integers(0, N, 40)]))
     ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
     ys, ss = oracle.gemm_mx32(a, ea, b, eb, at=(ms, ns))
-    check(y[ms, ns], ys, ss, K, f"mx wide {M}x{N}x{K}")
+    check(y[ms, ns], ys, ss, K, f"mx wide {M}x{N}x{K}", cls="wide")
 
 
 def test_mx_workload_sampled():
     w = synth.MX
     a, b, ea, eb = synth.mx_operands(w)
     y = _gpu_mx(a, ea, b, eb)
-    ms, ns = _sample(w.M, w.N, 4000, 4)
+    ms, ns = _sample(w.M, w.N, 5000, 4)
     ys, ss = oracle.gemm_mx32(a, ea, b, eb, at=(ms, ns))
-    check(y[ms, ns], ys, ss, w.K, "mxfp8 8192^3")
+    check(y[ms, ns], ys, ss, w.K, "mxfp8 8192^3 (c5)", cls="wide")
     assert not np.any(y == SENT)
 
 
@@ -497,7 +505,7 @@ def test_mx_packed_words_full(M, N, K, la, lb):
     eb = synth.e8m0_exponents(72, N, K // 32, tensor_id=4)
     y = _gpu_mx_layouts(a, ea, b, eb, la, lb)
     ys, ss = oracle.gemm_mx32(a, ea, b, eb)
-    check(y, ys, ss, K, f"mx packed {la}/{lb} {M}x{N}x{K}")
+    check(y, ys, ss, K, f"mx packed {la}/{lb} {M}x{N}x{K}", cls="wide")
 
 
 # 256x256 tiles (at least 256 of them) with packed words, ragged in both directions
@@ -515,16 +523,16 @@ def test_mx_packed_words_wide_sampled(la, lb):
     cols = np.unique(np.concatenate([[0, 63, 64, 255, 256, 4095, 4096, 4199], g.integers(0, N, 40)]))
     ms, ns = (v.ravel() for v in np.meshgrid(rows, cols, indexing="ij"))
     ys, ss = oracle.gemm_mx32(a, ea, b, eb, at=(ms, ns))
-    check(y[ms, ns], ys, ss, K, f"mx packed wide {la}/{lb}")
+    check(y[ms, ns], ys, ss, K, f"mx packed wide {la}/{lb}", cls="wide")
 
 
 def test_mx_packed_words_workload_sampled():
     w = synth.MX
     a, b, ea, eb = synth.mx_operands(w)
     y = _gpu_mx_layouts(a, ea, b, eb, "col", "col")
-    ms, ns = _sample(w.M, w.N, 4000, 6)
+    ms, ns = _sample(w.M, w.N, 5000, 6)
     ys, ss = oracle.gemm_mx32(a, ea, b, eb, at=(ms, ns))
-    check(y[ms, ns], ys, ss, w.K, "mxfp8 8192^3, column-major packed words")
+    check(y[ms, ns], ys, ss, w.K, "mxfp8 8192^3, column-major packed words", cls="wide")
     assert not np.any(y == SENT)
 
 
@@ -547,7 +555,7 @@ def test_quant_g32_packed_words_feed_the_mx_gemm():
     qo, so = oracle.group_quant(xb, 32, oracle.SCALE_UE8M0, "row")
     assert np.array_equal(q.cpu().numpy(), qo)
     ys, ss = oracle.gemm_mx32(qo, so, b, eb)
-    check(y.cpu().numpy().view(np.uint16), ys, ss, K, "quant G=32 packed -> MX32")
+    check(y.cpu().numpy().view(np.uint16), ys, ss, K, "quant G=32 packed -> MX32", cls="outlier")
 
 
 # ----------------------------------------------------------------------------- API behaviour
@@ -698,11 +706,11 @@ def test_moe_second_stage_sampled():
         qo, so = oracle.group_quant(h[e][rows], G, oracle.SCALE_UE8M0, "row", silu=True)
         assert np.array_equal(qg[e][rows], qo), f"expert {e}: codes"
         assert np.array_equal(wg[e][rows], oracle.pack_ue8m0(so)), f"expert {e}: packed scale words"
-        cols = np.unique(np.concatenate([[0, 127, 128, N - 1], g.integers(0, N, 60)]))
+        cols = np.unique(np.concatenate([[0, 127, 128, N - 1], g.integers(0, N, 100)]))
         ms, ns = (v.ravel() for v in np.meshgrid(np.arange(rows.size), cols, indexing="ij"))
         ys, ss = oracle.gemm_block128(qo, so, wts[e][0], wts[e][1], oracle.SCALE_UE8M0, "row", at=(ms, ns))
         got.append(yg[e][rows][ms, ns]); want.append(ys); size.append(ss)
-    check(np.concatenate(got), np.concatenate(want), np.concatenate(size), K, "moe second stage")
+    check(np.concatenate(got), np.concatenate(want), np.concatenate(size), K, "moe second stage", cls="silu")
 
 
 # ----------------------------------------------------------------------------- segments / contiguous
