@@ -11,6 +11,8 @@ namespace {
 thread_local std::string g_last_error;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_device_cus[kMaxDevices];
+std::atomic<int> g_device_xcds[kMaxDevices];
 }  // namespace
 
 void set_error(const std::string& msg) { g_last_error = msg; }
@@ -29,6 +31,12 @@ static int query_device(int device) {
     return fail(FP8Q_EDEVICE, "cannot query HIP device " + std::to_string(device));
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(FP8Q_EDEVICE, std::string("device is ") + prop.gcnArchName + ", this library targets gfx950");
+  int xcds = 1;
+  if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, device) != hipSuccess || xcds < 1) xcds = 1;
+  if (device < kMaxDevices) {
+    g_device_cus[device].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1, std::memory_order_relaxed);
+    g_device_xcds[device].store(xcds, std::memory_order_relaxed);
+  }
   return FP8Q_OK;
 }
 
@@ -43,6 +51,14 @@ int check_current_device() {
   const int rc = query_device(dev);
   if (dev < kMaxDevices) g_device_state[dev].store(rc == FP8Q_OK ? 1 : 2, std::memory_order_relaxed);
   return rc;
+}
+
+DeviceShape current_device_shape() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DeviceShape{256, 8};
+  const int cus = g_device_cus[dev].load(std::memory_order_relaxed);
+  const int xcds = g_device_xcds[dev].load(std::memory_order_relaxed);
+  return DeviceShape{cus > 0 ? cus : 256, xcds > 0 ? xcds : 8};
 }
 
 }  // namespace fp8q

@@ -56,6 +56,10 @@ int grouped_rows_entry(const std::string& pre, const uint8_t* a, int64_t lda, co
     return fail(FP8Q_EINVAL, pre + "negative size, stride or expected_rows");
   if (T >= (int64_t(1) << 31)) return fail(FP8Q_EUNSUPPORTED, pre + "at most 2^31 - 1 rows");
   if (seg_indptr && S > 2048) return fail(FP8Q_EUNSUPPORTED, pre + "at most 2048 segments");
+  // the device builds a 32-bit prefix of the segments' tile counts (segments may overlap,
+  // so each can reach every row): bound its total
+  if (seg_indptr && S * ((T + 127) / 128) * ((N + 127) / 128) >= (int64_t(1) << 31))
+    return fail(FP8Q_EUNSUPPORTED, pre + "too many output tiles over the segments");
   int rc = check_operands(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy, T, N,
                           K, FP8Q_GEMM_BLOCK128);
   if (rc != FP8Q_OK) return rc;

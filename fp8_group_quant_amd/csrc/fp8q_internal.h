@@ -8,6 +8,7 @@
 #include <string>
 
 #include "fp8q.h"
+#include "tile_order.h"
 
 namespace fp8q {
 
@@ -17,6 +18,14 @@ int fail(int status, const std::string& msg);
 
 // Validates the current device once per device (gfx950 only).
 int check_current_device();
+
+// Compute units and XCDs of the current device, as queried by check_current_device (which
+// must have returned FP8Q_OK on this device first).
+struct DeviceShape {
+  int cus;
+  int xcds;
+};
+DeviceShape current_device_shape();
 
 // ------------------------------------------------------------------ quant launcher
 struct QuantParams {
@@ -59,6 +68,7 @@ struct GemmParams {
   int sa_fmt, sb_fmt;
   int sa_packed;  // UE8M0 activation scales packed 4 K blocks per 32-bit word (sa strides in words)
   int sb_packed;  // MX32 only: E8M0 weight scales packed likewise (sb strides in words)
+  int xcds;       // XCDs of the device (workgroup b runs on XCD b % xcds)
 };
 
 int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t stream);

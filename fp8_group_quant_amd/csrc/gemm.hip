@@ -61,8 +61,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 128;   // K per step (= one BLOCK128 scale block)
-constexpr int kXcds = 8;
-constexpr int kCUs = 256;
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int GROUP_M_>
 struct TileCfg {
@@ -548,17 +546,10 @@ __device__ Tile tile_at(const GemmParams& p, const int32_t* pref, int64_t t) {
   return tile;
 }
 
-// XCD-contiguous split of the tile list: workgroup w runs on XCD w % 8 (the grid is a
-// multiple of 8), and each XCD takes one contiguous eighth of the list.
-struct TileRange {
-  int64_t beg, end, stride;
-  __device__ TileRange(int64_t T) {
-    const int64_t xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nslots = gridDim.x / kXcds;
-    beg = (xcd * T) / kXcds + slot;
-    end = ((xcd + 1) * T) / kXcds;
-    stride = nslots;
-  }
-};
+// The tiles of this workgroup: an XCD-contiguous split of the tile list (tile_order.h).
+__device__ __forceinline__ TileSpan my_tiles(const GemmParams& p, int64_t tiles) {
+  return tile_span(tiles, blockIdx.x, gridDim.x, p.xcds);
+}
 
 template <class C, bool MX, int SA_FMT, int SB_FMT>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
@@ -566,7 +557,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(GemmParams p) {
   __shared__ Stage<C> stage1;
   __shared__ int32_t part[C::kThreads];
   extern __shared__ int32_t pref[];  // masked only, E + 1 entries
-  const TileRange tr(build_tile_list<C>(p, part, pref));
+  const TileSpan tr = my_tiles(p, build_tile_list<C>(p, part, pref));
   for (int64_t t = tr.beg; t < tr.end; t += tr.stride)
   {
     const Tile tile = tile_at<C>(p, pref, t);
@@ -1214,7 +1205,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_dma_kernel(GemmParams p) 
   __shared__ __attribute__((aligned(16))) uint8_t smem[DmaLayout<SCM, C>::kBytes];
   __shared__ int32_t pref[DmaLayout<SCM, C>::kMaxPrefix + 1];  // masked only, E + 1 entries
   int32_t* part = reinterpret_cast<int32_t*>(smem);  // scan scratch, used before any load
-  const TileRange tr(build_tile_list<C>(p, part, pref));
+  const TileSpan tr = my_tiles(p, build_tile_list<C>(p, part, pref));
   for (int64_t t = tr.beg; t < tr.end; t += tr.stride)
   {
     const Tile tile = tile_at<C>(p, pref, t);
@@ -1505,6 +1496,198 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void gemm_skinny_dma_kernel(Gemm
   }
 }
 
+// Small M through registers: each workgroup owns 16 rows of B (one MFMA n slice) against all
+// M rows of A, like the kernels above, but its waves take contiguous ranges of the K blocks
+// and load their fragments of A and B (and the scales) straight from global memory into
+// registers, a pass of P blocks at a time, the next pass issued before the current one is
+// computed. With K = 7168 a wave's whole range is in flight from the start for M <= 16, so
+// the launch pays about one memory latency instead of one per block. The operand fragments
+// are buffer loads: a lane's row and chunk are a fixed 32-bit offset, the block a scalar
+// offset, so a load costs no address arithmetic; rows past N or M read as zeros (the
+// buffer's bounds) and are never stored. The partial sums of the waves are added through
+// LDS in wave order (fixed, so results are reproducible), each wave finishing one 16-row
+// slice of the output.
+template <int SM>
+struct SmallCfg {
+  // Eight waves (two per SIMD, 256 VGPRs each). Blocks per pass: two passes of fragments
+  // (B 8 VGPRs, A 8 per 16 rows, scales) fit the registers.
+  static_assert(SM == 1 || SM == 2, "M <= 32");
+  static constexpr int kWaves = 8;
+  static constexpr int P = SM == 2 ? 3 : 4;
+};
+
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource: 32-bit data format, no swizzle
+
+__device__ __forceinline__ v8i frag_buffer(__amdgpu_buffer_rsrc_t r, uint32_t voff, int kb) {
+  const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, kb * BK, 0));
+  const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 64, kb * BK, 0));
+  v8i v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
+template <int SM, int SA_FMT, int SB_FMT>
+__global__ __launch_bounds__(64 * SmallCfg<SM>::kWaves, 1) void gemm_small_m_kernel(GemmParams p) {
+  constexpr int P = SmallCfg<SM>::P, kSmallWaves = SmallCfg<SM>::kWaves;
+  constexpr int sab = SA_FMT == FP8Q_SCALE_F32 ? 4 : 1, sbb = SB_FMT == FP8Q_SCALE_F32 ? 4 : 1;
+  __shared__ v4f red[kSmallWaves][SM][64];
+  // Every parameter is read here, before any branch, so the kernel-argument loads go out as
+  // one batch (read where they are used, they became several dependent round trips). The
+  // launcher guarantees that every offset below fits in 31 bits.
+  const uint8_t* const A = p.a;
+  const uint8_t* const B = p.b;
+  const uint8_t* const SA = static_cast<const uint8_t*>(p.sa);
+  const uint8_t* const SB = static_cast<const uint8_t*>(p.sb);
+  uint16_t* const Y = p.y;
+  const int M = static_cast<int>(p.M), N = static_cast<int>(p.N), nkb = static_cast<int>(p.K / BK);
+  const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+  const int sa_sm = static_cast<int>(p.sa_sm), sa_sk = static_cast<int>(p.sa_sk);
+  const int sb_sn = static_cast<int>(p.sb_sn), sb_sk = static_cast<int>(p.sb_sk);
+  const int64_t ldy = p.ldy;
+  const bool packed = p.sa_packed != 0;
+  // (an empty statement that uses every parameter: it keeps the compiler from sinking their
+  // loads into later blocks)
+  asm volatile("" ::"s"(A), "s"(B), "s"(SA), "s"(SB), "s"(Y), "s"(M), "s"(N), "s"(nkb), "s"(lda), "s"(ldb),
+               "s"(ldy), "s"(sa_sm), "s"(sa_sk), "s"(sb_sn), "s"(sb_sk), "s"(p.sa_packed));
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int kb_beg = (nkb * wave) / kSmallWaves, kb_end = (nkb * (wave + 1)) / kSmallWaves;
+  const int l16 = lane & 15, chunk = (lane >> 4) * 16;
+  // B: this workgroup's rows (fewer than 16 in the last one); A: all M rows
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(B + static_cast<int64_t>(n0) * ldb), 0, min(16, N - n0) * ldb, kBufWord3);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A), 0, M * lda, kBufWord3);
+  const uint32_t wo = static_cast<uint32_t>(l16 * ldb + chunk);
+  uint32_t xo[SM], sa_row[SM];
+#pragma unroll
+  for (int i = 0; i < SM; i++) {
+    xo[i] = static_cast<uint32_t>((i * 16 + l16) * lda + chunk);
+    // activation scale (m, kb) at byte sa_row[i] + sa_col(kb): packed UE8M0 words hold K
+    // blocks 4j..4j+3 of a row in bytes 0..3 (strides in words), other layouts one element
+    // per (m, kb); rows past M read row M - 1
+    const int m = min(i * 16 + l16, M - 1);
+    sa_row[i] = static_cast<uint32_t>(packed ? 4 * m * sa_sm : m * sa_sm * sab);
+  }
+  auto sa_col = [&](int kb) -> uint32_t {
+    return static_cast<uint32_t>(packed ? 4 * (kb >> 2) * sa_sk + (kb & 3) : kb * sa_sk * sab);
+  };
+  const uint8_t* const sb_row = SB + static_cast<int64_t>((n0 / 128) * sb_sn) * sbb;
+
+  struct Pass {
+    v8i w[P];
+    v8i x[P][SM];
+    uint32_t sa[P][SM];
+    uint32_t sb[P];
+  };
+  // loads of blocks kb0 .. kb0+P-1; indices past the wave's range reload its last block
+  // (a wave with an empty range, when K has fewer than one block per wave, reloads block 0),
+  // whose products are then not added
+  const int kb_last = max(kb_end - 1, 0);
+  auto issue = [&](Pass& b, int kb0) {
+#pragma unroll
+    for (int u = 0; u < P; u++) {
+      const int kb = min(kb0 + u, kb_last);
+      b.w[u] = frag_buffer(rb, wo, kb);
+      const uint32_t sc = sa_col(kb);
+#pragma unroll
+      for (int i = 0; i < SM; i++) {
+        b.x[u][i] = frag_buffer(ra, xo[i], kb);
+        const uint32_t so = sa_row[i] + sc;
+        b.sa[u][i] = SA_FMT == FP8Q_SCALE_F32 ? *reinterpret_cast<const uint32_t*>(SA + so) : SA[so];
+      }
+      const uint32_t bo = static_cast<uint32_t>(kb * sb_sk * sbb);
+      b.sb[u] = SB_FMT == FP8Q_SCALE_F32 ? *reinterpret_cast<const uint32_t*>(sb_row + bo) : sb_row[bo];
+    }
+  };
+  v4f acc[SM];
+#pragma unroll
+  for (int i = 0; i < SM; i++) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  // products of blocks outside the range are computed and dropped (a select, no branch)
+  auto compute = [&](const Pass& b, int kb0) {
+#pragma unroll
+    for (int u = 0; u < P; u++) {
+      const bool valid = kb0 + u < kb_end;
+      const float sbv = scale_value<SB_FMT>(b.sb[u]);
+#pragma unroll
+      for (int i = 0; i < SM; i++) {
+        const v4f z = {0.f, 0.f, 0.f, 0.f};
+        const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b.w[u], b.x[u][i], z, 0, 0, 0, 0, 0, 0);
+        const float sv = scale_value<SA_FMT>(b.sa[u][i]) * sbv;
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[i][r] = valid ? fmaf(pr[r], sv, acc[i][r]) : acc[i][r];
+      }
+    }
+  };
+  Pass b0, b1;
+  issue(b0, kb_beg);
+  issue(b1, kb_beg + P);
+  for (int kb0 = kb_beg;; kb0 += 2 * P) {
+    compute(b0, kb0);
+    if (kb0 + P >= kb_end) break;
+    if (kb0 + 2 * P < kb_end) issue(b0, kb0 + 2 * P);
+    compute(b1, kb0 + P);
+    if (kb0 + 2 * P >= kb_end) break;
+    if (kb0 + 3 * P < kb_end) issue(b1, kb0 + 3 * P);
+  }
+#pragma unroll
+  for (int i = 0; i < SM; i++) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  // wave w finishes 16-row slices w, w + kSmallWaves, ...: the partials added in wave order
+  for (int i = wave; i < SM; i += kSmallWaves) {
+    v4f t = red[0][i][lane];
+#pragma unroll
+    for (int w = 1; w < kSmallWaves; w++) {
+      const v4f o = red[w][i][lane];
+      t[0] += o[0]; t[1] += o[1]; t[2] += o[2]; t[3] += o[3];
+    }
+    const int m = i * 16 + l16;
+    if (m >= M) continue;
+    uint16_t* yrow = Y + m * ldy;
+    const int n = n0 + 4 * (lane >> 4);
+    const uint32_t h0 = bf16_rne(t[0]), h1 = bf16_rne(t[1]), h2 = bf16_rne(t[2]), h3 = bf16_rne(t[3]);
+    if (n + 3 < N) {
+      *reinterpret_cast<uint32_t*>(yrow + n) = h0 | (h1 << 16);
+      *reinterpret_cast<uint32_t*>(yrow + n + 2) = h2 | (h3 << 16);
+    } else {
+      if (n < N) yrow[n] = static_cast<uint16_t>(h0);
+      if (n + 1 < N) yrow[n + 1] = static_cast<uint16_t>(h1);
+      if (n + 2 < N) yrow[n + 2] = static_cast<uint16_t>(h2);
+    }
+  }
+}
+
+// Whether every offset of the small-M kernel fits in 31 bits (else the large kernels run it).
+bool small_m_fits(const GemmParams& p) {
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t sab = p.sa_fmt == FP8Q_SCALE_F32 ? 4 : 1, sbb = p.sb_fmt == FP8Q_SCALE_F32 ? 4 : 1;
+  const int64_t nkb = p.K / BK;
+  const int64_t sa_max = p.sa_packed ? 4 * ((p.M - 1) * p.sa_sm + ((nkb - 1) / 4) * p.sa_sk) + 3
+                                     : ((p.M - 1) * p.sa_sm + (nkb - 1) * p.sa_sk) * sab + sab;
+  const int64_t sb_max = (((p.N - 1) / 128) * p.sb_sn + (nkb - 1) * p.sb_sk) * sbb + sbb;
+  return p.M * p.lda < lim && 16 * p.ldb < lim && p.N < (int64_t(1) << 30) && sa_max < lim && sb_max < lim &&
+         p.lda < lim && p.ldb < lim && p.K < lim;
+}
+
+template <int SM, int SA_FMT, int SB_FMT>
+void launch_small_m_sm(const GemmParams& p, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((p.N + 15) / 16)), block(64 * SmallCfg<SM>::kWaves);
+  hipLaunchKernelGGL((gemm_small_m_kernel<SM, SA_FMT, SB_FMT>), grid, block, 0, s, p);
+}
+
+// M <= kSmallMaxM: the register kernel above; larger M (up to kSkinnyMaxM) keeps the
+// LDS-staged kernel, which moves whole cache lines (there every workgroup streams all of A:
+// 0.9 MB at M = 128, and the register kernel measured 36.6 against 23.5 us).
+constexpr int64_t kSmallMaxM = 32;
+
+template <int SA_FMT, int SB_FMT>
+void launch_small_m(const GemmParams& p, hipStream_t s) {
+  if (p.M <= 16) launch_small_m_sm<1, SA_FMT, SB_FMT>(p, s);
+  else launch_small_m_sm<2, SA_FMT, SB_FMT>(p, s);
+}
+
 template <int SM, int SA_FMT, int SB_FMT>
 void launch_skinny(const GemmParams& p, hipStream_t s) {
   const int grid = static_cast<int>((p.N + 15) / 16);
@@ -1554,10 +1737,12 @@ void launch(const GemmParams& p, int grid, hipStream_t s) {
   hipLaunchKernelGGL((gemm_kernel<C, MX, SA_FMT, SB_FMT>), dim3(grid), dim3(C::kThreads), lds, s, p);
 }
 
-int grid_for(int64_t tiles) {
-  int64_t g = std::min<int64_t>(tiles, kCUs);  // one resident workgroup per CU
-  g = ((g + kXcds - 1) / kXcds) * kXcds;
-  return static_cast<int>(std::max<int64_t>(g, kXcds));
+// Persistent grid: one resident workgroup per CU (at most as many as tiles), a multiple of
+// the XCD count so that every XCD runs the same number of workgroups.
+int grid_for(int64_t tiles, const DeviceShape& ds) {
+  int64_t g = std::min<int64_t>(tiles, ds.cus);
+  g = ((g + ds.xcds - 1) / ds.xcds) * ds.xcds;
+  return static_cast<int>(std::max<int64_t>(g, ds.xcds));
 }
 
 int finish(const char* what) {
@@ -1631,9 +1816,9 @@ void launch_dma(const GemmParams& p, int grid, hipStream_t s) {
 // for one launch. Cost in rounds of 256x256 tiles; a 128x256 tile takes about 0.8 of one
 // (half the MFMA work at a lower MFMA utilisation; measured on 8192x7168x2048, where the
 // split takes 143 instead of 150 us). A split must save at least 3%.
-int64_t wide_split_columns(const GemmParams& p) {
+int64_t wide_split_columns(const GemmParams& p, int64_t cus) {
   const int64_t mt = (p.M + 255) / 256, nt = (p.N + 255) / 256, mh = (p.M + 127) / 128;
-  auto rounds = [](int64_t tiles) { return static_cast<double>((tiles + kCUs - 1) / kCUs); };
+  auto rounds = [cus](int64_t tiles) { return static_cast<double>((tiles + cus - 1) / cus); };
   const double whole = rounds(mt * nt);
   double best = whole;
   int64_t best_n1 = 0;
@@ -1664,7 +1849,9 @@ GemmParams rows_as_words(const GemmParams& p) {
 
 int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t stream) {
   using C = Large;
-  const GemmParams p = rows_as_words(p_in);
+  const DeviceShape ds = current_device_shape();
+  GemmParams p = rows_as_words(p_in);
+  p.xcds = ds.xcds;
   // launch sizing only (the device tile list decides the work): masked and segment launches
   // use the row hint; a segment adds at most one partial tile
   auto tiles_for = [&](int64_t bm, int64_t bn) -> int64_t {
@@ -1674,9 +1861,16 @@ int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t
     if (p.seg_indptr) return ((rows + bm - 1) / bm + p.E) * tn;
     return ((p.M + bm - 1) / bm) * tn;
   };
-  const int grid = grid_for(tiles_for(C::BM, C::BN));
+  const int grid = grid_for(tiles_for(C::BM, C::BN), ds);
   const bool a8 = p.sa_fmt == FP8Q_SCALE_UE8M0, b8 = p.sb_fmt == FP8Q_SCALE_UE8M0;
   const bool grouped = p.masked_m || p.seg_indptr || p.m_indices;
+  if (!grouped && p.M <= kSmallMaxM && small_m_fits(p)) {
+    if (a8 && b8) launch_small_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, stream);
+    else if (a8) launch_small_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, stream);
+    else if (b8) launch_small_m<FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, stream);
+    else launch_small_m<FP8Q_SCALE_F32, FP8Q_SCALE_F32>(p, stream);
+    return finish("block-scaled GEMM launch");
+  }
   if (!grouped && p.M <= kSkinnyMaxM) {
     if (try_skinny_dma(p, stream)) return finish("block-scaled GEMM launch");
     if (a8 && b8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, stream);
@@ -1697,7 +1891,7 @@ int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t
     // grouped: 128-row tiles pad a group's rows to a multiple of 128 instead of 256 (and
     // are the aligned blocks of the contiguous layout)
     using T = DmaCfgT;
-    const int g = grid_for(tiles_for(T::BM, T::BN));
+    const int g = grid_for(tiles_for(T::BM, T::BN), ds);
     if (dm == kScE8Col) launch_dma<kScE8Col, T>(p, g, stream);
     else if (dm == kScE8E8) launch_dma<kScE8E8, T>(p, g, stream);
     else if (dm == kScPkE8) launch_dma<kScPkE8, T>(p, g, stream);
@@ -1712,16 +1906,16 @@ int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t
     // still give every CU a tile
     using W = DmaCfgW;
     const int64_t wt = ((p.M + W::BM - 1) / W::BM) * ((p.N + W::BN - 1) / W::BN);
-    if (wt >= kCUs) {
+    if (wt >= ds.cus) {
       auto wide = [&](const GemmParams& q, int64_t tiles) {
-        if (dm == kScE8Col) launch_dma<kScE8Col, W>(q, grid_for(tiles), stream);
-        else if (dm == kScE8E8) launch_dma<kScE8E8, W>(q, grid_for(tiles), stream);
-        else if (dm == kScPkE8) launch_dma<kScPkE8, W>(q, grid_for(tiles), stream);
-        else if (dm == kScE8Pk) launch_dma<kScE8Pk, W>(q, grid_for(tiles), stream);
-        else if (dm == kScF32Grp) launch_dma<kScF32Grp, W>(q, grid_for(tiles), stream);
-        else launch_dma<kScF32Row, W>(q, grid_for(tiles), stream);
+        if (dm == kScE8Col) launch_dma<kScE8Col, W>(q, grid_for(tiles, ds), stream);
+        else if (dm == kScE8E8) launch_dma<kScE8E8, W>(q, grid_for(tiles, ds), stream);
+        else if (dm == kScPkE8) launch_dma<kScPkE8, W>(q, grid_for(tiles, ds), stream);
+        else if (dm == kScE8Pk) launch_dma<kScE8Pk, W>(q, grid_for(tiles, ds), stream);
+        else if (dm == kScF32Grp) launch_dma<kScF32Grp, W>(q, grid_for(tiles, ds), stream);
+        else launch_dma<kScF32Row, W>(q, grid_for(tiles, ds), stream);
       };
-      const int64_t n1 = wide_split_columns(p);
+      const int64_t n1 = wide_split_columns(p, ds.cus);
       if (n1 == 0) {
         wide(p, wt);
         return finish("block-scaled GEMM launch");
@@ -1736,7 +1930,7 @@ int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t
       p2.y = p.y + n1;
       wide(p1, ((p.M + W::BM - 1) / W::BM) * (n1 / W::BN));
       using T = DmaCfgT;
-      const int g = grid_for(((p.M + T::BM - 1) / T::BM) * ((p2.N + T::BN - 1) / T::BN));
+      const int g = grid_for(((p.M + T::BM - 1) / T::BM) * ((p2.N + T::BN - 1) / T::BN), ds);
       if (dm == kScE8Col) launch_dma<kScE8Col, T>(p2, g, stream);
       else if (dm == kScE8E8) launch_dma<kScE8E8, T>(p2, g, stream);
       else if (dm == kScPkE8) launch_dma<kScPkE8, T>(p2, g, stream);
@@ -1759,20 +1953,23 @@ int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t
   return finish("block-scaled GEMM launch");
 }
 
-int launch_gemm_mx32(const GemmParams& p, hipStream_t stream) {
+int launch_gemm_mx32(const GemmParams& p_in, hipStream_t stream) {
   using C = Large;
+  const DeviceShape ds = current_device_shape();
+  GemmParams p = p_in;
+  p.xcds = ds.xcds;
   const int64_t tiles = ((p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN);
   const int dm = dma_mode(p, true);
   using W = DmaCfgW;
   const int64_t wt = ((p.M + W::BM - 1) / W::BM) * ((p.N + W::BN - 1) / W::BN);
-  if (dm >= 0 && wt >= kCUs) {
+  if (dm >= 0 && wt >= ds.cus) {
     // 256x256 tiles with per-step scale loads (8 jobs: 256 activation and 256 weight rows)
-    launch_dma<kScMx, W>(p, grid_for(wt), stream);
+    launch_dma<kScMx, W>(p, grid_for(wt, ds), stream);
     return finish("MXFP8 GEMM launch");
   }
-  if (dm == kScMxGrp) launch_dma<kScMxGrp>(p, grid_for(tiles), stream);
-  else if (dm == kScMx) launch_dma<kScMx>(p, grid_for(tiles), stream);
-  else launch<C, true, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid_for(tiles), stream);
+  if (dm == kScMxGrp) launch_dma<kScMxGrp>(p, grid_for(tiles, ds), stream);
+  else if (dm == kScMx) launch_dma<kScMx>(p, grid_for(tiles, ds), stream);
+  else launch<C, true, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, grid_for(tiles, ds), stream);
   return finish("MXFP8 GEMM launch");
 }
 

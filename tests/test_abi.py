@@ -122,6 +122,26 @@ def test_gemm_scale_format_validation_before_any_device_call(mode, sa_fmt, sb_fm
     assert rc == status
 
 
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks host validation on a machine without a GPU")
+@pytest.mark.parametrize("S,T,N,status", [
+    (2048, 2 ** 22, 4096, 2),   # 2048 segments that may each span 32768 row tiles x 32 column tiles: EUNSUPPORTED
+    (16, 4096, 4096, 4),        # a modest call passes validation (EDEVICE here)
+])
+def test_segments_tile_count_bound(S, T, N, status):
+    """The device builds a 32-bit prefix of the segments' tile counts; segments may overlap,
+    so the host refuses calls whose bound S * ceil(T/128) * ceil(N/128) reaches 2^31."""
+    lib = _lib()
+    I64, P, I = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    fn = lib.fp8q_grouped_gemm_segments
+    fn.argtypes = [P, I64, P, I, I64, I64, P, I64, I64, P, I, I64, I64, I64, P, I64, P, P, I64, I64, I64, I64, I64,
+                   I64, P]
+    fn.restype = ctypes.c_int
+    K = 1024
+    rc = fn(0x10000, K, 0x30000, 0, K // 128, 1, 0x20000, N * K, K, 0x40000, 0, (N // 128) * (K // 128), K // 128, 1,
+            0x50000, N, 0x60000, None, S, T, 1, N, K, 0, None)
+    assert rc == status
+
+
 def test_binding_reads_scale_layout_from_strides():
     import fp8_group_quant_amd as fq
     row = fq.alloc_scales(None, 6, 4, "f32", "row", "cpu")
