@@ -4,8 +4,7 @@ One step = the whole hot path over one batch of synthetic input resident in HBM:
 per-token-group quantization of bf16 activations (UE8M0 column-major scales) followed by
 the 1x128 x 128x128 block-scaled FP8 GEMM against e4m3 weights, bf16 output. The default
 workload is the dense DeepSeek-V3-like projection at M = 4096 (X [4096, 7168], W [4096,
-7168]); --workload picks another named shape for reporting (extra lines are only printed
-when asked for).
+7168]); --workload picks another named shape for the step line.
 
 Timing: W untimed warm-up steps, then exactly K steps between two synchronizations,
 measured with HIP events on the stream the kernels run on. The per-kernel roofline figures
@@ -13,12 +12,24 @@ come from two more event-timed loops of K launches of each kernel alone. To defe
 Infinity Cache and the L2s, the steps rotate over enough independent input/output buffer
 sets that the working set exceeds 1 GB.
 
-The CPU baseline is the plain oracle (single-threaded C), timed on a bounded sample of the
-same workload in the same run and scaled to the metric's unit.
+Besides the step line's headline figures, the same JSON line carries:
+  configs      every named workload (tiny; dense M = 1, 16, 128, 4096; the fused silu
+               down-projection; the masked MoE; MXFP8 8192^3): each kernel's duration,
+               rate and fraction of the roofline that binds it, timed as a captured HIP graph
+               of back-to-back launches (so microsecond kernels are not timed against the
+               host's launch rate) over >= 1 GB of rotating buffers where memory allows
+  ceilings     reference kernels moving the same bytes with no arithmetic: a bf16 -> byte
+               copy of the quant's traffic, and a read of the small-M GEMM's weights
+  parity       a gate in the same run: the dense M = 4096 quant output compared byte for
+               byte with the CPU oracle, and sampled GEMM outputs (>= 4096 and one whole
+               256 x 256 tile) checked with the parity tests' tolerance rule
+  cpu_baseline the plain CPU oracle timed on the host's cores (all of them, and one),
+               on bounded samples of the same workload, scaled to the metric's unit
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -33,6 +44,7 @@ METRIC = "block-FP8 GEMM TFLOP/s & % MFMA peak; group-quant GB/s & % HBM peak"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+BENCH_LIB = os.path.join(ROOT, "fp8_group_quant_amd", "libfp8q_bench.so")
 
 
 def _kernel_source_tag(name: str) -> str:
@@ -70,6 +82,11 @@ def quant_bytes(rows: int, K: int, G: int, in_bytes: int, scale_bytes: int, silu
     return rows * (width * in_bytes + K + (K // G) * scale_bytes)
 
 
+def gemm_bytes(M: int, N: int, K: int, sa_bytes: int, sb_bytes: int) -> int:
+    """Algorithmic bytes of one block-scaled GEMM: A, B and their scales once, Y (bf16) once."""
+    return M * K + N * K + M * (K // 128) * sa_bytes + (-(-N // 128)) * (K // 128) * sb_bytes + M * N * 2
+
+
 def build_workload(name: str):
     import synth
     if name.startswith("dense"):
@@ -82,6 +99,293 @@ def build_workload(name: str):
     raise SystemExit(f"unknown workload {name!r}")
 
 
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def graph_time_ms(fn, n: int) -> float:
+    """Average ms per launch of fn(0..n-1) captured into one HIP graph and replayed (after an
+    untimed replay): the launches run back to back on the GPU."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(min(n, 3)):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    del g
+    return ms
+
+
+def _nsets(set_bytes: int, cap: int = 8) -> int:
+    return max(1, min(cap, -(-(1 << 30) // max(set_bytes, 1))))
+
+
+# --------------------------------------------------------------------------- ceilings
+def _bench_lib():
+    lib = ctypes.CDLL(BENCH_LIB)
+    for name in ("fp8q_bench_copy", "fp8q_bench_stream"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+    lib.fp8q_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.fp8q_bench_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    return lib
+
+
+def ceilings(launches: int) -> dict:
+    """The copy and stream reference kernels at the sizes of the dense workload."""
+    import torch
+    lib = _bench_lib()
+    dev = torch.device("cuda", 0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    M, K, N = 4096, 7168, 4096
+    out = {}
+    ns = _nsets(3 * M * K)
+    xs = [torch.zeros((M, K), dtype=torch.int16, device=dev) for _ in range(ns)]
+    qs = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(ns)]
+    stream = lambda: torch.cuda.current_stream().cuda_stream
+    best = None
+    for grid in (2048, 4096, 8192):
+        def cp(i, grid=grid):
+            rc = lib.fp8q_bench_copy(xs[i % ns].data_ptr(), qs[i % ns].data_ptr(), M * K, grid, stream())
+            assert rc == 0, rc
+        ms = graph_time_ms(cp, launches)
+        if best is None or ms < best[0]:
+            best = (ms, grid)
+    nbytes = 3 * M * K
+    out["copy"] = {"what": "bf16 -> byte copy, the dense M=4096 quant's traffic without scales",
+                   "bytes": nbytes, "us": round(best[0] * 1e3, 2),
+                   "GB/s": round(nbytes / (best[0] * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(nbytes / (best[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "grid": best[1]}
+    del xs, qs
+    ns = _nsets(N * K, 40)
+    ws = [torch.zeros((N, K), dtype=torch.uint8, device=dev) for _ in range(ns)]
+    sink = torch.empty(cus * 256, dtype=torch.int32, device=dev)
+
+    def rd(i):
+        rc = lib.fp8q_bench_stream(ws[i % ns].data_ptr(), N * K, sink.data_ptr(), cus, stream())
+        assert rc == 0, rc
+    ms = graph_time_ms(rd, launches)
+    out["weight_stream"] = {"what": "read of the dense weights W [4096, 7168] once, one slice per CU",
+                            "bytes": N * K, "us": round(ms * 1e3, 2), "GB/s": round(N * K / (ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(N * K / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del ws
+    torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------- configs
+def _rec(cfg, workload, kernel, ms, bound, flops=None, nbytes=None, extra=None):
+    rec = {"config": cfg, "workload": workload, "kernel": kernel, "us": round(ms * 1e3, 2), "bound": bound}
+    if flops:
+        t = flops / (ms * 1e-3) / 1e12
+        rec["TFLOP/s"] = round(t, 1)
+    if nbytes:
+        rec["GB/s"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        rec["algorithmic_bytes"] = int(nbytes)
+    if bound == "mfma":
+        rec["frac"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
+    elif bound == "hbm":
+        rec["frac"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    if extra:
+        rec.update(extra)
+    return rec
+
+
+def configs(launches: int, ceil: dict | None) -> list:
+    """One record per kernel of every named workload (graph-replayed launch loops)."""
+    import torch
+    import fp8_group_quant_amd as fq
+    import synth
+    dev = torch.device("cuda", 0)
+    recs = []
+    copy_gbs = ceil["copy"]["GB/s"] if ceil else None
+    stream_gbs = ceil["weight_stream"]["GB/s"] if ceil else None
+
+    def note(r):
+        recs.append(r)
+        print(json.dumps(r), file=sys.stderr, flush=True)
+
+    # c1 tiny, c2 dense (M = 1, 16, 128, 4096) and c3 (fused silu): quant then GEMM, rotating
+    # buffer sets. Binding roofline: the quant streams HBM at M = 4096 and 8192 (smaller M is
+    # latency-bound); the GEMM is bound by HBM (reading W) for M <= 128 and by the matrix
+    # cores at M = 4096 and 8192; the tiny workload is latency-bound throughout.
+    weights = {}
+    for cfg, w in (("c1", synth.TINY), ("c2", synth.dense(1)), ("c2", synth.dense(16)), ("c2", synth.dense(128)),
+                   ("c2", synth.dense(4096)), ("c3", synth.SILU)):
+        M, K, N, G = w.M, w.K, w.N, w.G
+        x = torch.from_numpy(synth.quant_input(w)).to(dev).view(torch.bfloat16)
+        key = (w.seed, N, K)
+        if key not in weights:
+            wq, wsc = synth.weights(w)
+            weights = {key: (torch.from_numpy(wq).to(dev), torch.from_numpy(wsc).to(dev))}
+        wd, wsd = weights[key]
+        set_bytes = x.numel() * 2 + M * K + wd.numel() + M * N * 2
+        ns = _nsets(set_bytes, 40)
+        sets = [dict(x=x.clone(), q=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                     s=fq.alloc_scales(None, M, K // G, w.scale_fmt, w.layout, dev), w=wd.clone(), sw=wsd.clone(),
+                     y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(ns)]
+        qf = fq.fp8q_silu_mul_group_quant if w.silu else fq.fp8q_group_quant
+        sb = 1 if w.scale_fmt == "ue8m0" else 4
+        big = M >= 4096
+        ms = graph_time_ms(lambda i: qf(sets[i % ns]["x"], sets[i % ns]["q"], sets[i % ns]["s"], G), launches)
+        qb = quant_bytes(M, K, G, 2, sb, w.silu)
+        extra = {"frac_copy": round(qb / (ms * 1e-3) / 1e9 / copy_gbs, 4)} if copy_gbs and big else None
+        note(_rec(cfg, w.name, "silu_mul_group_quant" if w.silu else "group_quant", ms, "hbm" if big else "latency",
+                  nbytes=qb, extra=extra))
+        ms = graph_time_ms(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["q"], sets[i % ns]["s"], sets[i % ns]["w"],
+                                                             sets[i % ns]["sw"], sets[i % ns]["y"]), launches)
+        gb = gemm_bytes(M, N, K, sb, 4)
+        bound = "latency" if w.name == "tiny" else ("mfma" if big else "hbm")
+        extra = None
+        if bound == "hbm" and stream_gbs:
+            extra = {"frac_weight_stream": round(gb / (ms * 1e-3) / 1e9 / stream_gbs, 4)}
+        note(_rec(cfg, w.name, "gemm_blockscaled", ms, bound, flops=2.0 * M * N * K, nbytes=gb, extra=extra))
+        del sets, x
+        torch.cuda.empty_cache()
+    del weights
+    torch.cuda.empty_cache()
+
+    # c4 masked MoE: masked quant and the masked grouped GEMM over the 32 experts
+    w = synth.MASKED
+    E, cap, K, N, G = w.E, w.M, w.K, w.N, w.G
+    mm = synth.masked_rows(w.seed, E, cap)
+    rows = int(mm.sum())
+    x = torch.from_numpy(np.stack([synth.quant_input(w, e) for e in range(E)])).to(dev).view(torch.bfloat16)
+    mmd = torch.from_numpy(mm).to(dev)
+    q = torch.empty((E, cap, K), dtype=torch.uint8, device=dev)
+    sq = fq.alloc_scales(E, cap, K // G, "ue8m0", "col", dev)
+    ms = graph_time_ms(lambda i: fq.fp8q_group_quant(x, q, sq, G, masked_m=mmd, expected_m=cap // 2), launches)
+    note(_rec("c4", w.name, "group_quant_masked", ms, "hbm", nbytes=quant_bytes(rows, K, G, 2, 1, False),
+              extra={"sum_masked_m": rows}))
+    del x
+    wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+    for e in range(E):
+        a, b = synth.weights(w, e)
+        wq[e].copy_(torch.from_numpy(a))
+        ws[e].copy_(torch.from_numpy(b))
+    y = torch.empty((E, cap, N), dtype=torch.bfloat16, device=dev)
+    ms = graph_time_ms(lambda i: fq.fp8q_grouped_gemm_masked(q, sq, wq, ws, y, mmd, cap // 2), max(4, launches // 4))
+    active = int((mm > 0).sum())
+    gb = rows * K + active * N * K + rows * (K // 128) + active * (N // 128) * (K // 128) * 4 + rows * N * 2
+    note(_rec("c4", w.name, "grouped_gemm_masked", ms, "hbm", flops=2.0 * rows * N * K, nbytes=gb,
+              extra={"sum_masked_m": rows}))
+    del wq, ws, q, y
+    torch.cuda.empty_cache()
+
+    # c5 MXFP8 8192^3, E8M0 row-major bytes [rows, K/32]
+    w = synth.MX
+    a, b, ea, eb = synth.mx_operands(w)
+    ad, bd, ead, ebd = (torch.from_numpy(t).to(dev) for t in (a, b, ea, eb))
+    ns = _nsets(a.nbytes + b.nbytes + w.M * w.N * 2, 4)
+    sets = [dict(a=ad.clone(), b=bd.clone(), ea=ead.clone(), eb=ebd.clone(),
+                 y=torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)) for _ in range(ns)]
+    ms = graph_time_ms(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
+                                                         sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32),
+                       max(4, launches // 4))
+    note(_rec("c5", w.name, "gemm_mx32", ms, "mfma", flops=2.0 * w.M * w.N * w.K,
+              nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
+              extra={"scales": "E8M0 bytes, row-major [rows, K/32]"}))
+    del sets
+    torch.cuda.empty_cache()
+    return recs
+
+
+# --------------------------------------------------------------------------- parity gate
+def parity_gate(w, x_host, w_host, sw_host, q_dev, s_dev, y_dev) -> dict:
+    """The step's own outputs (set 0) against the CPU oracle: every quant byte, and sampled
+    GEMM outputs under the parity tests' rule (tests/gemm_check.py)."""
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gemm_check import check
+    t0 = time.perf_counter()
+    fmt = oracle.SCALE_UE8M0 if w.scale_fmt == "ue8m0" else oracle.SCALE_F32
+    qo, so = oracle.group_quant(x_host, w.G, fmt, w.layout, silu=w.silu)
+    qg = q_dev.cpu().numpy()
+    sg = s_dev.cpu().numpy() if w.layout == "row" else s_dev.t().cpu().numpy()
+    q_diff = int(np.count_nonzero(qg != qo))
+    s_diff = int(np.count_nonzero(sg.view(np.uint8) != np.ascontiguousarray(so).view(np.uint8)))
+    g = np.random.default_rng(2024)
+    M, N = w.M, w.N
+    ms = g.integers(0, M, 5000)
+    ns = g.integers(0, N, 5000)
+    m0 = int(g.integers(0, -(-M // 256))) * 256
+    n0 = int(g.integers(0, -(-N // 256))) * 256
+    tm, tn = np.meshgrid(np.arange(m0, min(M, m0 + 256)), np.arange(n0, min(N, n0 + 256)), indexing="ij")
+    ms = np.concatenate([ms, tm.ravel()])
+    ns = np.concatenate([ns, tn.ravel()])
+    ys, ss = oracle.gemm_block128(qo, so, w_host, sw_host, fmt, w.layout, at=(ms, ns))
+    yg = y_dev.view(__import__("torch").int16).cpu().numpy().view(np.uint16)[ms, ns]
+    gate = {"quant_rows": M, "quant_codes_differing": q_diff, "quant_scale_bytes_differing": s_diff}
+    try:
+        st = check(yg, ys, ss, w.K, "bench parity gate", cls="quant")
+        gate["gemm"] = {k: st[k] for k in ("n", "n_cancel", "max_excess_over_S", "gamma", "n_beyond_gamma", "frob",
+                                            "frob_bf16_floor")}
+        gemm_ok = True
+    except AssertionError as err:
+        gate["gemm"] = {"n": int(ms.size), "failure": str(err)[:300]}
+        gemm_ok = False
+    gate["pass"] = bool(q_diff == 0 and s_diff == 0 and gemm_ok)
+    gate["seconds"] = round(time.perf_counter() - t0, 1)
+    return gate
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def _oracle_step_time(w, x_host, w_host, sw_host, rows: int, cols: int) -> tuple[float, float]:
+    """Seconds the oracle takes for `rows` quantized rows and rows x cols GEMM outputs, and the
+    full step time extrapolated per row and per output."""
+    import oracle
+    M, N = w.M, w.N
+    fmt = oracle.SCALE_UE8M0 if w.scale_fmt == "ue8m0" else oracle.SCALE_F32
+    t0 = time.perf_counter()
+    q, s = oracle.group_quant(x_host[:rows], w.G, fmt, w.layout, silu=w.silu)
+    t1 = time.perf_counter()
+    ms = np.repeat(np.arange(rows), cols)
+    ns = np.tile(np.arange(cols), rows)
+    oracle.gemm_block128(q, s, w_host, sw_host, fmt, w.layout, at=(ms, ns))
+    t2 = time.perf_counter()
+    return t2 - t0, (t1 - t0) / rows * M + (t2 - t1) / (rows * cols) * (M * N)
+
+
+def cpu_baseline(w, x_host, w_host, sw_host, rows: int) -> dict:
+    """The plain oracle on the host's cores (its OpenMP loops over rows and outputs; each
+    row or output is computed whole by one thread), on a bounded sample of the same
+    workload, scaled to the step: all cores, and one core."""
+    import oracle
+    flops = 2.0 * w.M * w.N * w.K
+    nproc = os.cpu_count()
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    threads = oracle.max_threads()
+    rows_all = min(w.M, 4 * rows)
+    t_all, step_all = _oracle_step_time(w, x_host, w_host, sw_host, rows_all, 1024)
+    with oracle.threads(1):
+        t_one, step_one = _oracle_step_time(w, x_host, w_host, sw_host, rows // 2, 512)
+    return {"value": round(flops / step_all / 1e12, 8), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_all} rows quantized + {rows_all}x1024 GEMM outputs of the same workload on {threads} "
+                      f"threads ({t_all:.1f} s); step time extrapolated per row / per output = {step_all:.1f} s",
+            "nproc": nproc, "cpus_available": avail,
+            "single_core": {"value": round(flops / step_one / 1e12, 8), "unit": "TFLOP/s", "cores": 1,
+                            "sample": f"{rows // 2} rows + {rows // 2}x512 outputs ({t_one:.1f} s); "
+                                      f"extrapolated step = {step_one:.0f} s"}}
+
+
+# --------------------------------------------------------------------------- the step line
 def run(args) -> dict:
     import torch
     import fp8_group_quant_amd as fq
@@ -139,8 +443,7 @@ def run(args) -> dict:
         """average ms of n back-to-back launches between two events on the kernels' stream,
         after `warm` untimed launches queued right before them (the GPU is busy, not idle
         after a synchronize, when the first timed launch starts)"""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0, e1 = _events()
         torch.cuda.synchronize()
         for i in range(warm):
             fn(n + i)
@@ -185,6 +488,11 @@ def run(args) -> dict:
     gemm_step_tflops = flops / (gemm_in_step * 1e-3) / 1e12
     value = flops / (ms_step * 1e-3) / 1e12
 
+    # the outputs of set 0, for the parity gate (the last step that used set 0 wrote them)
+    step(0)
+    torch.cuda.synchronize()
+    out_set = sets[0]
+
     traffic = _measured_traffic("gemm.hip", w.name)
     out = {
         "metric": METRIC,
@@ -218,32 +526,18 @@ def run(args) -> dict:
                                  "frac_mfma": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)},
         },
     }
+    del sets[1:]
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        ceil = ceilings(args.config_launches)
+        out["ceilings"] = ceil
+        out["kernels"]["group_quant"]["frac_copy"] = round(quant_gbs / ceil["copy"]["GB/s"], 4)
+        out["configs"] = configs(args.config_launches, ceil)
+    if not args.no_parity:
+        out["parity"] = parity_gate(w, x_host, w_host, sw_host, out_set["q"], out_set["s"], out_set["y"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x_host, w_host, sw_host, args.cpu_rows)
     return out
-
-
-def cpu_baseline(w, x_host, w_host, sw_host, rows: int) -> dict:
-    """Times the plain oracle on a bounded sample of the same workload: quantization of
-    `rows` activation rows, then the GEMM outputs of those rows against 512 weight rows.
-    The per-row and per-output costs are scaled up to the full step and reported in the
-    metric's unit."""
-    import oracle
-    M, K, N, G = w.M, w.K, w.N, w.G
-    fmt = oracle.SCALE_UE8M0 if w.scale_fmt == "ue8m0" else oracle.SCALE_F32
-    t0 = time.perf_counter()
-    q, s = oracle.group_quant(x_host[:rows], G, fmt, w.layout, silu=w.silu)
-    t1 = time.perf_counter()
-    cols = min(N, 512)
-    ms = np.repeat(np.arange(rows), cols)
-    ns = np.tile(np.arange(cols), rows)
-    oracle.gemm_block128(q, s, w_host, sw_host, fmt, w.layout, at=(ms, ns))
-    t2 = time.perf_counter()
-    t_step = (t1 - t0) / rows * M + (t2 - t1) / (rows * cols) * (M * N)
-    return {"value": round(2.0 * M * N * K / t_step / 1e12, 8), "unit": "TFLOP/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{rows} rows quantized + {rows}x{cols} GEMM outputs of the same workload "
-                      f"({t2 - t0:.1f} s); step time extrapolated per row / per output = {t_step:.0f} s"}
 
 
 def _timed(fn, n, warm=0):
@@ -260,10 +554,6 @@ def _timed(fn, n, warm=0):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
-
-
-def _nsets(set_bytes: int, cap: int = 8) -> int:
-    return max(1, min(cap, -(-(1 << 30) // max(set_bytes, 1))))
 
 
 SUITE_SECTIONS = ("flat", "variants", "masked", "moe_down", "mxfp8")
@@ -483,7 +773,11 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_m4096")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--config-launches", type=int, default=40,
+                    help="launches per graph-replayed loop in the configs and ceilings records")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the configs and ceilings records")
+    ap.add_argument("--no-parity", action="store_true", help="skip the in-run parity gate")
     ap.add_argument("--only", default=None,
                     help="with --suite: comma-separated sections to run (" + ",".join(SUITE_SECTIONS) + ")")
     ap.add_argument("--suite", action="store_true",

@@ -1,7 +1,9 @@
-"""Builds libfp8q.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Builds libfp8q.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
+libfp8q_bench.so (csrc_bench/: the benchmark's reference copy and stream kernels, loaded only
+by bench.py).
 
-Every call recompiles: objects go to fp8_group_quant_amd/_build/, the library to
-fp8_group_quant_amd/libfp8q.so.
+Every call recompiles: objects go to fp8_group_quant_amd/_build/, the libraries next to this
+file.
 """
 from __future__ import annotations
 
@@ -14,8 +16,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+CSRC_BENCH = os.path.join(HERE, "csrc_bench")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp8q.so")
+BENCH_LIB = os.path.join(HERE, "libfp8q_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -43,17 +47,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    bench_srcs = sorted(glob.glob(os.path.join(CSRC_BENCH, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + bench_srcs))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], BENCH_LIB, verbose)
     return LIB
 
 
