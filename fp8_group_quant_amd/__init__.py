@@ -43,6 +43,9 @@ _SIGNATURES = {
                               _I64, _I64, _INT, _P, _I64, _P],
     "fp8q_gemm_blockscaled": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _P, _INT, _I64, _I64, _P, _I64,
                               _I64, _I64, _I64, _INT, _P],
+    "fp8q_gemm_blockscaled_ws": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _P, _INT, _I64, _I64, _P, _I64,
+                                 _I64, _I64, _I64, _INT, _P, _I64, _P],
+    "fp8q_gemm_workspace_size": [_I64, _I64, _I64, _INT],
     "fp8q_grouped_gemm_masked": [_P, _I64, _I64, _P, _INT, _I64, _I64, _I64, _P, _I64, _I64, _P, _INT,
                                  _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64, _P],
     "fp8q_grouped_gemm_segments": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _I64, _P, _INT, _I64, _I64, _I64,
@@ -77,7 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         if fn is None:  # calling it later raises AttributeError; tests check every export
             continue
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name in ("fp8q_status_string", "fp8q_last_error") else _INT
+        fn.restype = (ctypes.c_char_p if name in ("fp8q_status_string", "fp8q_last_error")
+                      else _I64 if name == "fp8q_gemm_workspace_size" else _INT)
     _lib = lib
     return lib
 
@@ -225,14 +229,29 @@ def _u8(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.uint8) if t.dtype != torch.uint8 else t
 
 
+_WS_SIZES: dict = {}
+
+
+def fp8q_gemm_workspace_size(M: int, N: int, K: int, mode: int = GEMM_BLOCK128) -> int:
+    """Bytes of workspace with which fp8q_gemm_blockscaled_ws takes its split-K path for this
+    shape on the current device (0: none needed)."""
+    key = (torch.cuda.current_device(), M, N, K, mode)
+    if key not in _WS_SIZES:
+        _WS_SIZES[key] = int(load_library().fp8q_gemm_workspace_size(M, N, K, mode))
+    return _WS_SIZES[key]
+
+
 def fp8q_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
-                          y: torch.Tensor, mode: int = GEMM_BLOCK128, stream=None) -> None:
+                          y: torch.Tensor, mode: int = GEMM_BLOCK128, stream=None,
+                          workspace: torch.Tensor | None = None) -> None:
     """Y[M, N] (bf16) = dequant(a [M, K]) @ dequant(b [N, K])^T.
     BLOCK128: sa viewed as [M, K/128], sb as [ceil(N/128), K/128] (float32 or uint8 UE8M0;
     sa may be int32 packed UE8M0 words [M, K/512]).
     MX32: sa [M, K/32], sb [N, K/32], uint8 E8M0; or either as int32 packed words [rows, K/128]
     (the four E8M0 bytes of one 128-wide K step per word; a [K/128, rows] storage viewed
-    transposed gives the column-major words that load fastest)."""
+    transposed gives the column-major words that load fastest).
+    Calls fp8q_gemm_blockscaled_ws: when the shape can use a workspace and none is given, one
+    is taken from torch's allocator on a's device (stream-ordered, capturable)."""
     a8, b8 = _u8(a), _u8(b)
     M, K = a8.shape
     N = b8.shape[0]
@@ -240,10 +259,16 @@ def fp8q_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb
         raise ValueError("shape mismatch")
     if a8.stride(1) != 1 or b8.stride(1) != 1 or y.stride(1) != 1:
         raise ValueError("innermost dimensions must be contiguous")
-    _check(load_library().fp8q_gemm_blockscaled(
+    if workspace is None and mode == GEMM_BLOCK128:
+        nbytes = fp8q_gemm_workspace_size(M, N, K, mode)
+        if nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=a8.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().fp8q_gemm_blockscaled_ws(
         _ptr(a8), a8.stride(0), _ptr(sa), _scale_fmt_of(sa), sa.stride(0), sa.stride(1),
         _ptr(b8), b8.stride(0), _ptr(sb), _scale_fmt_of(sb), sb.stride(0), sb.stride(1),
-        _ptr(y), y.stride(0), M, N, K, mode, _stream(stream)))
+        _ptr(y), y.stride(0), M, N, K, mode, ws_ptr, ws_bytes, _stream(stream)))
 
 
 def fp8q_grouped_gemm_masked(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,

@@ -99,18 +99,12 @@ int grouped_rows_entry(const std::string& pre, const uint8_t* a, int64_t lda, co
   return launch_gemm_block128(p, expected_rows, static_cast<hipStream_t>(stream));
 }
 
-}  // namespace
-}  // namespace fp8q
-
-extern "C" {
-
-int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t sa_sm,
-                          int64_t sa_sk, const uint8_t* b, int64_t ldb, const void* sb, int sb_fmt,
-                          int64_t sb_sn, int64_t sb_sk, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
-                          int64_t K, int mode, void* stream) {
-  using namespace fp8q;
+// the dense call, with an optional fp32 workspace (nullptr: the paths that need none)
+int dense_entry(const std::string& pre, const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t sa_sm,
+                int64_t sa_sk, const uint8_t* b, int64_t ldb, const void* sb, int sb_fmt, int64_t sb_sn,
+                int64_t sb_sk, uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, int mode, float* ws,
+                int64_t ws_bytes, void* stream) {
   set_error("");
-  const std::string pre = "fp8q_gemm_blockscaled: ";
   int rc = check_operands(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy, M,
                           N, K, mode);
   if (rc != FP8Q_OK || M == 0 || N == 0 || K == 0) return rc;
@@ -138,8 +132,48 @@ int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda, const void* sa, int sa_
   p.sa_fmt = p.sa_packed ? FP8Q_SCALE_UE8M0 : sa_fmt;
   p.sb_packed = sb_fmt == FP8Q_SCALE_UE8M0_PACKED ? 1 : 0;
   p.sb_fmt = p.sb_packed ? FP8Q_SCALE_UE8M0 : sb_fmt;
+  p.ws = ws;
+  p.ws_bytes = ws_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return mode == FP8Q_GEMM_MX32 ? launch_gemm_mx32(p, s) : launch_gemm_block128(p, 0, s);
+}
+
+}  // namespace
+}  // namespace fp8q
+
+extern "C" {
+
+int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t sa_sm,
+                          int64_t sa_sk, const uint8_t* b, int64_t ldb, const void* sb, int sb_fmt,
+                          int64_t sb_sn, int64_t sb_sk, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                          int64_t K, int mode, void* stream) {
+  return fp8q::dense_entry("fp8q_gemm_blockscaled: ", a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn,
+                           sb_sk, y, ldy, M, N, K, mode, nullptr, 0, stream);
+}
+
+int fp8q_gemm_blockscaled_ws(const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t sa_sm,
+                             int64_t sa_sk, const uint8_t* b, int64_t ldb, const void* sb, int sb_fmt,
+                             int64_t sb_sn, int64_t sb_sk, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                             int64_t K, int mode, void* workspace, int64_t workspace_bytes, void* stream) {
+  using namespace fp8q;
+  const std::string pre = "fp8q_gemm_blockscaled_ws: ";
+  if (workspace_bytes < 0) {
+    set_error("");
+    return fail(FP8Q_EINVAL, pre + "negative workspace size");
+  }
+  if (workspace && !aligned(workspace, 16)) {
+    set_error("");
+    return fail(FP8Q_EALIGN, pre + "workspace must be 16-byte aligned");
+  }
+  return dense_entry(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy, M, N, K, mode,
+                     static_cast<float*>(workspace), workspace ? workspace_bytes : 0, stream);
+}
+
+int64_t fp8q_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode) {
+  using namespace fp8q;
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || mode != FP8Q_GEMM_BLOCK128) return 0;
+  if (M == 0 || N == 0 || K == 0 || check_current_device() != FP8Q_OK) return 0;
+  return gemm_workspace_bytes(M, N, K);
 }
 
 int fp8q_grouped_gemm_masked(const uint8_t* a, int64_t a_se, int64_t lda, const void* sa, int sa_fmt,

@@ -69,9 +69,14 @@ struct GemmParams {
   int sa_packed;  // UE8M0 activation scales packed 4 K blocks per 32-bit word (sa strides in words)
   int sb_packed;  // MX32 only: E8M0 weight scales packed likewise (sb strides in words)
   int xcds;       // XCDs of the device (workgroup b runs on XCD b % xcds)
+  float* ws;          // dense BLOCK128 only: fp32 workspace of the split-K small-M path, or nullptr
+  int64_t ws_bytes;   // its size
 };
 
 int launch_gemm_block128(const GemmParams& p, int64_t expected_m, hipStream_t stream);
+// Bytes of workspace with which a dense BLOCK128 GEMM of this shape takes the split-K path on
+// the current device (0: it needs none).
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int launch_gemm_mx32(const GemmParams& p, hipStream_t stream);
 
 }  // namespace fp8q

@@ -188,8 +188,6 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int r, int lane) {
   return v;
 }
 
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // float value of a raw scale word: fp32 bits, or a UE8M0 byte b -> 2^(b-127)
 template <int FMT>
 __device__ __forceinline__ float scale_value(uint32_t raw) {
@@ -1731,6 +1729,320 @@ bool try_skinny_dma(const GemmParams& p, hipStream_t s) {
   return rc == 0;
 }
 
+// ------------------------------------------------------------------ small M, split K
+// For 32 < M <= 128 the kernels above give every workgroup 16 columns and all of K, so each
+// streams all M x K of A through its CU (0.9 MB at M = 128, 256 times over). Here a workgroup
+// owns C = 64 NF columns (four waves, NF 16-column MFMA slices each) and one of S contiguous
+// ranges of the K blocks, so A is read once per C columns and per range while the grid
+// (ceil(N / C) x S workgroups) still fills the chip.
+//   * The A rows of the whole range go to LDS (straight from global memory, whole cache
+//     lines) before anything else is issued, so the only loads still in flight afterwards
+//     are the B fragments, and the waits the compiler places before each MFMA wait for
+//     exactly the fragment it reads: the loop runs while B streams in.
+//   * Each wave loads its B fragments of the whole range into registers (buffer loads of
+//     each row's contiguous K range, issued back to back, so the rows stream from HBM
+//     together).
+//   * The steps are software-pipelined: step i reads the A fragments of block i + 1 from
+//     LDS, runs the MFMAs of block i (each into its own registers) and scales and adds the
+//     products of block i - 1, so LDS, the matrix core and the vector ALU work at once.
+// With S > 1 the partial sums go to an fp32 workspace [S][M][N] and a second kernel adds
+// them in range order (fixed, so results are reproducible) and rounds to bf16; with S == 1
+// the bf16 output is stored directly.
+template <int SM>
+struct SplitCfg {
+  static constexpr int MR = 16 * SM;              // A rows held per block
+  static constexpr int NF = SM == 8 ? 2 : 1;      // 16-column slices per wave
+  static constexpr int C = 64 * NF;               // columns per workgroup
+  static constexpr int kMaxBlocks = SM == 8 ? 7 : 14;  // K blocks of a range (registers)
+  static constexpr int kLoads = MR / 32;          // 1 KB A pieces per wave and block
+  static constexpr int kA = kMaxBlocks * MR * BK; // 112 KB
+  static constexpr int kLds = kA + kMaxBlocks * (MR + 1) * 4;
+  static_assert(kLds <= 160 * 1024, "A range and scale tables fit in LDS");
+  static_assert(C % 128 == 0 || 128 % C == 0, "a column tile lies in one weight scale block");
+};
+
+template <int SM, int SA_FMT, int SB_FMT>
+__global__ __launch_bounds__(256, 1) void gemm_splitk_kernel(GemmParams p, int S) {
+  using D = SplitCfg<SM>;
+  constexpr int MR = D::MR, NF = D::NF, KL = D::kLoads, NB = D::kMaxBlocks;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint8_t* const A = p.a;
+  const uint8_t* const B = p.b;
+  const int M = static_cast<int>(p.M), N = static_cast<int>(p.N), nkb = static_cast<int>(p.K / BK);
+  const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = blockIdx.x % S, nt = blockIdx.x / S;
+  const int n0 = nt * D::C;
+  const int kb0 = (nkb * ks) / S, nblk = (nkb * (ks + 1)) / S - kb0;  // 1 <= nblk <= NB (host)
+  float* const sa_tab = reinterpret_cast<float*>(smem + D::kA);     // [nblk][MR]
+  float* const sb_tab = sa_tab + NB * MR;                           // [nblk]
+
+  // 1. scale tables of the range: rows past M repeat row M - 1 (their outputs are not stored)
+  constexpr int U = (NB * MR + 255) / 256;  // entries per thread
+  const int total = nblk * MR;
+  uint32_t tv[U];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const int idx = tid + u * 256;
+    tv[u] = 0;
+    if (idx < total) {
+      const int64_t si = sa_index(p, min(idx % MR, M - 1), kb0 + idx / MR);
+      tv[u] = SA_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(p.sa)[si] : static_cast<const uint8_t*>(p.sa)[si];
+    }
+  }
+  uint32_t tw = 0;
+  if (tid < nblk) {
+    const int64_t bi = (n0 / 128) * p.sb_sn + static_cast<int64_t>(kb0 + tid) * p.sb_sk;
+    tw = SB_FMT == FP8Q_SCALE_F32 ? static_cast<const uint32_t*>(p.sb)[bi] : static_cast<const uint8_t*>(p.sb)[bi];
+  }
+
+  // 2. A blocks kb0 .. kb0 + nblk - 1, rows 0 .. MR - 1 (rows past M read row M - 1). Block i
+  // is at LDS i * MR * BK; the wave's 1 KB pieces q = wave * KL + j hold rows 8q .. 8q + 7
+  // (lane l: row 8q + l/8, LDS chunk l%8 = logical chunk (l%8) ^ swz(row)).
+  {
+    uint32_t voff[KL];
+#pragma unroll
+    for (int j = 0; j < KL; j++) {
+      const int row = (wave * KL + j) * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
+      voff[j] = static_cast<uint32_t>(min(row, M - 1) * lda + c * 16);
+    }
+    const uint32_t base = lds_addr(smem);
+    for (int i = 0; i < nblk; i++) {
+#pragma unroll
+      for (int j = 0; j < KL; j++) dma16(base + i * MR * BK + (wave * KL + j) * 1024, A + (kb0 + i) * BK, voff[j]);
+    }
+  }
+  asm volatile("" ::: "memory");
+
+  // 3. B: rows n0 + 16 (NF wave + f) + lane%16 of the range, fragments straight to registers
+  // (rows past N read as zeros: the buffer ends at row N - 1). The first kLead blocks now
+  // (blocks past the range repeat the last one, so every wave issues 2 NF kLead loads), each
+  // later one kLead steps ahead of its use: the requests of all CUs then reach memory
+  // roughly in block order, so early blocks return early and the steps overlap the stream.
+  // With 64 rows (a quarter of the MFMAs per step) everything at once measured faster.
+  constexpr int kLead = SM == 8 ? 4 : NB;
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(B + static_cast<int64_t>(n0) * ldb), 0, min(D::C, N - n0) * ldb, kBufWord3);
+  uint32_t wo[NF];
+#pragma unroll
+  for (int f = 0; f < NF; f++) wo[f] = static_cast<uint32_t>(((wave * NF + f) * 16 + l16) * ldb + (lane >> 4) * 16);
+  v8i wf[NF][NB];
+#pragma unroll
+  for (int u = 0; u < kLead; u++) {
+#pragma unroll
+    for (int f = 0; f < NF; f++) wf[f][u] = frag_buffer(rb, wo[f], kb0 + min(u, nblk - 1));
+  }
+  asm volatile("" ::: "memory");
+
+  // 4. the tables and this wave's A pieces have landed once at most the B loads are in flight
+  wait_vmcnt<2 * NF * kLead>();
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const int idx = tid + u * 256;
+    if (idx < total) sa_tab[idx] = scale_value<SA_FMT>(tv[u]);
+  }
+  if (tid < nblk) sb_tab[tid] = scale_value<SB_FMT>(tw);
+  // every wave's A pieces and table entries are in LDS (a bare barrier: __syncthreads would
+  // also wait for the B loads)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  v4f acc[NF][SM];
+#pragma unroll
+  for (int f = 0; f < NF; f++)
+#pragma unroll
+    for (int j = 0; j < SM; j++) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i xf[2][SM];   // A fragments of blocks i (xf[i & 1]) and i + 1
+  v4f pr[2][NF][SM];  // products of blocks i (pr[i & 1]) and i - 1
+  float sv[SM];    // scales of the block being added
+  // products of block b (held in pr[h]) scaled by their row and block scales into acc
+  auto add_block = [&](int h, int b) {
+#pragma unroll
+    for (int j = 0; j < SM; j++)
+#pragma unroll
+      for (int f = 0; f < NF; f++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[f][j][r] = fmaf(pr[h][f][j][r], sv[j], acc[f][j][r]);
+    (void)b;
+  };
+  auto load_scales = [&](int b) {
+    const float sbv = sb_tab[b];
+#pragma unroll
+    for (int j = 0; j < SM; j++) sv[j] = sa_tab[b * MR + j * 16 + l16] * sbv;
+  };
+#pragma unroll
+  for (int j = 0; j < SM; j++) xf[0][j] = frag(smem, j * 16, lane);
+#pragma unroll
+  for (int i = 0; i < NB; i++) {
+    if (i < nblk) {
+      const int h = i & 1;
+      if (i > 0) load_scales(i - 1);  // before the prefetch: LDS reads complete in order
+      if (i + 1 < nblk) {
+        const uint8_t* st = smem + (i + 1) * MR * BK;
+#pragma unroll
+        for (int j = 0; j < SM; j++) xf[h ^ 1][j] = frag(st, j * 16, lane);
+      }
+      if (i + kLead < NB && i + kLead < nblk) {
+#pragma unroll
+        for (int f = 0; f < NF; f++) wf[f][i + kLead] = frag_buffer(rb, wo[f], kb0 + i + kLead);
+      }
+      const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < NF; f++)
+#pragma unroll
+        for (int j = 0; j < SM; j++)
+          pr[h][f][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[f][i], xf[h][j], z, 0, 0, 0, 0, 0, 0);
+      if (i > 0) add_block(h ^ 1, i - 1);
+    }
+  }
+  load_scales(nblk - 1);
+  if ((nblk - 1) & 1)
+    add_block(1, nblk - 1);
+  else
+    add_block(0, nblk - 1);
+
+  // lane holds rows m = 16 j + lane%16, columns n .. n+3, n = n0 + 16 (NF wave + f) + 4 (lane/16)
+#pragma unroll
+  for (int f = 0; f < NF; f++) {
+    const int n = n0 + (wave * NF + f) * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < SM; j++) {
+      const int m = j * 16 + l16;
+      if (m >= M) continue;
+      if (S > 1) {
+        float* prow = p.ws + (static_cast<int64_t>(ks) * M + m) * N;
+        if (n + 3 < N && (N & 3) == 0) {
+          *reinterpret_cast<v4f*>(prow + n) = acc[f][j];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; r++)
+            if (n + r < N) prow[n + r] = acc[f][j][r];
+        }
+      } else {
+        uint16_t* yrow = p.y + m * p.ldy;
+        const uint32_t h0 = bf16_rne(acc[f][j][0]), h1 = bf16_rne(acc[f][j][1]);
+        const uint32_t h2 = bf16_rne(acc[f][j][2]), h3 = bf16_rne(acc[f][j][3]);
+        if (n + 3 < N) {
+          *reinterpret_cast<uint32_t*>(yrow + n) = h0 | (h1 << 16);
+          *reinterpret_cast<uint32_t*>(yrow + n + 2) = h2 | (h3 << 16);
+        } else {
+          if (n < N) yrow[n] = static_cast<uint16_t>(h0);
+          if (n + 1 < N) yrow[n + 1] = static_cast<uint16_t>(h1);
+          if (n + 2 < N) yrow[n + 2] = static_cast<uint16_t>(h2);
+        }
+      }
+    }
+  }
+}
+
+constexpr int kMaxSplit = 16;
+
+// Y[m][n] = bf16( sum over the S ranges, in range order, of part[s][m][n] ); each thread four
+// consecutive columns of one row, all S loads issued before the first add.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
+                                                            uint16_t* __restrict__ y, int64_t ldy) {
+  const int nq = (N + 3) / 4;
+  const int64_t total = static_cast<int64_t>(M) * nq;
+  const int64_t plane = static_cast<int64_t>(M) * N;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; t < total;
+       t += static_cast<int64_t>(gridDim.x) * 256) {
+    const int m = static_cast<int>(t / nq), n = static_cast<int>(t % nq) * 4;
+    const float* src = part + static_cast<int64_t>(m) * N + n;
+    uint16_t* yrow = y + m * ldy;
+    if (n + 3 < N && (N & 3) == 0) {
+      v4f v[kMaxSplit];
+#pragma unroll
+      for (int s = 0; s < kMaxSplit; s++)
+        if (s < S) v[s] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + s * plane));
+      v4f a = v[0];
+#pragma unroll
+      for (int s = 1; s < kMaxSplit; s++)
+        if (s < S) { a[0] += v[s][0]; a[1] += v[s][1]; a[2] += v[s][2]; a[3] += v[s][3]; }
+      *reinterpret_cast<uint32_t*>(yrow + n) = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
+      *reinterpret_cast<uint32_t*>(yrow + n + 2) = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
+    } else {
+      for (int r = 0; r < 4 && n + r < N; r++) {
+        float a = src[r];
+        for (int s = 1; s < S; s++) a += src[r + s * plane];
+        yrow[n + r] = static_cast<uint16_t>(bf16_rne(a));
+      }
+    }
+  }
+}
+
+// The split for a problem on `cus` CUs: sm 16-row slices of A (M <= 64: 4, else 8), the
+// fewest ranges that keep every range within the blocks a workgroup holds, raised (up to
+// kMaxSplit) until the grid fills the chip. Ranges differ by at most one block.
+struct SplitPlan {
+  int sm;      // 4 or 8
+  int S;       // K ranges
+  int64_t ws;  // workspace bytes (0 when S == 1)
+  bool ok;
+};
+
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int cus) {
+  SplitPlan pl{M <= 64 ? 4 : 8, 1, 0, false};
+  if (M <= kSmallMaxM || M > kSkinnyMaxM || K % BK != 0 || N < 1) return pl;
+  const int64_t nkb = K / BK;
+  const int64_t C = pl.sm == 8 ? SplitCfg<8>::C : SplitCfg<4>::C;
+  const int64_t nbmax = pl.sm == 8 ? SplitCfg<8>::kMaxBlocks : SplitCfg<4>::kMaxBlocks;
+  const int64_t tiles = (N + C - 1) / C;
+  const int64_t s_min = (nkb + nbmax - 1) / nbmax;  // ranges short enough for the registers
+  const int64_t s_fill = std::max<int64_t>(1, std::min<int64_t>(cus / tiles, kMaxSplit));
+  const int64_t S = std::min<int64_t>(std::max(s_min, s_fill), nkb);
+  if (S > kMaxSplit || (nkb + S - 1) / S > nbmax) return pl;
+  pl.S = static_cast<int>(S);
+  pl.ws = S > 1 ? S * M * N * 4 : 0;
+  pl.ok = true;
+  return pl;
+}
+
+template <int SM, int SA_FMT, int SB_FMT>
+int launch_splitk_sm(const GemmParams& p, int S, hipStream_t s) {
+  using D = SplitCfg<SM>;
+  auto kern = gemm_splitk_kernel<SM, SA_FMT, SB_FMT>;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, D::kLds) !=
+      hipSuccess)
+    return -1;
+  const int grid = static_cast<int>((p.N + D::C - 1) / D::C) * S;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), D::kLds, s, p, S);
+  if (S > 1) {
+    const int64_t work = p.M * ((p.N + 3) / 4);
+    const int rgrid = static_cast<int>(std::min<int64_t>((work + 255) / 256, 4096));
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rgrid), dim3(256), 0, s, static_cast<const float*>(p.ws), S,
+                       static_cast<int>(p.M), static_cast<int>(p.N), p.y, p.ldy);
+  }
+  return 0;
+}
+
+// The split-K path when the problem fits it and the workspace is large enough; false to use
+// another kernel.
+bool try_splitk(const GemmParams& p, const DeviceShape& ds, hipStream_t s) {
+  const SplitPlan pl = split_plan(p.M, p.N, p.K, ds.cus);
+  if (!pl.ok || (pl.S > 1 && (p.ws == nullptr || p.ws_bytes < pl.ws))) return false;
+  if ((reinterpret_cast<uintptr_t>(p.ws) & 15) != 0) return false;
+  // every offset of the kernel in 31 bits
+  const int64_t lim = int64_t(1) << 31;
+  if (p.M * p.lda >= lim || 128 * p.ldb >= lim || p.N >= (int64_t(1) << 30) || p.K >= lim || p.M * p.ldy >= lim)
+    return false;
+  const bool f = p.sa_fmt == FP8Q_SCALE_F32, g = p.sb_fmt == FP8Q_SCALE_F32;
+  int rc;
+  if (pl.sm == 4) {
+    rc = f ? (g ? launch_splitk_sm<4, FP8Q_SCALE_F32, FP8Q_SCALE_F32>(p, pl.S, s)
+                : launch_splitk_sm<4, FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, pl.S, s))
+           : (g ? launch_splitk_sm<4, FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, pl.S, s)
+                : launch_splitk_sm<4, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, pl.S, s));
+  } else {
+    rc = f ? (g ? launch_splitk_sm<8, FP8Q_SCALE_F32, FP8Q_SCALE_F32>(p, pl.S, s)
+                : launch_splitk_sm<8, FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, pl.S, s))
+           : (g ? launch_splitk_sm<8, FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, pl.S, s)
+                : launch_splitk_sm<8, FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, pl.S, s));
+  }
+  return rc == 0;
+}
+
 template <class C, bool MX, int SA_FMT, int SB_FMT>
 void launch(const GemmParams& p, int grid, hipStream_t s) {
   const size_t lds = (p.masked_m || p.seg_indptr) ? static_cast<size_t>(p.E + 1) * sizeof(int32_t) : 0;
@@ -1872,6 +2184,7 @@ int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t
     return finish("block-scaled GEMM launch");
   }
   if (!grouped && p.M <= kSkinnyMaxM) {
+    if (try_splitk(p, ds, stream)) return finish("block-scaled GEMM launch");
     if (try_skinny_dma(p, stream)) return finish("block-scaled GEMM launch");
     if (a8 && b8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_UE8M0>(p, stream);
     else if (a8) launch_skinny_m<FP8Q_SCALE_UE8M0, FP8Q_SCALE_F32>(p, stream);
@@ -1951,6 +2264,11 @@ int launch_gemm_block128(const GemmParams& p_in, int64_t expected_m, hipStream_t
   else if (b8) launch<C, false, FP8Q_SCALE_F32, FP8Q_SCALE_UE8M0>(p, grid, stream);
   else launch<C, false, FP8Q_SCALE_F32, FP8Q_SCALE_F32>(p, grid, stream);
   return finish("block-scaled GEMM launch");
+}
+
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const SplitPlan pl = split_plan(M, N, K, current_device_shape().cus);
+  return pl.ok ? pl.ws : 0;
 }
 
 int launch_gemm_mx32(const GemmParams& p_in, hipStream_t stream) {

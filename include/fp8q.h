@@ -195,6 +195,33 @@ int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda,
                           int64_t M, int64_t N, int64_t K, int mode, void* stream);
 
 /*
+ * fp8q_gemm_workspace_size / fp8q_gemm_blockscaled_ws — the dense call with a workspace
+ * [FI sections 6-7, as fp8q_gemm_blockscaled]
+ *
+ * Same operation, arguments and requirements as fp8q_gemm_blockscaled, plus a caller-owned
+ * device workspace. fp8q_gemm_workspace_size returns the bytes of workspace with which a
+ * BLOCK128 problem of this shape takes the split-K path on the current device (today:
+ * 32 < M <= 128, when the K blocks split into several ranges; their fp32 partial sums are
+ * added in a fixed order by a second kernel), or 0 when the call needs none; it returns 0 for
+ * MX32 and for arguments the GEMM would reject. With workspace_bytes at least that size the
+ * call takes the split-K path; with a smaller or NULL workspace it runs exactly as
+ * fp8q_gemm_blockscaled. Results of the two paths may differ in the last bits (summation
+ * order) and both meet the accuracy of fp8q_gemm_blockscaled; each path is deterministic.
+ * The workspace must be 16-byte aligned [EALIGN]; workspace_bytes < 0 is EINVAL. The
+ * library writes only the first fp8q_gemm_workspace_size bytes; concurrent calls must not
+ * share a workspace.
+ */
+int64_t fp8q_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode);
+
+int fp8q_gemm_blockscaled_ws(const uint8_t* a, int64_t lda,
+                             const void* sa, int sa_fmt, int64_t sa_sm, int64_t sa_sk,
+                             const uint8_t* b, int64_t ldb,
+                             const void* sb, int sb_fmt, int64_t sb_sn, int64_t sb_sk,
+                             uint16_t* y, int64_t ldy,
+                             int64_t M, int64_t N, int64_t K, int mode,
+                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * fp8q_grouped_gemm_masked — per-expert BLOCK128 GEMM over the masked EP-MoE layout
  * [FI section 7: DeepGEMM grouped masked, expected_m + masked_m; PR30924 item 2]
  *

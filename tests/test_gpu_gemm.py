@@ -254,6 +254,128 @@ def test_dense_small_m(M):
     check(y, ys, ss, w.K, f"dense M={M} (c2)")
 
 
+# ----------------------------------------------------------------------------- split K
+def _gpu_block_ws(a, sa, b, sb, sa_layout="row", workspace=None, packed=False):
+    """As _gpu_block through fp8q_gemm_blockscaled_ws: workspace None lets the binding size
+    one; a zero-length tensor passes none."""
+    f = fq()
+    M, K = a.shape
+    N = b.shape[0]
+    y = torch.full((M, N), SENT_I16, dtype=torch.int16, device="cuda")
+    if packed:
+        sa_v = _packed_words(sa, sa_layout)
+    else:
+        sa_d = _dev(sa)
+        sa_v = sa_d if sa_layout == "row" else sa_d.t()
+    f.fp8q_gemm_blockscaled(_dev(a), sa_v, _dev(b), _dev(sb), y.view(torch.bfloat16), f.GEMM_BLOCK128,
+                            workspace=workspace)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16)
+
+
+def _split_ranges(M, N, K):
+    """K ranges the workspace size implies (1: no workspace)."""
+    nbytes = fq().fp8q_gemm_workspace_size(M, N, K, fq().GEMM_BLOCK128)
+    assert nbytes % (M * N * 4) == 0
+    return max(1, nbytes // (M * N * 4))
+
+
+# 32 < M <= 128 with a workspace: the split-K kernel (64-row variant for M <= 64, 128-row
+# above) with K ranges of one block, of uneven length (K / 128 not a multiple of the range
+# count), ragged N and rows past M inside the last 16-row slice, under every scale layout
+@pytest.mark.parametrize("M,N,K", [(33, 300, 1024), (64, 1000, 2048), (65, 260, 3072), (100, 200, 1536),
+                                   (128, 130, 896)])
+@pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col", "packed-col", "ue8m0-row"])
+@pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
+def test_split_k_full(M, N, K, sa_kind, sb_kind):
+    if sa_kind == "packed-col" and K % 512:
+        K += 512 - K % 512
+    assert _split_ranges(M, N, K) > 1
+    w = synth.Workload("sk", seed=90 + M, M=M, K=K, N=N, scale_fmt=sa_kind.split("-")[0].replace("packed", "ue8m0"))
+    a, sa = synth.gemm_activation(w)
+    if sb_kind == "f32":
+        b, sb = synth.weights(w)
+    else:
+        b, sb = _ue8m0_weights(w, 91)
+    layout = sa_kind.split("-")[1]
+    if sa_kind.startswith("packed"):
+        y = _gpu_block_ws(a, sa, b, sb, layout, packed=True)
+        ys, ss = oracle.gemm_block128(a, sa, b, sb, oracle.SCALE_UE8M0, "row", _fmt(sb))
+    else:
+        sa_store = sa if layout == "row" else np.ascontiguousarray(sa.T)
+        y = _gpu_block_ws(a, sa_store, b, sb, layout)
+        ys, ss = oracle.gemm_block128(a, sa_store, b, sb, _fmt(sa), layout, _fmt(sb))
+    check(y, ys, ss, K, f"split K {M}x{N}x{K} {sa_kind} {sb_kind}")
+
+
+# Full-size shapes: the dense projection's K with ranges of 6 and 7 blocks (K / 128 = 57),
+# N not a multiple of the column tile, and a problem wide enough for one range (no
+# workspace: bf16 stored by the split kernel itself); sampled outputs plus a whole tile
+@pytest.mark.parametrize("M,N,K,ranges", [(100, 4096, 7296, "several"), (128, 4100, 7168, "several"),
+                                          (48, 16448, 1792, "one")])
+def test_split_k_large_sampled(M, N, K, ranges):
+    s = _split_ranges(M, N, K)
+    assert (s > 1) == (ranges == "several")
+    w = synth.Workload("skl", seed=95 + M, M=M, K=K, N=N, scale_fmt="ue8m0")
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    sa_col = np.ascontiguousarray(sa.T)
+    y = _gpu_block_ws(a, sa_col, b, sb, "col")
+    assert not np.any(y == SENT)
+    ms, ns = _sample(M, N, 4096, 13, tile=128)
+    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", at=(ms, ns))
+    check(y[ms, ns], ys, ss, K, f"split K {M}x{N}x{K} ({s} ranges)")
+
+
+# The workspace contract: a workspace one byte short, or none, runs the kernel of the plain
+# call (identical bits); the exact size runs the split path (within tolerance, last bits may
+# differ); a negative size and a misaligned workspace are rejected before any launch.
+def test_split_k_workspace_contract():
+    f = fq()
+    M, N, K = 64, 4096, 7168
+    nbytes = f.fp8q_gemm_workspace_size(M, N, K, f.GEMM_BLOCK128)
+    assert nbytes == _split_ranges(M, N, K) * M * N * 4 and nbytes > 0
+    assert f.fp8q_gemm_workspace_size(M, N, K, f.GEMM_MX32) == 0
+    assert f.fp8q_gemm_workspace_size(16, N, K, f.GEMM_BLOCK128) == 0
+    assert f.fp8q_gemm_workspace_size(4096, N, K, f.GEMM_BLOCK128) == 0
+    assert f.fp8q_gemm_workspace_size(M, N, 200, f.GEMM_BLOCK128) == 0
+    w = synth.dense(M)
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    sa_col = np.ascontiguousarray(sa.T)
+    ms, ns = _sample(M, N, 4096, 14, tile=128)
+    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col", at=(ms, ns))
+    exact = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    short = torch.empty(nbytes - 1, dtype=torch.uint8, device="cuda")
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    y_split = _gpu_block_ws(a, sa_col, b, sb, "col", exact)
+    y_short = _gpu_block_ws(a, sa_col, b, sb, "col", short)
+    y_none = _gpu_block_ws(a, sa_col, b, sb, "col", none)
+    y_plain = _gpu_block(a, sa_col, b, sb, "col")  # the binding sizes a workspace: split path
+    assert np.array_equal(y_short, y_none)
+    assert np.array_equal(y_split, y_plain)
+    for y, what in ((y_split, "split"), (y_none, "no workspace")):
+        check(y[ms, ns], ys, ss, K, f"dense M={M}, {what}")
+    lib = f.load_library()
+    ad, bd, sad, sbd = _dev(a), _dev(b), _dev(sa_col).t(), _dev(sb)
+    y = torch.full((M, N), SENT_I16, dtype=torch.int16, device="cuda")
+    big = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
+
+    def call(ws_ptr, ws_bytes):
+        return lib.fp8q_gemm_blockscaled_ws(
+            ad.data_ptr(), K, sad.data_ptr(), oracle.SCALE_UE8M0, sad.stride(0), sad.stride(1),
+            bd.data_ptr(), K, sbd.data_ptr(), oracle.SCALE_F32, sbd.stride(0), sbd.stride(1),
+            y.data_ptr(), N, M, N, K, f.GEMM_BLOCK128, ws_ptr, ws_bytes, torch.cuda.current_stream().cuda_stream)
+
+    assert call(big.data_ptr(), -1) == f.EINVAL
+    assert call(big.data_ptr() + 8, nbytes) == f.EALIGN
+    torch.cuda.synchronize()
+    assert torch.all(y == SENT_I16)
+    assert call(big.data_ptr() + 16, nbytes) == f.OK
+    torch.cuda.synchronize()
+    check(y.cpu().numpy().view(np.uint16)[ms, ns], ys, ss, K, "offset workspace")
+
+
 def test_dense_m4096_sampled():
     w = synth.dense(4096)
     a, sa = synth.gemm_activation(w)
