@@ -46,6 +46,8 @@ _SIGNATURES = {
     "fp8q_gemm_blockscaled_ws": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _P, _INT, _I64, _I64, _P, _I64,
                                  _I64, _I64, _I64, _INT, _P, _I64, _P],
     "fp8q_gemm_workspace_size": [_I64, _I64, _I64, _INT],
+    "fp8q_gemm_blockscaled_noalloc": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _P, _INT, _I64, _I64, _P, _I64,
+                                      _I64, _I64, _I64, _INT, _P],
     "fp8q_grouped_gemm_masked": [_P, _I64, _I64, _P, _INT, _I64, _I64, _I64, _P, _I64, _I64, _P, _INT,
                                  _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64, _P],
     "fp8q_grouped_gemm_segments": [_P, _I64, _P, _INT, _I64, _I64, _P, _I64, _I64, _P, _INT, _I64, _I64, _I64,
@@ -269,6 +271,23 @@ def fp8q_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb
         _ptr(a8), a8.stride(0), _ptr(sa), _scale_fmt_of(sa), sa.stride(0), sa.stride(1),
         _ptr(b8), b8.stride(0), _ptr(sb), _scale_fmt_of(sb), sb.stride(0), sb.stride(1),
         _ptr(y), y.stride(0), M, N, K, mode, ws_ptr, ws_bytes, _stream(stream)))
+
+
+def fp8q_gemm_blockscaled_noalloc(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                                  y: torch.Tensor, mode: int = GEMM_BLOCK128, stream=None) -> None:
+    """fp8q_gemm_blockscaled with the split-K partial sums in the library's own device array
+    (no allocation anywhere; calls that overlap on one device race on that array)."""
+    a8, b8 = _u8(a), _u8(b)
+    M, K = a8.shape
+    N = b8.shape[0]
+    if b8.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    if a8.stride(1) != 1 or b8.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("innermost dimensions must be contiguous")
+    _check(load_library().fp8q_gemm_blockscaled_noalloc(
+        _ptr(a8), a8.stride(0), _ptr(sa), _scale_fmt_of(sa), sa.stride(0), sa.stride(1),
+        _ptr(b8), b8.stride(0), _ptr(sb), _scale_fmt_of(sb), sb.stride(0), sb.stride(1),
+        _ptr(y), y.stride(0), M, N, K, mode, _stream(stream)))
 
 
 def fp8q_grouped_gemm_masked(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,

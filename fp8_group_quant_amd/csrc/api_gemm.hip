@@ -2,8 +2,36 @@
 // before any device call), the device check, then the launch. Semantics: include/fp8q.h.
 #include "fp8q_internal.h"
 
+#include <mutex>
+
+// Device scratch of fp8q_gemm_blockscaled_noalloc (the split-K partial sums): every device
+// the library's code is loaded on holds its own copy until the process ends. Host code uses
+// the per-device address from hipGetSymbolAddress, never this name.
+static __device__ __align__(256) uint8_t scratch[FP8Q_NOALLOC_SCRATCH_BYTES];
+
 namespace fp8q {
 namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];  // device address of `scratch`, per device
+
+// This device's scratch address, looked up on the first call with the device current.
+int scratch_address(const std::string& pre, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(FP8Q_EDEVICE, pre + "no current HIP device");
+  if (dev >= kScratchDevices) return fail(FP8Q_EUNSUPPORTED, pre + "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(FP8Q_EDEVICE, pre + "hipGetSymbolAddress(scratch) failed: " + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP8Q_OK;
+}
 
 constexpr int64_t kMaxExperts = 4096;
 
@@ -167,6 +195,30 @@ int fp8q_gemm_blockscaled_ws(const uint8_t* a, int64_t lda, const void* sa, int 
   }
   return dense_entry(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy, M, N, K, mode,
                      static_cast<float*>(workspace), workspace ? workspace_bytes : 0, stream);
+}
+
+int fp8q_gemm_blockscaled_noalloc(const uint8_t* a, int64_t lda, const void* sa, int sa_fmt, int64_t sa_sm,
+                                  int64_t sa_sk, const uint8_t* b, int64_t ldb, const void* sb, int sb_fmt,
+                                  int64_t sb_sn, int64_t sb_sk, uint16_t* y, int64_t ldy, int64_t M, int64_t N,
+                                  int64_t K, int mode, void* stream) {
+  using namespace fp8q;
+  const std::string pre = "fp8q_gemm_blockscaled_noalloc: ";
+  set_error("");
+  int rc = check_operands(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy, M,
+                          N, K, mode);
+  if (rc != FP8Q_OK || M == 0 || N == 0 || K == 0) return rc;
+  rc = check_current_device();
+  if (rc != FP8Q_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(pre, &ws);
+  if (rc != FP8Q_OK) return rc;
+  const int64_t need = mode == FP8Q_GEMM_BLOCK128 ? gemm_workspace_bytes(M, N, K) : 0;
+  if (need > FP8Q_NOALLOC_SCRATCH_BYTES)
+    return fail(FP8Q_EUNSUPPORTED, pre + "this shape needs " + std::to_string(need) +
+                                       " bytes of scratch, more than the library's " +
+                                       std::to_string(FP8Q_NOALLOC_SCRATCH_BYTES));
+  return dense_entry(pre, a, lda, sa, sa_fmt, sa_sm, sa_sk, b, ldb, sb, sb_fmt, sb_sn, sb_sk, y, ldy, M, N, K, mode,
+                     static_cast<float*>(ws), FP8Q_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int64_t fp8q_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode) {

@@ -222,6 +222,30 @@ int fp8q_gemm_blockscaled_ws(const uint8_t* a, int64_t lda,
                              void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * fp8q_gemm_blockscaled_noalloc — for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc)
+ *
+ * Same arguments, requirements and results as fp8q_gemm_blockscaled_ws given a workspace of
+ * fp8q_gemm_workspace_size bytes, but the workspace is a device array of the library,
+ * FP8Q_NOALLOC_SCRATCH_BYTES (32 MiB) per device, instead of the caller's. The call allocates
+ * nothing and calls no allocating routine: each device holds its own array from when the
+ * library's code is loaded on it until the process ends, and the array's device address is
+ * looked up on the first call on each device (a failed lookup is FP8Q_EDEVICE). A shape whose
+ * workspace size exceeds FP8Q_NOALLOC_SCRATCH_BYTES is FP8Q_EUNSUPPORTED, before anything is
+ * launched or written. All calls on one device share the array, which keeps the last call's
+ * contents (nothing in it has to start at zero): calls that overlap in time on one device
+ * (several streams or host threads) race on it, so the caller must order them.
+ */
+#define FP8Q_NOALLOC_SCRATCH_BYTES (32 << 20)
+
+int fp8q_gemm_blockscaled_noalloc(const uint8_t* a, int64_t lda,
+                                  const void* sa, int sa_fmt, int64_t sa_sm, int64_t sa_sk,
+                                  const uint8_t* b, int64_t ldb,
+                                  const void* sb, int sb_fmt, int64_t sb_sn, int64_t sb_sk,
+                                  uint16_t* y, int64_t ldy,
+                                  int64_t M, int64_t N, int64_t K, int mode, void* stream);
+
+/*
  * fp8q_grouped_gemm_masked — per-expert BLOCK128 GEMM over the masked EP-MoE layout
  * [FI section 7: DeepGEMM grouped masked, expected_m + masked_m; PR30924 item 2]
  *

@@ -16,7 +16,7 @@ LIB = os.path.join(ROOT, "fp8_group_quant_amd", "libfp8q.so")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(fp8q_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:int|int64_t|const char\*)\s+(fp8q_\w+)\s*\(", text, flags=re.M)))
 
 
 def _lib():
@@ -29,9 +29,17 @@ def _lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("fp8q_group_quant", "fp8q_silu_mul_group_quant", "fp8q_group_quant_int8", "fp8q_gemm_blockscaled",
+              "fp8q_gemm_blockscaled_ws", "fp8q_gemm_workspace_size", "fp8q_gemm_blockscaled_noalloc",
               "fp8q_grouped_gemm_masked", "fp8q_grouped_gemm_segments", "fp8q_grouped_gemm_contiguous",
               "fp8q_status_string", "fp8q_last_error", "fp8q_device_check"):
         assert n in names
+
+
+def test_binding_has_a_signature_for_every_compute_entry():
+    import fp8_group_quant_amd as fq
+    sigs = set(fq._SIGNATURES)
+    missing = [n for n in _declared() if n not in sigs and n not in ("fp8q_status_string", "fp8q_last_error")]
+    assert not missing, missing
 
 
 def test_library_exports_every_declared_symbol():
@@ -140,6 +148,29 @@ def test_segments_tile_count_bound(S, T, N, status):
     rc = fn(0x10000, K, 0x30000, 0, K // 128, 1, 0x20000, N * K, K, 0x40000, 0, (N // 128) * (K // 128), K // 128, 1,
             0x50000, N, 0x60000, None, S, T, 1, N, K, 0, None)
     assert rc == status
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks host validation on a machine without a GPU")
+def test_workspace_entries_validate_before_any_device_call():
+    # Host validation returns before the library touches a pointer or the device; the
+    # addresses below are never dereferenced.
+    lib = _lib()
+    I64, P, I = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    args = [P, I64, P, I, I64, I64, P, I64, P, I, I64, I64, P, I64, I64, I64, I64, I]
+    lib.fp8q_gemm_blockscaled_ws.argtypes = args + [P, I64, P]
+    lib.fp8q_gemm_blockscaled_noalloc.argtypes = args + [P]
+    lib.fp8q_gemm_workspace_size.argtypes = [I64, I64, I64, I]
+    lib.fp8q_gemm_workspace_size.restype = I64
+    M, N, K = 64, 4096, 7168
+    op = [0x10000, K, 0x30000, 1, 1, M, 0x20000, K, 0x40000, 0, K // 128, 1, 0x50000, N, M, N, K, 0]
+    assert lib.fp8q_gemm_blockscaled_ws(*op, 0x60000, -1, None) == 1       # negative workspace size: EINVAL
+    assert lib.fp8q_gemm_blockscaled_ws(*op, 0x60008, 1 << 24, None) == 3  # misaligned workspace: EALIGN
+    assert lib.fp8q_gemm_blockscaled_ws(*op, 0x60000, 1 << 24, None) == 4  # valid: EDEVICE here
+    assert lib.fp8q_gemm_blockscaled_noalloc(*op, None) == 4                # valid: EDEVICE here
+    bad = list(op)
+    bad[16] = 200                                                            # K % 128 != 0
+    assert lib.fp8q_gemm_blockscaled_noalloc(*bad, None) == 1
+    assert lib.fp8q_gemm_workspace_size(M, N, K, 0) == 0                    # no device: no workspace
 
 
 def test_binding_reads_scale_layout_from_strides():
