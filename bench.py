@@ -76,6 +76,87 @@ def _measured_traffic(kernel_file: str, workload: str):
         return None
 
 
+def _counter_dispatches(run_dir: str, counter: str) -> list:
+    """[(dispatch_id, kernel_name, value)] of one counter from the rocpd databases under
+    run_dir (a rocprofv3 --pmc run), values summed over the counter's hardware instances,
+    in dispatch order."""
+    import glob
+    import sqlite3
+    vals, names = {}, {}
+    dbs = sorted(glob.glob(os.path.join(run_dir, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocpd database under {run_dir}")
+    for i, db in enumerate(dbs):
+        con = sqlite3.connect(db)
+        for name, did, cn, v in con.execute(
+                "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+            if cn == counter:
+                vals[(i, did)] = vals.get((i, did), 0.0) + (v or 0.0)
+                names[(i, did)] = name
+        con.close()
+    return [(k, names[k], vals[k]) for k in sorted(vals)]
+
+
+CALIBRATION_ELEMS = 1 << 24  # bf16 values the calibration copies move (32 MiB in, 16 MiB out)
+
+# kernels of each source file, by name
+_KERNEL_FILES = {"quant.hip": ("group_quant_kernel", "token_quant_kernel"),
+                 "gemm.hip": ("gemm_", "splitk_reduce_kernel")}
+
+
+def record_traffic(workload: str, fetch_dir: str, write_dir: str) -> dict:
+    """HBM bytes per quant and per GEMM call of `workload` from two rocprofv3 runs of this
+    script's step loop (the first with --pmc FETCH_SIZE, the second with --pmc WRITE_SIZE;
+    both KiB per dispatch). Each counter is scaled by what it reads for the reference copy
+    kernel (copy_hi_bytes, run --calibration-copies times on CALIBRATION_ELEMS bf16 values:
+    exactly 2n bytes read and n written); the result is merged into profiles/traffic.json
+    with the source tag of each kernel file."""
+    import numpy as np
+    n = CALIBRATION_ELEMS
+    truth = {"FETCH_SIZE": 2 * n, "WRITE_SIZE": n}
+    runs = {"FETCH_SIZE": _counter_dispatches(fetch_dir, "FETCH_SIZE"),
+            "WRITE_SIZE": _counter_dispatches(write_dir, "WRITE_SIZE")}
+    scale, per_file = {}, {}
+    for cn, disp in runs.items():
+        copies = [v for _, name, v in disp if "copy_hi_bytes" in name and v > 0]
+        if not copies:
+            raise SystemExit(f"{cn}: no calibration copies (run the step loop with --calibration-copies)")
+        scale[cn] = truth[cn] / (float(np.median(copies)) * 1024.0)
+        for fname, pats in _KERNEL_FILES.items():
+            ks = [(n, v) for _, n, v in disp if any(p in n for p in pats)]
+            if ks:
+                per_file.setdefault(fname, {})[cn] = ks
+    out = {}
+    for fname, d in per_file.items():
+        if "FETCH_SIZE" not in d or "WRITE_SIZE" not in d:
+            continue
+        ent = {"source_sha256_16": _kernel_source_tag(fname)}
+        total = 0.0
+        kinds = sorted({n for n, _ in d["FETCH_SIZE"]})
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            kib = sum(float(np.median([v for n, v in d[cn] if n == k])) for k in kinds)
+            ent[cn.split("_")[0].lower() + "_kib"] = round(kib, 1)
+            ent[cn.split("_")[0].lower() + "_bytes"] = int(kib * 1024 * scale[cn])
+            total += kib * 1024 * scale[cn]
+        ent["kernels"] = [k[:120] for k in kinds]
+        ent["bytes_per_launch"] = int(total)
+        ent["launches"] = min(sum(1 for n, _ in d["FETCH_SIZE"] if n == k) for k in kinds)
+        out[fname] = ent
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec["_note"] = ("HBM bytes per call from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed "
+                    "over a call's kernels), each scaled by what it reads for a reference copy of known size "
+                    "(bench.py --calibration-copies); fetch_scale and write_scale are per workload")
+    rec[workload] = dict(out, fetch_scale=round(scale["FETCH_SIZE"], 4), write_scale=round(scale["WRITE_SIZE"], 4))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec[workload]
+
+
 def quant_bytes(rows: int, K: int, G: int, in_bytes: int, scale_bytes: int, silu: bool) -> int:
     """Algorithmic bytes of one group-quant launch: read the input once, write codes + scales."""
     width = 2 * K if silu else K
@@ -136,6 +217,11 @@ def _nsets(set_bytes: int, cap: int = 8) -> int:
 
 
 # --------------------------------------------------------------------------- ceilings
+def _progress(msg: str) -> None:
+    """One line per finished phase on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def _bench_lib():
     lib = ctypes.CDLL(BENCH_LIB)
     for name in ("fp8q_bench_copy", "fp8q_bench_stream"):
@@ -417,6 +503,17 @@ def run(args) -> dict:
         sets.append(dict(x=x0.clone(), q=q, s=s, w=w0.clone(), sw=sw0.clone(),
                          y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     torch.cuda.synchronize()
+    if args.calibration_copies:
+        # reference copies of known size for counter runs (record_traffic)
+        src = torch.zeros(CALIBRATION_ELEMS, dtype=torch.int16, device=dev)
+        dst = torch.empty(CALIBRATION_ELEMS, dtype=torch.uint8, device=dev)
+        blib = _bench_lib()
+        for _ in range(args.calibration_copies):
+            rc = blib.fp8q_bench_copy(src.data_ptr(), dst.data_ptr(), CALIBRATION_ELEMS, 4096,
+                                      torch.cuda.current_stream().cuda_stream)
+            assert rc == 0, rc
+        torch.cuda.synchronize()
+        del src, dst
 
     stream = torch.cuda.current_stream()
 
@@ -528,15 +625,19 @@ def run(args) -> dict:
     }
     del sets[1:]
     torch.cuda.empty_cache()
+    _progress(f"steps timed: {out['ms_per_step']} ms per step")
     if not args.no_configs:
         ceil = ceilings(args.config_launches)
         out["ceilings"] = ceil
         out["kernels"]["group_quant"]["frac_copy"] = round(quant_gbs / ceil["copy"]["GB/s"], 4)
+        _progress("ceilings done")
         out["configs"] = configs(args.config_launches, ceil)
     if not args.no_parity:
         out["parity"] = parity_gate(w, x_host, w_host, sw_host, out_set["q"], out_set["s"], out_set["y"])
+        _progress("parity gate done")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x_host, w_host, sw_host, args.cpu_rows)
+        _progress("cpu baseline done")
     return out
 
 
@@ -782,7 +883,15 @@ def main(argv=None) -> int:
                     help="with --suite: comma-separated sections to run (" + ",".join(SUITE_SECTIONS) + ")")
     ap.add_argument("--suite", action="store_true",
                     help="print per-kernel lines for every named workload instead of the step line")
+    ap.add_argument("--calibration-copies", type=int, default=0,
+                    help="launch this many reference copies of known size before the steps (counter runs)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="(no GPU) merge the --workload's HBM bytes per call from two rocprofv3 counter runs "
+                         "of the step loop into profiles/traffic.json")
     args = ap.parse_args(argv)
+    if args.record_traffic:
+        print(json.dumps(record_traffic(args.workload, *args.record_traffic)), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
               f"multi-GPU path", file=sys.stderr)

@@ -54,3 +54,48 @@ def test_committed_traffic_matches_the_current_kernels():
     for src in ("quant.hip", "gemm.hip"):
         tag = bench._kernel_source_tag(src)
         assert (bench._measured_traffic(src, "dense_m4096") is not None) == (tag == rec["dense_m4096"][src]["source_sha256_16"])
+
+
+def _counter_db(path, rows):
+    import sqlite3
+    path.parent.mkdir(parents=True, exist_ok=True)
+    con = sqlite3.connect(str(path))
+    con.execute("create table counters_collection (kernel_name text, dispatch_id int, counter_name text, value real)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_record_traffic_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    """Counters of a run are scaled so that the reference copy reads 2n and writes n bytes;
+    a call's kernels (split GEMM + reduction) are summed; values of one dispatch's hardware
+    instances are summed first."""
+    n = bench.CALIBRATION_ELEMS
+    fetch, write = [], []
+    d = 0
+    for _ in range(4):  # copy: FETCH reads half the truth (scale 2), WRITE exact
+        d += 1
+        fetch += [("copy_hi_bytes(...)", d, "FETCH_SIZE", n / 1024)]
+        write += [("copy_hi_bytes(...)", d, "WRITE_SIZE", n / 2048), ("copy_hi_bytes(...)", d, "WRITE_SIZE", n / 2048)]
+    for _ in range(3):
+        d += 1
+        fetch += [("group_quant_kernel<0, 128>", d, "FETCH_SIZE", 100.0)]
+        write += [("group_quant_kernel<0, 128>", d, "WRITE_SIZE", 50.0)]
+        d += 1
+        fetch += [("gemm_splitk_kernel<8, 1, 0>", d, "FETCH_SIZE", 1000.0)]
+        write += [("gemm_splitk_kernel<8, 1, 0>", d, "WRITE_SIZE", 400.0)]
+        d += 1
+        fetch += [("splitk_reduce_kernel(...)", d, "FETCH_SIZE", 300.0)]
+        write += [("splitk_reduce_kernel(...)", d, "WRITE_SIZE", 30.0)]
+    _counter_db(tmp_path / "f" / "host" / "run_results.db", fetch)
+    _counter_db(tmp_path / "w" / "host" / "run_results.db", write)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    ent = bench.record_traffic("dense_m128", str(tmp_path / "f"), str(tmp_path / "w"))
+    assert ent["fetch_scale"] == 2.0 and ent["write_scale"] == 1.0
+    q, g = ent["quant.hip"], ent["gemm.hip"]
+    assert q["fetch_bytes"] == 100 * 1024 * 2 and q["write_bytes"] == 50 * 1024
+    assert g["fetch_bytes"] == 1300 * 1024 * 2 and g["write_bytes"] == 430 * 1024
+    assert g["bytes_per_launch"] == g["fetch_bytes"] + g["write_bytes"] and g["launches"] == 3
+    assert g["source_sha256_16"] == bench._kernel_source_tag("gemm.hip")
+    with open(tmp_path / "traffic.json") as f:
+        assert json.load(f)["dense_m128"]["gemm.hip"]["bytes_per_launch"] == g["bytes_per_launch"]
