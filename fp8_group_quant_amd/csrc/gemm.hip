@@ -1509,9 +1509,9 @@ template <int SM>
 struct SmallCfg {
   // Eight waves (two per SIMD, 256 VGPRs each). Blocks per pass: two passes of fragments
   // (B 8 VGPRs, A 8 per 16 rows, scales) fit the registers.
-  static_assert(SM == 1 || SM == 2, "M <= 32");
+  static_assert(SM == 1, "M <= 16");
   static constexpr int kWaves = 8;
-  static constexpr int P = SM == 2 ? 3 : 4;
+  static constexpr int P = 4;
 };
 
 constexpr int kBufWord3 = 0x00020000;  // raw buffer resource: 32-bit data format, no swizzle
@@ -1675,15 +1675,16 @@ void launch_small_m_sm(const GemmParams& p, hipStream_t s) {
   hipLaunchKernelGGL((gemm_small_m_kernel<SM, SA_FMT, SB_FMT>), grid, block, 0, s, p);
 }
 
-// M <= kSmallMaxM: the register kernel above; larger M (up to kSkinnyMaxM) keeps the
-// LDS-staged kernel, which moves whole cache lines (there every workgroup streams all of A:
-// 0.9 MB at M = 128, and the register kernel measured 36.6 against 23.5 us).
-constexpr int64_t kSmallMaxM = 32;
+// M <= kSmallMaxM: the register kernel above; larger M (up to kSkinnyMaxM) takes the split-K
+// kernel below when the caller gives a workspace, else the LDS-staged kernel, which moves
+// whole cache lines (there every workgroup streams all of A). Graph-replayed at N = 4096,
+// K = 7168: M = 32 in the register kernel (two 16-row slices) 16.7 us, split-K 13.7, the
+// LDS-staged kernel 14.7; at M = 128 the register kernel measured 36.6 against 23.5 us.
+constexpr int64_t kSmallMaxM = 16;
 
 template <int SA_FMT, int SB_FMT>
 void launch_small_m(const GemmParams& p, hipStream_t s) {
-  if (p.M <= 16) launch_small_m_sm<1, SA_FMT, SB_FMT>(p, s);
-  else launch_small_m_sm<2, SA_FMT, SB_FMT>(p, s);
+  launch_small_m_sm<1, SA_FMT, SB_FMT>(p, s);
 }
 
 template <int SM, int SA_FMT, int SB_FMT>
@@ -1730,7 +1731,7 @@ bool try_skinny_dma(const GemmParams& p, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ small M, split K
-// For 32 < M <= 128 the kernels above give every workgroup 16 columns and all of K, so each
+// For 16 < M <= 128 the kernels above give every workgroup 16 columns and all of K, so each
 // streams all M x K of A through its CU (0.9 MB at M = 128, 256 times over). Here a workgroup
 // owns C = 64 NF columns (four waves, NF 16-column MFMA slices each) and one of S contiguous
 // ranges of the K blocks, so A is read once per C columns and per range while the grid

@@ -201,7 +201,7 @@ int fp8q_gemm_blockscaled(const uint8_t* a, int64_t lda,
  * Same operation, arguments and requirements as fp8q_gemm_blockscaled, plus a caller-owned
  * device workspace. fp8q_gemm_workspace_size returns the bytes of workspace with which a
  * BLOCK128 problem of this shape takes the split-K path on the current device (today:
- * 32 < M <= 128, when the K blocks split into several ranges; their fp32 partial sums are
+ * 16 < M <= 128, when the K blocks split into several ranges; their fp32 partial sums are
  * added in a fixed order by a second kernel), or 0 when the call needs none; it returns 0 for
  * MX32 and for arguments the GEMM would reject. With workspace_bytes at least that size the
  * call takes the split-K path; with a smaller or NULL workspace it runs exactly as

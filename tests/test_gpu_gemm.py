@@ -280,11 +280,11 @@ def _split_ranges(M, N, K):
     return max(1, nbytes // (M * N * 4))
 
 
-# 32 < M <= 128 with a workspace: the split-K kernel (64-row variant for M <= 64, 128-row
+# 16 < M <= 128 with a workspace: the split-K kernel (64-row variant for M <= 64, 128-row
 # above) with K ranges of one block, of uneven length (K / 128 not a multiple of the range
 # count), ragged N and rows past M inside the last 16-row slice, under every scale layout
-@pytest.mark.parametrize("M,N,K", [(33, 300, 1024), (64, 1000, 2048), (65, 260, 3072), (100, 200, 1536),
-                                   (128, 130, 896)])
+@pytest.mark.parametrize("M,N,K", [(17, 300, 1024), (32, 520, 2048), (33, 300, 1024), (64, 1000, 2048),
+                                   (65, 260, 3072), (100, 200, 1536), (128, 130, 896)])
 @pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col", "packed-col", "ue8m0-row"])
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
 def test_split_k_full(M, N, K, sa_kind, sb_kind):
@@ -330,6 +330,19 @@ def test_split_k_large_sampled(M, N, K, ranges):
 # The workspace contract: a workspace one byte short, or none, runs the kernel of the plain
 # call (identical bits); the exact size runs the split path (within tolerance, last bits may
 # differ); a negative size and a misaligned workspace are rejected before any launch.
+@pytest.mark.parametrize("M", [17, 24, 32])
+def test_rows_17_to_32_without_workspace(M):
+    """The plain call (no workspace) takes the LDS-staged kernel for 16 < M <= 128."""
+    N, K = 300, 1024
+    w = synth.Workload("nw", seed=97 + M, M=M, K=K, N=N, scale_fmt="ue8m0")
+    a, sa = synth.gemm_activation(w)
+    b, sb = synth.weights(w)
+    sa_col = np.ascontiguousarray(sa.T)
+    y = _gpu_block_ws(a, sa_col, b, sb, "col", workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    ys, ss = oracle.gemm_block128(a, sa_col, b, sb, oracle.SCALE_UE8M0, "col")
+    check(y, ys, ss, K, f"no workspace M={M}")
+
+
 def test_split_k_workspace_contract():
     f = fq()
     M, N, K = 64, 4096, 7168

@@ -84,7 +84,7 @@ def test_noalloc_refuses_shapes_beyond_its_scratch():
 
 
 def test_noalloc_without_scratch_need():
-    """Shapes that need no workspace (M <= 32, large M) run as the plain call."""
+    """Shapes that need no workspace (M <= 16, large M) run as the plain call."""
     f = _fq()
     for M in (16, 300):
         N, K = 256, 1024
