@@ -14,10 +14,12 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M", [1, 16, 128, 300])
+# M = 24, 64 and 128 take the split-K GEMM (two kernels and a workspace the binding takes
+# from torch's allocator inside the capture)
+@pytest.mark.parametrize("M", [1, 16, 24, 64, 128, 300])
 def test_quant_gemm_step_replays_in_a_graph(M):
     import fp8_group_quant_amd as fq
-    w = synth.dense(M) if M in (1, 16, 128) else synth.Workload("g", seed=80, M=M, K=7168, N=4096)
+    w = synth.dense(M) if M in (1, 16, 64, 128) else synth.Workload("g", seed=80, M=M, K=7168, N=4096)
     K, N, G = w.K, w.N, 128
     b, sb = synth.weights(w)
     bd, sbd = torch.from_numpy(b).cuda(), torch.from_numpy(sb).cuda()
@@ -129,3 +131,49 @@ def test_masked_moe_step_replays_with_new_counts():
                 qo, so = oracle.group_quant(inputs[i][e, :r], G, oracle.SCALE_UE8M0, "col", silu=True)
                 assert np.array_equal(q_e[e, :r].cpu().numpy(), qo), f"expert {e}: codes vs the oracle"
                 assert np.array_equal(s_e[e, :r].cpu().numpy(), so.T), f"expert {e}: scales vs the oracle"
+
+
+def test_noalloc_gemm_replays_in_a_graph():
+    """The allocation-free GEMM (split-K partial sums in the library's own array) captured
+    and replayed: every replay, with new activations and eager work between replays, equals
+    the eager call bit for bit."""
+    import fp8_group_quant_amd as fq
+    M, N, K = 128, 4096, 7168
+    w = synth.Workload("gna", seed=85, M=M, K=K, N=N, scale_fmt="ue8m0")
+    b, sb = synth.weights(w)
+    bd, sbd = torch.from_numpy(b).cuda(), torch.from_numpy(sb).cuda()
+    a = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((K // 128, M), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        fq.fp8q_gemm_blockscaled_noalloc(a, sa.t(), bd, sbd, y)
+
+    ops = []
+    for i in range(3):
+        wi = synth.Workload("gna", seed=86 + i, M=M, K=K, N=N, scale_fmt="ue8m0")
+        ai, sai = synth.gemm_activation(wi)
+        ops.append((torch.from_numpy(ai), torch.from_numpy(np.ascontiguousarray(sai.T))))
+    a.copy_(ops[0][0])
+    sa.copy_(ops[0][1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i, (ai, sai) in enumerate(ops):
+        a.copy_(ai)
+        sa.copy_(sai)
+        call()
+        torch.cuda.synchronize()
+        y_e = y.clone()
+        y.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_e.view(torch.int16)), f"replay {i}: Y differs from the eager call"
