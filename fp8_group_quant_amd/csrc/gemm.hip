@@ -657,6 +657,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 using DmaCfg = TileCfg<256, 128, 4, 2, 4>;
 using DmaCfgW = TileCfg<256, 256, 2, 4, 4>;
 using DmaCfgT = TileCfg<128, 256, 2, 4, 4>;
+using DmaCfgW4 = TileCfg<256, 256, 2, 2, 4>;  // four waves of 128 x 128
 
 // Per-tile state of the direct-to-LDS loop.
 template <class C, int SCM>
@@ -675,13 +676,13 @@ struct DmaRun {
   static constexpr bool E8W = SCM == kScE8E8 || SCM == kScPkE8;
   static constexpr bool NOFOLD = MX || E8W;
   static constexpr int SM = C::SM, SN = C::SN;
-  static_assert((C::BM == 256 || C::BM == 128) && SN == 4 && C::WTN == 64, "64-wide wave tiles");
+  static_assert((C::BM == 256 || C::BM == 128) && (SN == 4 || SN == 8) && C::WTN == 16 * SN, "wave tiles");
   static constexpr int kW = C::kWaves;
   static constexpr int kLA = (C::BM / 8) / kW, kLB = (C::BN / 8) / kW;  // 1 KB blocks per wave
   static constexpr int kSc = L::kGrouped ? 1 : 8 / kW;                // scale jobs per wave
   // loads per wave and step: tile blocks, then scale jobs
   static constexpr int kGroup = kLA + kLB + kSc;
-  static constexpr int kPerStep = 4 * SM;  // MFMAs per wave and step
+  static constexpr int kPerStep = SN * SM;  // MFMAs per wave and step
 
   const GemmParams& p;
   uint8_t* smem;       // three stages
@@ -785,7 +786,7 @@ struct DmaRun {
 #pragma unroll
         for (int i = 0; i < SM; i++) ea[i] = ring[16 * (wm * C::WTM + i * 16 + (lane & 15)) + 4 * q + (lane >> 4)];
 #pragma unroll
-        for (int j = 0; j < SN; j++) eb[j] = ring[4096 + 16 * (wn * 64 + j * 16 + (lane & 15)) + 4 * q + (lane >> 4)];
+        for (int j = 0; j < SN; j++) eb[j] = ring[4096 + 16 * (wn * C::WTN + j * 16 + (lane & 15)) + 4 * q + (lane >> 4)];
       } else {
 #pragma unroll
         for (int i = 0; i < SM; i++) sa[i] = reinterpret_cast<const float*>(ring)[4 * (wm * C::WTM + i * 16 + (lane & 15)) + q];
@@ -805,10 +806,17 @@ struct DmaRun {
 #pragma unroll
       for (int j = 0; j < SN; j++) eb[j] = w;
     } else if constexpr (MX) {
+      // one lane offset for all reads (kept opaque, so each read is that register plus an
+      // immediate offset rather than a hoisted address per row: with four waves of 128x128
+      // the hoisted addresses did not fit the registers)
+      int lo = 4 * (lane & 15) + (lane >> 4);
+      asm volatile("" : "+v"(lo));
+      const uint8_t* sa_l = sc + 4 * wm * C::WTM + lo;
+      const uint8_t* sb_l = sc + 1024 + 4 * wn * C::WTN + lo;
 #pragma unroll
-      for (int i = 0; i < SM; i++) ea[i] = sc[4 * (wm * C::WTM + i * 16 + (lane & 15)) + (lane >> 4)];
+      for (int i = 0; i < SM; i++) ea[i] = sa_l[64 * i];
 #pragma unroll
-      for (int j = 0; j < SN; j++) eb[j] = sc[1024 + 4 * (wn * 64 + j * 16 + (lane & 15)) + (lane >> 4)];
+      for (int j = 0; j < SN; j++) eb[j] = sb_l[64 * j];
     } else {
 #pragma unroll
       for (int i = 0; i < SM; i++) {
@@ -832,7 +840,7 @@ struct DmaRun {
   __device__ __forceinline__ void load_ops(int st) {
     const uint8_t* s = stage(st);
 #pragma unroll
-    for (int j = 0; j < SN; j++) wf[j] = frag(s + C::BM * BK, wn * 64 + j * 16, lane);
+    for (int j = 0; j < SN; j++) wf[j] = frag(s + C::BM * BK, wn * C::WTN + j * 16, lane);
     x0 = frag(s, wm * C::WTM, lane);
     if constexpr (kAhead == 2) x1 = frag(s, wm * C::WTM + 16, lane);
     load_scales(st, 0);
@@ -844,7 +852,7 @@ struct DmaRun {
   template <int S, int NXT, int T>
   __device__ __forceinline__ void mf(const v8i& xf, const float (&f)[SM], const uint32_t (&eas)[SM],
                                      const uint32_t (&ebs)[SN]) {
-    constexpr int i = T / 4, j = T % 4;
+    constexpr int i = T / SN, j = T % SN;
     if constexpr (NOFOLD) {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf, acc[i][j], 0, 0, 0,
                                                                    static_cast<int>(ebs[j]), 0,
@@ -852,8 +860,8 @@ struct DmaRun {
     } else {
       constexpr int g = kSlot0 * S + T;
       constexpr int slot = g % kRingN, pslot = (g + 1) % kRingN;
-      constexpr int ip = T >= kLag ? (T - kLag) / 4 : SM - 1;
-      constexpr int jp = T >= kLag ? (T - kLag) % 4 : 4 - kLag + T;
+      constexpr int ip = T >= kLag ? (T - kLag) / SN : SM - 1;
+      constexpr int jp = T >= kLag ? (T - kLag) % SN : SN - kLag + T;
       const float sp = T >= kLag ? f[ip] : pend_s;
       const v4f z = {0.f, 0.f, 0.f, 0.f};
       if constexpr (E8)
@@ -864,17 +872,19 @@ struct DmaRun {
 #pragma unroll
       for (int r = 0; r < 4; r++) acc[ip][jp][r] = fmaf(pr[pslot][r], sp, acc[ip][jp][r]);
     }
-    if constexpr (NXT >= 0) wf[j] = frag(stage(NXT) + C::BM * BK, wn * 64 + j * 16, lane);
+    if constexpr (NXT >= 0) wf[j] = frag(stage(NXT) + C::BM * BK, wn * C::WTN + j * 16, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  template <int S, int NXT, int I, int... J>
+  __device__ __forceinline__ void row_j(const v8i& xf, const float (&f)[SM], const uint32_t (&eas)[SM],
+                                       const uint32_t (&ebs)[SN], std::integer_sequence<int, J...>) {
+    (mf<S, NXT, SN * I + J>(xf, f, eas, ebs), ...);
+  }
   template <int S, int NXT, int I>
   __device__ __forceinline__ void row(const v8i& xf, const float (&f)[SM], const uint32_t (&eas)[SM],
                                      const uint32_t (&ebs)[SN]) {
-    mf<S, NXT, 4 * I + 0>(xf, f, eas, ebs);
-    mf<S, NXT, 4 * I + 1>(xf, f, eas, ebs);
-    mf<S, NXT, 4 * I + 2>(xf, f, eas, ebs);
-    mf<S, NXT, 4 * I + 3>(xf, f, eas, ebs);
+    row_j<S, NXT, I>(xf, f, eas, ebs, std::make_integer_sequence<int, SN>{});
   }
 
   // Activation fragments are read kAhead = 2 rows before their MFMAs (the first two of a
@@ -903,7 +913,7 @@ struct DmaRun {
       const int slot = (kSlot0 * S + kPerStep - kLag + q) % kRingN;
 #pragma unroll
       for (int r = 0; r < 4; r++)
-        acc[SM - 1][4 - kLag + q][r] = fmaf(pr[slot][r], pend_s, acc[SM - 1][4 - kLag + q][r]);
+        acc[SM - 1][SN - kLag + q][r] = fmaf(pr[slot][r], pend_s, acc[SM - 1][SN - kLag + q][r]);
     }
   }
 
@@ -992,6 +1002,7 @@ __device__ void run_tile_dma(const GemmParams& p, uint8_t* smem, const Tile& t) 
     const int row = (wave * R::kLB + q) * 8 + (lane >> 3), c = (lane & 7) ^ swz(row);
     r.b_off[q] = static_cast<uint32_t>((min(n0 + row, nmax) - n0) * p.ldb + c * 16);
   }
+
   // Scale job js = q * kW + wave (8 per step). Default: 4 bytes of A into the spare area.
   constexpr int kNb = C::BN / 128;  // weight blocks per tile
 #pragma unroll
@@ -2282,8 +2293,11 @@ int launch_gemm_mx32(const GemmParams& p_in, hipStream_t stream) {
   using W = DmaCfgW;
   const int64_t wt = ((p.M + W::BM - 1) / W::BM) * ((p.N + W::BN - 1) / W::BN);
   if (dm >= 0 && wt >= ds.cus) {
-    // 256x256 tiles with per-step scale loads (8 jobs: 256 activation and 256 weight rows)
-    launch_dma<kScMx, W>(p, grid_for(wt, ds), stream);
+    // 256x256 tiles with per-step scale loads (8 jobs: 256 activation and 256 weight rows),
+    // as four waves of 128x128 (one per SIMD): with no fold the 256 accumulators of a lane
+    // fit, and each wave reads a quarter less from LDS per MFMA than a 128x64 wave. 8192^3,
+    // same box, three interleaved rounds: 482-488 us against 509-515 for eight 128x64 waves.
+    launch_dma<kScMx, DmaCfgW4>(p, grid_for(wt, ds), stream);
     return finish("MXFP8 GEMM launch");
   }
   if (dm == kScMxGrp) launch_dma<kScMxGrp>(p, grid_for(tiles, ds), stream);
