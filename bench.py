@@ -388,6 +388,18 @@ def configs(launches: int, ceil: dict | None) -> list:
     note(_rec("c5", w.name, "gemm_mx32", ms, "mfma", flops=2.0 * w.M * w.N * w.K,
               nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
               extra={"scales": "E8M0 bytes, row-major [rows, K/32]"}))
+    # the same operands with both scale tensors as column-major packed words [K/128, rows]
+    # (the layout the G=32 quant writes with packed column-major UE8M0 scales)
+    def col_words(e):
+        return torch.from_numpy(np.ascontiguousarray(np.ascontiguousarray(e).view(np.uint32).T).view(np.int32)).to(dev).t()
+    for st in sets:
+        st["ea"], st["eb"] = col_words(ea), col_words(eb)
+    ms = graph_time_ms(lambda i: fq.fp8q_gemm_blockscaled(sets[i % ns]["a"], sets[i % ns]["ea"], sets[i % ns]["b"],
+                                                         sets[i % ns]["eb"], sets[i % ns]["y"], fq.GEMM_MX32),
+                       max(4, launches // 4))
+    note(_rec("c5", w.name, "gemm_mx32", ms, "mfma", flops=2.0 * w.M * w.N * w.K,
+              nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
+              extra={"scales": "E8M0 packed words, column-major [K/128, rows]"}))
     del sets
     torch.cuda.empty_cache()
     return recs
