@@ -264,7 +264,15 @@ def fp8q_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb
     if workspace is None and mode == GEMM_BLOCK128:
         nbytes = fp8q_gemm_workspace_size(M, N, K, mode)
         if nbytes > 0:
-            workspace = torch.empty(nbytes, dtype=torch.uint8, device=a8.device)
+            # allocated on the stream the kernels run on, so that the caching allocator hands
+            # the block to no other stream's work before they finish
+            if stream is None:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=a8.device)
+            else:
+                st = stream if isinstance(stream, torch.cuda.Stream) else \
+                    torch.cuda.ExternalStream(int(stream), device=a8.device)
+                with torch.cuda.stream(st):
+                    workspace = torch.empty(nbytes, dtype=torch.uint8, device=a8.device)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().fp8q_gemm_blockscaled_ws(

@@ -12,11 +12,15 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
-def test_concurrent_streams_match_serial_results():
+# M = 64 takes the split-K GEMM: the binding allocates each call's workspace on the stream
+# the call runs on
+@pytest.mark.parametrize("M", [256, 64])
+def test_concurrent_streams_match_serial_results(M):
     import fp8_group_quant_amd as fq
     n_threads, iters = 4, 12
-    M, K, N, G = 256, 2048, 512, 128
+    K, N, G = 2048, 512, 128
     w = synth.Workload("c", seed=90, M=M, K=K, N=N)
+    assert (fq.fp8q_gemm_workspace_size(M, N, K) > 0) == (M == 64)
     b, sb = synth.weights(w)
     bd, sbd = torch.from_numpy(b).cuda(), torch.from_numpy(sb).cuda()
     xs = [torch.from_numpy(synth.activations_bf16(91 + t, M, K)).cuda().view(torch.bfloat16) for t in range(n_threads)]
@@ -50,6 +54,12 @@ def test_concurrent_streams_match_serial_results():
                         return
         except Exception as ex:  # reported below
             errors.append(f"thread {t}: {ex!r}")
+
+    # a raw stream handle (not the current stream) also works
+    st = torch.cuda.Stream()
+    q, s, y = step(xs[0], st.cuda_stream)
+    st.synchronize()
+    assert torch.equal(y.view(torch.int16).cpu(), ref[0][2])
 
     threads = [threading.Thread(target=worker, args=(t,)) for t in range(n_threads)]
     for th in threads:
