@@ -63,15 +63,27 @@ double ora_e4m3_decode(uint8_t b) {
   return s ? -mag : mag;
 }
 
+/* The values of the 127 non-negative finite codes, in code order: ora_e4m3_decode of each
+ * (filled once when the library loads, so the search below does not decode 127 codes for
+ * every value). */
+static double ora_e4m3_values[0x7F];
+
+__attribute__((constructor)) static void ora_fill_e4m3_values(void) {
+  for (int c = 0; c <= 0x7E; c++) ora_e4m3_values[c] = ora_e4m3_decode((uint8_t)c);
+}
+
 /* Nearest finite e4m3 value to v, ties to the even code (the code's low bit is the low
  * mantissa bit). v must be finite with |v| <= 448 (the caller clamps first). The search
- * walks the 127 non-negative finite codes in increasing order of value. */
+ * walks the 127 non-negative finite codes in increasing order of value, and stops at the
+ * first code farther above |v| than the nearest one so far: every later code is farther
+ * still (a code exactly as far is still compared, for the tie rule). */
 uint8_t ora_e4m3_encode(float v) {
   double a = fabs((double)v);
   int best = 0;
   double bestd = INFINITY;
   for (int c = 0; c <= 0x7E; c++) {
-    double d = fabs(ora_e4m3_decode((uint8_t)c) - a);
+    if (ora_e4m3_values[c] - a > bestd) break;
+    double d = fabs(ora_e4m3_values[c] - a);
     if (d < bestd || (d == bestd && (c & 1) == 0)) {
       best = c;
       bestd = d;
@@ -380,6 +392,8 @@ void ora_e4m3_decode_array(const uint8_t* in, double* out, int64_t n) {
 }
 
 void ora_e4m3_encode_array(const float* in, uint8_t* out, int64_t n) {
+  /* elements are independent: one thread encodes each */
+#pragma omp parallel for schedule(static) if (n > 65536)
   for (int64_t i = 0; i < n; i++) out[i] = ora_e4m3_encode(in[i]);
 }
 

@@ -98,6 +98,30 @@ def test_encode_fp32_sweep_matches_torch():
     assert np.array_equal(oracle.e4m3_encode(v), _torch_e4m3(v))
 
 
+def test_encode_every_fp32_pattern_after_the_clamp():
+    """Every fp32 pattern through the clamp to [-448, 448] and the encoder, against torch's
+    cast: the 2 x 1,138,753,537 patterns of magnitude <= 448 (both signs, zeros and
+    subnormals) one by one, in chunks; every larger finite or infinite magnitude becomes
+    +-448 at the clamp, so it meets the encoder as that one value (checked with its
+    neighbours). NaN is outside the contract (finite inputs)."""
+    top = 0x43E00000  # 448.0
+    assert np.array([top], np.uint32).view(np.float32)[0] == 448.0
+    step = 1 << 25
+    n = 0
+    for lo in range(0, top + 1, step):
+        bits = np.arange(lo, min(lo + step, top + 1), dtype=np.uint32)
+        v = bits.view(np.float32)
+        for sv in (v, -v):
+            assert np.array_equal(oracle.e4m3_encode(sv), _torch_e4m3(sv)), f"chunk from {lo:#x}"
+            n += sv.size
+    assert n == 2 * (top + 1)
+    big = np.array([448.0, np.nextafter(np.float32(448), np.float32(np.inf)), 480.0, 3.4e38, np.inf], np.float32)
+    for sv in (big, -big):
+        c = np.clip(sv, -448, 448).astype(np.float32)
+        assert np.array_equal(oracle.e4m3_encode(c), _torch_e4m3(c))
+        assert set(oracle.e4m3_encode(c).tolist()) == {0x7E if sv[0] > 0 else 0xFE}
+
+
 def test_encode_tiny_values_round_to_signed_zero():
     v = np.array([1e-30, -1e-30, 2.0 ** -10, -(2.0 ** -10), 1e-40], dtype=np.float32)
     assert oracle.e4m3_encode(v).tolist() == [0x00, 0x80, 0x00, 0x80, 0x00]
