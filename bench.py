@@ -230,11 +230,15 @@ def _bench_lib():
     lib.fp8q_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     lib.fp8q_bench_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_void_p]
+    lib.fp8q_bench_mfma.restype = ctypes.c_int
+    lib.fp8q_bench_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
     return lib
 
 
 def ceilings(launches: int) -> dict:
-    """The copy and stream reference kernels at the sizes of the dense workload."""
+    """The copy and stream reference kernels at the sizes of the dense workload, and the
+    GEMM's MFMA instruction mix run from registers."""
     import torch
     lib = _bench_lib()
     dev = torch.device("cuda", 0)
@@ -271,6 +275,24 @@ def ceilings(launches: int) -> dict:
                             "bytes": N * K, "us": round(ms * 1e3, 2), "GB/s": round(N * K / (ms * 1e-3) / 1e9, 1),
                             "frac_hbm": round(N * K / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del ws
+    # the GEMM's per-step instruction mix from registers (32 scaled FP8 MFMAs per wave and
+    # step on real e4m3 codes, with or without the BLOCK128 fold), eight waves on every CU
+    import synth
+    codes = torch.from_numpy(synth.weight_codes(7, cus * 512, 192)).to(dev)
+    sink = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    iters = 400
+    flops = float(cus) * 8 * iters * 32 * 2 * 16 * 16 * 128
+    for key, fold in (("mfma_stream", 0), ("mfma_fold_stream", 1)):
+        def mx(i, fold=fold):
+            rc = lib.fp8q_bench_mfma(codes.data_ptr(), iters, fold, sink.data_ptr(), cus, stream())
+            assert rc == 0, rc
+        ms = graph_time_ms(mx, max(4, launches // 8))
+        out[key] = {"what": "32 scaled 16x16x128 FP8 MFMAs per wave and step from registers on e4m3 codes, "
+                            + ("each product folded into fp32 by fma (BLOCK128)" if fold else
+                               "accumulated in the matrix core (MXFP8)") + "; 8 waves per CU",
+                    "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+    del codes, sink
     torch.cuda.empty_cache()
     return out
 
@@ -302,6 +324,8 @@ def configs(launches: int, ceil: dict | None) -> list:
     recs = []
     copy_gbs = ceil["copy"]["GB/s"] if ceil else None
     stream_gbs = ceil["weight_stream"]["GB/s"] if ceil else None
+    fold_tf = ceil["mfma_fold_stream"]["TFLOP/s"] if ceil else None
+    mix_tf = ceil["mfma_stream"]["TFLOP/s"] if ceil else None
 
     def note(r):
         recs.append(r)
@@ -341,6 +365,8 @@ def configs(launches: int, ceil: dict | None) -> list:
         extra = None
         if bound == "hbm" and stream_gbs:
             extra = {"frac_weight_stream": round(gb / (ms * 1e-3) / 1e9 / stream_gbs, 4)}
+        elif bound == "mfma" and fold_tf:
+            extra = {"frac_mfma_mix": round(2.0 * M * N * K / (ms * 1e-3) / 1e12 / fold_tf, 4)}
         note(_rec(cfg, w.name, "gemm_blockscaled", ms, bound, flops=2.0 * M * N * K, nbytes=gb, extra=extra))
         del sets, x
         torch.cuda.empty_cache()
@@ -387,7 +413,8 @@ def configs(launches: int, ceil: dict | None) -> list:
                        max(4, launches // 4))
     note(_rec("c5", w.name, "gemm_mx32", ms, "mfma", flops=2.0 * w.M * w.N * w.K,
               nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
-              extra={"scales": "E8M0 bytes, row-major [rows, K/32]"}))
+              extra={"scales": "E8M0 bytes, row-major [rows, K/32]",
+                     **({"frac_mfma_mix": round(2.0 * w.M * w.N * w.K / (ms * 1e-3) / 1e12 / mix_tf, 4)} if mix_tf else {})}))
     # the same operands with both scale tensors as column-major packed words [K/128, rows]
     # (the layout the G=32 quant writes with packed column-major UE8M0 scales)
     def col_words(e):
@@ -399,7 +426,8 @@ def configs(launches: int, ceil: dict | None) -> list:
                        max(4, launches // 4))
     note(_rec("c5", w.name, "gemm_mx32", ms, "mfma", flops=2.0 * w.M * w.N * w.K,
               nbytes=a.nbytes + b.nbytes + ea.nbytes + eb.nbytes + w.M * w.N * 2,
-              extra={"scales": "E8M0 packed words, column-major [K/128, rows]"}))
+              extra={"scales": "E8M0 packed words, column-major [K/128, rows]",
+                     **({"frac_mfma_mix": round(2.0 * w.M * w.N * w.K / (ms * 1e-3) / 1e12 / mix_tf, 4)} if mix_tf else {})}))
     del sets
     torch.cuda.empty_cache()
     return recs
@@ -642,6 +670,9 @@ def run(args) -> dict:
         ceil = ceilings(args.config_launches)
         out["ceilings"] = ceil
         out["kernels"]["group_quant"]["frac_copy"] = round(quant_gbs / ceil["copy"]["GB/s"], 4)
+        # the GEMM against what its own MFMA-and-fold instruction mix sustains from registers
+        out["kernels"]["gemm_blockscaled"]["frac_mfma_mix"] = round(
+            gemm_tflops / ceil["mfma_fold_stream"]["TFLOP/s"], 4)
         _progress("ceilings done")
         out["configs"] = configs(args.config_launches, ceil)
     if not args.no_parity:

@@ -8,6 +8,12 @@
 //   fp8q_bench_stream  reads `bytes` once (one contiguous slice per workgroup, every load of
 //                      a batch issued before any is used) and writes one word per workgroup:
 //                      the weight traffic of the small-M GEMM, which is bound by reading B.
+//   fp8q_bench_mfma    the large GEMM's per-step instruction mix with its operands already in
+//                      registers: per step each wave runs the 8 x 4 scaled 16x16x128 FP8 MFMAs
+//                      of a 128x64 wave tile on real e4m3 codes, and (fold = 1) folds each
+//                      product into fp32 accumulators with one fma per value, as the BLOCK128
+//                      kernels do, or (fold = 0) accumulates in the matrix core, as MXFP8
+//                      does. Eight waves per workgroup (two per SIMD), like the GEMM.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,6 +59,52 @@ __global__ __launch_bounds__(256) void stream_read(const uint8_t* __restrict__ w
   out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = acc;
 }
 
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+template <bool FOLD>
+__global__ __launch_bounds__(512, 1) void mfma_mix(const v8i_t* __restrict__ codes, int iters,
+                                                   float* __restrict__ out) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 512 + threadIdx.x;
+  v8i_t a[2], b[4];  // operand fragments of this lane (6 x 32 bytes of codes)
+#pragma unroll
+  for (int i = 0; i < 2; i++) a[i] = codes[t * 6 + i];
+#pragma unroll
+  for (int j = 0; j < 4; j++) b[j] = codes[t * 6 + 2 + j];
+  const float s = 1.0f + static_cast<float>(threadIdx.x & 7) * 0x1p-10f;  // a fold factor per lane
+  v4f_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = v4f_t{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; it++) {
+    // the operands are opaque to the compiler from step to step, so no product is hoisted
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      // (opaque per row too: rows sharing a fragment must not share their products)
+      asm volatile("" : "+v"(a[i & 1]));
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if constexpr (FOLD) {
+          const v4f_t z = {0.f, 0.f, 0.f, 0.f};
+          const v4f_t pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i & 1], z, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int r = 0; r < 4; r++) acc[i][j][r] = fmaf(pr[r], s, acc[i][j][r]);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i & 1], acc[i][j], 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) sum += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
+  out[t] = sum;  // one word per lane, so no MFMA can be dropped
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,6 +124,20 @@ int fp8q_bench_stream(const void* w, int64_t bytes, void* out, int grid, void* s
   const int64_t slice = ((bytes + grid - 1) / grid + 15) / 16 * 16;
   hipLaunchKernelGGL(stream_read, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint8_t*>(w), bytes, slice, static_cast<uint32_t*>(out));
+  return static_cast<int>(hipGetLastError());
+}
+
+// codes holds grid * 512 * 192 bytes of e4m3 codes (16-byte aligned), out grid * 512 floats.
+// Each lane runs iters steps of 32 MFMAs (2 * 16 * 16 * 128 flops each). Returns 0 or a HIP
+// error code.
+int fp8q_bench_mfma(const void* codes, int iters, int fold, void* out, int grid, void* stream) {
+  if (iters < 1 || grid < 1) return static_cast<int>(hipErrorInvalidValue);
+  if (fold)
+    hipLaunchKernelGGL(mfma_mix<true>, dim3(grid), dim3(512), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const v8i_t*>(codes), iters, static_cast<float*>(out));
+  else
+    hipLaunchKernelGGL(mfma_mix<false>, dim3(grid), dim3(512), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const v8i_t*>(codes), iters, static_cast<float*>(out));
   return static_cast<int>(hipGetLastError());
 }
 
