@@ -293,6 +293,25 @@ def ceilings(launches: int) -> dict:
                     "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
                     "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
     del codes, sink
+    # context: the vendor library's FP8 GEMM (torch._scaled_mm, hipBLASLt) on the dense shape,
+    # with the simpler per-row x per-column fp32 scaling (no block-128 fold)
+    try:
+        xa = torch.from_numpy(synth.weight_codes(8, M, K)).to(dev).view(torch.float8_e4m3fn)
+        wb = torch.from_numpy(synth.weight_codes(9, N, K)).to(dev).view(torch.float8_e4m3fn)
+        sa = torch.ones((M, 1), dtype=torch.float32, device=dev)
+        sbt = torch.ones((1, N), dtype=torch.float32, device=dev)
+        wt = wb.t()
+
+        def mm(i):
+            torch._scaled_mm(xa, wt, scale_a=sa, scale_b=sbt, out_dtype=torch.bfloat16)
+        ms = graph_time_ms(mm, max(4, launches // 4))
+        out["vendor_fp8_gemm"] = {"what": "torch._scaled_mm (hipBLASLt) FP8 [4096, 7168] x [7168, 4096], row x column "
+                                          "fp32 scales, bf16 out (no 128-block fold)",
+                                  "us": round(ms * 1e3, 2),
+                                  "TFLOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        del xa, wb, wt
+    except Exception as ex:  # the backend may lack this form: recorded, not fatal
+        out["vendor_fp8_gemm"] = {"error": repr(ex)[:200]}
     torch.cuda.empty_cache()
     return out
 
