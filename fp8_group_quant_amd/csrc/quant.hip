@@ -220,6 +220,28 @@ __device__ int64_t masked_prefix(const QuantParams& p, int32_t* lds_pref) {
   const int E = static_cast<int>(p.E);
   int32_t* part = lds_pref + E + 1;
   const int tid = threadIdx.x;
+  if (E <= 64) {
+    // one expert per lane of wave 0: an inclusive scan over the wave (6 shuffle steps),
+    // then one barrier instead of the block-wide scan below
+    if (tid < 64) {
+      int32_t c = 0;
+      if (tid < E) {
+        c = p.masked_m[tid];
+        c = c < 0 ? 0 : (c > p.M ? static_cast<int32_t>(p.M) : c);
+      }
+      int32_t inc = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int32_t up = __shfl_up(inc, off, 64);
+        if (tid >= off) inc += up;
+      }
+      if (tid < E) lds_pref[tid] = inc - c;
+      if (tid == E - 1) lds_pref[E] = inc;
+      if (E == 0 && tid == 0) lds_pref[0] = 0;
+    }
+    __syncthreads();
+    return lds_pref[E];
+  }
   const int per = (E + kThreads - 1) / kThreads;
   const int beg = min(tid * per, E), end = min(beg + per, E);
   int32_t local = 0;
@@ -505,7 +527,7 @@ int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, b
   int64_t grid = (items + kWavesPerBlock - 1) / kWavesPerBlock;
   // masked launches rebuild the expert prefix sum in every block: cap the grid there so each
   // wave walks several rows instead
-  grid = std::max<int64_t>(1, std::min<int64_t>(grid, p.masked_m ? 2048 : 65535));
+  grid = std::max<int64_t>(1, std::min<int64_t>(grid, p.masked_m ? 4096 : 65535));
   const size_t lds = p.masked_m ? static_cast<size_t>(p.E + 1 + kThreads) * sizeof(int32_t) : 0;
   const int g = per_token ? 0 : group_size;
   switch (in_dtype) {

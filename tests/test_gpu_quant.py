@@ -251,6 +251,18 @@ def test_masked_small_full(layout):
     _full_case(x, oracle.BF16, 128, oracle.SCALE_F32, layout, masked_m=mm)
 
 
+# Up to 64 experts the expert prefix is one wave's scan; beyond, a block-wide scan: both
+# sides of the boundary, with empty, full and clamped counts among them
+@pytest.mark.parametrize("E", [64, 65, 300])
+def test_masked_many_experts(E):
+    M, K = 8, 256
+    x = _masked_input(E, M, K, 36 + E)
+    mm = synth.masked_rows(36 + E, E, M)
+    mm[0], mm[E // 2], mm[E - 1] = 0, M, M + 3
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_UE8M0, "col", masked_m=mm)
+    _full_case(x, oracle.BF16, 128, oracle.SCALE_F32, "row", masked_m=mm)
+
+
 def test_masked_counts_are_clamped():
     E, M, K = 4, 8, 256
     x = _masked_input(E, M, K, 32)
