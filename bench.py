@@ -48,17 +48,27 @@ BENCH_LIB = os.path.join(ROOT, "fp8_group_quant_amd", "libfp8q_bench.so")
 
 
 def _kernel_source_tag(name: str) -> str:
-    """Hash of a kernel source and the shared internal header, with // comments and blank
-    lines removed: a comment edit keeps the tag, any code change breaks it."""
+    """Hash of a kernel source, the shared internal header and every header of csrc/ that
+    they include (transitively), with // comments and blank lines removed: a comment edit
+    keeps the tag, any code change breaks it."""
     import hashlib
     import re
+    csrc = os.path.join(ROOT, "fp8_group_quant_amd", "csrc")
     h = hashlib.sha256()
-    for fn in (name, "fp8q_internal.h"):
-        with open(os.path.join(ROOT, "fp8_group_quant_amd", "csrc", fn), encoding="utf-8") as f:
+    todo, seen = [name, "fp8q_internal.h"], set()
+    while todo:
+        fn = todo.pop(0)
+        if fn in seen or not os.path.exists(os.path.join(csrc, fn)):
+            continue
+        seen.add(fn)
+        with open(os.path.join(csrc, fn), encoding="utf-8") as f:
             for line in f:
                 line = re.sub(r"//.*$", "", line).rstrip()
                 if line.strip():
                     h.update(line.encode() + b"\n")
+                m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+                if m:
+                    todo.append(m.group(1))
     return h.hexdigest()[:16]
 
 

@@ -1,6 +1,6 @@
 """Builds libfp8q.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
-libfp8q_bench.so (csrc_bench/: the benchmark's reference copy and stream kernels, loaded only
-by bench.py).
+libfp8q_bench.so (csrc_bench/: the benchmark's reference kernels, loaded by bench.py, and the
+exhaustive check of the quantizer's short division forms, loaded by the tests).
 
 Every call recompiles: objects go to fp8_group_quant_amd/_build/, the libraries next to this
 file.

@@ -28,8 +28,10 @@
 //
 // Floating point: this file must be compiled without contraction (-ffp-contract=off) and
 // with correctly rounded fp32 division; the arithmetic sequence is part of the contract
-// (bit-exact results), see fp8q.h.
+// (bit-exact results), see fp8q.h. Divisions whose operands stay in a checked domain use the
+// shorter correctly rounded forms of quant_math.h (same results, fewer instructions).
 #include "fp8q_internal.h"
+#include "quant_math.h"
 
 #pragma clang fp contract(off)
 
@@ -61,6 +63,10 @@ __device__ __forceinline__ float group_max(float v) {
   if constexpr (LANES >= 8) v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
   return v;
 }
+
+// Index of the calling wave in its block as a wave-uniform (scalar) value: the per-item row
+// and address arithmetic derived from it then runs on the scalar unit, not the vector ALU.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ------------------------------------------------------------------ element loads
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -137,37 +143,37 @@ __device__ __forceinline__ void widen(const Raw16<DT>& r, float (&v)[16]) {
 }
 
 // ------------------------------------------------------------------ silu(g) * u
-// exp(t) as a fixed fp32 sequence: Cody-Waite reduction by ln 2 (two-part constant, fma),
-// degree-7 Taylor polynomial in Horner form (fma), scaling by 2^n built from its bits.
-// Constants are the fp32 values nearest to log2(e), ln 2, the remainder of ln 2, and 1/k!.
-__device__ __forceinline__ float exp_fixed(float t) {
-  t = fminf(fmaxf(t, -87.0f), 88.0f);
-  const float n = rintf(t * 0x1.715476p+0f);
-  float r = fmaf(-n, 0x1.62e430p-1f, t);
-  r = fmaf(-n, -0x1.05c610p-29f, r);
-  float p = 0x1.a01a02p-13f;        // 1/7!
-  p = fmaf(p, r, 0x1.6c16c2p-10f);  // 1/6!
-  p = fmaf(p, r, 0x1.111112p-7f);   // 1/5!
-  p = fmaf(p, r, 0x1.555556p-5f);   // 1/4!
-  p = fmaf(p, r, 0x1.555556p-3f);   // 1/3!
-  p = fmaf(p, r, 0x1.000000p-1f);   // 1/2!
-  p = fmaf(p, r, 1.0f);             // 1/1!
-  p = fmaf(p, r, 1.0f);             // 1/0!
-  const float two_n = __uint_as_float(static_cast<uint32_t>(static_cast<int>(n) + 127) << 23);
-  return p * two_n;
-}
-
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float d = 1.0f + exp_fixed(-g);
-  const float s = g / d;  // correctly rounded division
-  return s * u;
+// silu(g) * u = (g / (1 + exp(-g))) * u for the 16 values of a lane, each step rounded to
+// fp32 (exp_fixed, then an IEEE add, a correctly rounded division and a multiply). The
+// division takes the short form unless some lane of the wave holds a gate below -87, where
+// 1 + exp(-g) exceeds 2^126 and its reciprocal is subnormal: that wave takes the general
+// division for its 16 values. Both forms give the same correctly rounded quotient.
+// Must be called by the whole wave (wave-uniform control flow).
+__device__ __forceinline__ void silu_mul16(float (&v)[16], const float (&u)[16]) {
+  float d[16];
+  bool low = false;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    d[j] = 1.0f + exp_fixed(-v[j]);
+    low |= v[j] < -87.0f;
+  }
+  if (__builtin_amdgcn_ballot_w64(low) == 0) {
+#pragma unroll
+    for (int j = 0; j < 16; j++) v[j] = div_short(v[j], d[j]) * u[j];
+  } else {
+    asm volatile("");  // keeps this branch from being speculated into the common path
+#pragma unroll
+    for (int j = 0; j < 16; j++) v[j] = (v[j] / d[j]) * u[j];
+  }
 }
 
 // ------------------------------------------------------------------ scale rules
 template <int FMT, bool I8>
 __device__ __forceinline__ float group_multiplier(float amax, uint32_t& scale_bits) {
   static_assert(!I8 || FMT == FP8Q_SCALE_F32, "int8 output takes fp32 scales");
-  const float r = amax / (I8 ? kImax : kFmax);  // correctly rounded
+  // amax >= 1e-10 (the floor), so both divisions are in their short forms' checked domains:
+  // r = amax / C, then 1 / r with r in [2e-13, 3e36] or infinite
+  const float r = I8 ? div_by_const<127>(amax) : div_by_const<448>(amax);
   if constexpr (FMT == FP8Q_SCALE_UE8M0) {
     const uint32_t bits = __float_as_uint(r);
     const uint32_t ex = ((bits >> 23) & 0xFFu) + ((bits & 0x7FFFFFu) != 0u ? 1u : 0u);
@@ -175,7 +181,7 @@ __device__ __forceinline__ float group_multiplier(float amax, uint32_t& scale_bi
     return __uint_as_float((254u - ex) << 23);  // 2^(127-(ex-127)), exact
   } else {
     scale_bits = __float_as_uint(r);
-    return 1.0f / r;  // correctly rounded
+    return div_short(1.0f, r);
   }
 }
 
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
 
   const int64_t items = total_rows * p.nseg;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6); t < items;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_index(); t < items;
        t += nwaves) {
     const int64_t row = t / p.nseg;
     const int seg = static_cast<int>(t - row * p.nseg);
@@ -335,8 +341,7 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
         if constexpr (SILU) {
           float u[16];
           widen<DT>(rb[c], u);
-#pragma unroll
-          for (int j = 0; j < 16; j++) v[j] = silu_mul(v[j], u[j]);
+          silu_mul16(v, u);
         }
         float amax = 0.0f;
 #pragma unroll
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void token_quant_kernel(QuantParams p) {
   const bool resident = nc <= kReg;
 
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6); row < total_rows;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave_index(); row < total_rows;
        row += nwaves) {
     int64_t e, m;
     row_at(p, lds_pref, masked, row, e, m);
@@ -420,8 +425,7 @@ __global__ __launch_bounds__(kThreads) void token_quant_kernel(QuantParams p) {
       if constexpr (SILU) {
         float u[16];
         widen<DT>(rb[c], u);
-#pragma unroll
-        for (int j = 0; j < 16; j++) v[j] = silu_mul(v[j], u[j]);
+        silu_mul16(v, u);
       }
     };
 

@@ -42,6 +42,12 @@ def test_traffic_tag_ignores_comments_only(tmp_path, monkeypatch):
     (csrc / "k.hip").write_text("int f() { return 1; }\n")
     (csrc / "fp8q_internal.h").write_text("struct P { int a; int b; };\n")
     assert bench._kernel_source_tag("k.hip") != t0
+    # headers included from csrc/ count too, transitively
+    (csrc / "fp8q_internal.h").write_text('#include "more.h"\nstruct P { int a; };\n')
+    (csrc / "more.h").write_text("int g();\n")
+    t1 = bench._kernel_source_tag("k.hip")
+    (csrc / "more.h").write_text("int g(int);\n")
+    assert bench._kernel_source_tag("k.hip") != t1
 
 
 def test_committed_traffic_matches_the_current_kernels():

@@ -22,7 +22,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE_C = os.path.join(ROOT, "oracle", "fp8q_oracle.c")
-QUANT_HIP = os.path.join(ROOT, "fp8_group_quant_amd", "csrc", "quant.hip")
+QUANT_MATH = os.path.join(ROOT, "fp8_group_quant_amd", "csrc", "quant_math.h")
 
 _HEX = r"-?0x[0-9a-fA-F]\.[0-9a-fA-F]+p[+-]?\d+f"
 
@@ -99,7 +99,7 @@ def test_oracle_literals_equal_their_definitions():
 
 
 def test_kernel_literals_equal_their_definitions():
-    src = open(QUANT_HIP, encoding="utf-8").read()
+    src = open(QUANT_MATH, encoding="utf-8").read()
     body = src[src.index("float exp_fixed(float t)"):]
     body = body[:body.index("\n}\n")]
     code = "\n".join(re.sub(r"//.*$", "", line) for line in body.splitlines())

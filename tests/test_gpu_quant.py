@@ -138,6 +138,29 @@ def test_silu_large_magnitudes():
     _full_case(x, oracle.BF16, 64, oracle.SCALE_UE8M0, "row", silu=True)
 
 
+def test_silu_division_paths():
+    # fp32 gates at the point (-87) below which a wave computes g / (1 + exp(-g)) with the
+    # general division instead of the short form, and other edge values of the quotient:
+    # rows 0-1 keep every 1024-wide chunk on the short form, rows 2-6 send one chunk or both
+    # to the general division. Codes and scales must match the oracle either way.
+    K = 2048
+    xb = synth.activations_bf16(31, 7, 2 * K)
+    x = (xb.astype(np.uint32) << 16).view(np.float32).copy()
+    f32 = np.float32
+    x[1, 5], x[1, 700], x[1, 1800] = f32(-87.0), f32(-86.99999), f32(-80.0)
+    x[2, 3] = np.nextafter(f32(-87.0), f32(-np.inf))
+    x[3, 1030], x[3, 1500] = f32(-87.3365479), f32(-88.5)
+    x[4, :64] = np.linspace(-100.0, -80.0, 64, dtype=np.float32)
+    x[5, 10:15] = [f32(1e-40), f32(-1e-40), f32(0.0), f32(-0.0), f32(1.4e-45)]
+    x[5, 1100] = f32(-1e30)
+    x[6, 20], x[6, K + 20] = f32(3e38), f32(0.5)
+    x[6, 21], x[6, K + 21] = f32(-3e38), f32(0.5)
+    x[6, 1200], x[6, K + 1200] = f32(2e9), f32(-3.0)
+    for G, fmt, layout in ((128, oracle.SCALE_F32, "row"), (32, oracle.SCALE_UE8M0, "col"),
+                           (K, oracle.SCALE_F32, "row"), (K, oracle.SCALE_UE8M0, "col")):
+        _full_case(x, oracle.F32, G, fmt, layout, silu=True)
+
+
 def test_strided_rows():
     # rows of x and q taken from wider buffers (row stride > K)
     f = fq()
