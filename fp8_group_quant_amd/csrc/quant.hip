@@ -369,6 +369,61 @@ __global__ __launch_bounds__(kThreads) void group_quant_kernel(QuantParams p) {
   }
 }
 
+// ------------------------------------------------------------------ flat, column-major UE8M0
+// Same arithmetic as group_quant_kernel (one 1024-element chunk per wave), for flat problems
+// whose UE8M0 scales are column-major bytes ([K/G][M], M % 4 == 0, 4-byte aligned strides):
+// the 4 waves of a block take rows 4q .. 4q+3 of one chunk, so each group's 4 scale bytes are
+// adjacent. The waves put them in LDS and one wave writes every group's 4 bytes as one word:
+// a fourth of the scattered scale stores (each byte of a group lands in its own cache line).
+template <int DT, int G, bool SILU>
+__global__ __launch_bounds__(kThreads) void group_quant_rows4_kernel(QuantParams p) {
+  constexpr int LANES = G / kPerLane;
+  constexpr int kGroups = kChunk / G;  // groups per chunk
+  __shared__ uint32_t words[2][kGroups];  // by iteration parity
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_index();
+  const int64_t blocks = (p.M >> 2) * p.nseg;  // (row quad, chunk) pairs
+  int par = 0;
+  for (int64_t bt = blockIdx.x; bt < blocks; bt += gridDim.x, par ^= 1) {
+    const int64_t q4 = bt / p.nseg;
+    const int seg = static_cast<int>(bt - q4 * p.nseg);
+    const int64_t m = 4 * q4 + wave;
+    const int64_t k = static_cast<int64_t>(seg) * kChunk + lane * kPerLane;
+    Raw16<DT> ra, rb;
+    zero_raw<DT>(ra);
+    if constexpr (SILU) zero_raw<DT>(rb);
+    if (k < p.K) {
+      load_raw<DT>(p.x, m * p.x_sm + k, ra);
+      if constexpr (SILU) load_raw<DT>(p.x, m * p.x_sm + p.K + k, rb);
+    }
+    float v[16];
+    widen<DT>(ra, v);
+    if constexpr (SILU) {
+      float u[16];
+      widen<DT>(rb, u);
+      silu_mul16(v, u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; j++) amax = fmaxf(amax, fabsf(v[j]));
+    amax = group_max<LANES>(amax);  // all lanes active here
+    amax = fmaxf(amax, kEps);
+    uint32_t sbits;
+    const float inv = group_multiplier<FP8Q_SCALE_UE8M0, false>(amax, sbits);
+    if (k < p.K) *reinterpret_cast<u32x4*>(p.q + m * p.q_sm + k) = encode16<false>(v, inv);
+    if ((lane & (LANES - 1)) == 0)
+      reinterpret_cast<uint8_t*>(words[par])[4 * (lane / LANES) + wave] = static_cast<uint8_t>(sbits);
+    __syncthreads();
+    // group g of rows 4q..4q+3: bytes g * s_sg + 4q .. +3; groups past K are not stored. The
+    // other buffer is written next, and this one again only after the next barrier.
+    if (wave == 0 && lane < kGroups) {
+      const int64_t g = static_cast<int64_t>(seg) * kGroups + lane;
+      if (g * G < p.K)
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.s) + g * p.s_sg + 4 * q4) = words[par][lane];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ the per-token kernel
 // Max over all 64 lanes, returned wave-uniform: 8-lane DPP butterfly, row_mirror for 16
 // lanes, then the four 16-lane rows through readlane.
@@ -502,6 +557,21 @@ void launch_variant(int fmt, bool silu, bool i8, const QuantParams& p, int grid,
   else launch_one<DT, G, FP8Q_SCALE_F32, false, false>(p, grid, lds, s);
 }
 
+template <int DT, int G>
+void launch_rows4(bool silu, const QuantParams& p, int grid, hipStream_t s) {
+  if (silu)
+    hipLaunchKernelGGL((group_quant_rows4_kernel<DT, G, true>), dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((group_quant_rows4_kernel<DT, G, false>), dim3(grid), dim3(kThreads), 0, s, p);
+}
+
+template <int DT>
+void launch_rows4_g(int g, bool silu, const QuantParams& p, int grid, hipStream_t s) {
+  if (g == 32) launch_rows4<DT, 32>(silu, p, grid, s);
+  else if (g == 64) launch_rows4<DT, 64>(silu, p, grid, s);
+  else launch_rows4<DT, 128>(silu, p, grid, s);
+}
+
 template <int DT>
 void launch_g(int g, int fmt, bool silu, bool i8, const QuantParams& p, int grid, size_t lds, hipStream_t s) {
   if (g == 32) launch_variant<DT, 32>(fmt, silu, i8, p, grid, lds, s);
@@ -534,6 +604,23 @@ int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, b
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, p.masked_m ? 4096 : 65535));
   const size_t lds = p.masked_m ? static_cast<size_t>(p.E + 1 + kThreads) * sizeof(int32_t) : 0;
   const int g = per_token ? 0 : group_size;
+  // flat problems with column-major UE8M0 bytes, rows a multiple of 4 and word-aligned scale
+  // columns: the row-quad kernel, which writes each group's scales 4 rows at a time. Measured
+  // on dense M=4096 x 7168: 17.8-18.6 us against 18.9-19.0 (outputs identical).
+  const bool rows4 = !per_token && !p.masked_m && p.E == 1 && scale_fmt == FP8Q_SCALE_UE8M0 && !i8 && !p.packed &&
+                     p.s_sm == 1 && p.M % 4 == 0 && p.s_sg % 4 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0;
+  if (rows4) {
+    const int64_t blocks = (p.M / 4) * p.nseg;
+    const int rgrid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(blocks, 65535)));
+    switch (in_dtype) {
+      case FP8Q_DTYPE_BF16: launch_rows4_g<FP8Q_DTYPE_BF16>(g, silu, p, rgrid, stream); break;
+      case FP8Q_DTYPE_F16: launch_rows4_g<FP8Q_DTYPE_F16>(g, silu, p, rgrid, stream); break;
+      default: launch_rows4_g<FP8Q_DTYPE_F32>(g, silu, p, rgrid, stream); break;
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(FP8Q_ELAUNCH, std::string("group quant launch: ") + hipGetErrorString(err));
+    return FP8Q_OK;
+  }
   switch (in_dtype) {
     case FP8Q_DTYPE_BF16: launch_g<FP8Q_DTYPE_BF16>(g, scale_fmt, silu, i8, p, (int)grid, lds, stream); break;
     case FP8Q_DTYPE_F16: launch_g<FP8Q_DTYPE_F16>(g, scale_fmt, silu, i8, p, (int)grid, lds, stream); break;

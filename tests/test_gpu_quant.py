@@ -177,6 +177,39 @@ def test_strided_rows():
     assert np.all(full[:, 896:] == FILL)
 
 
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("in_dtype", [oracle.BF16, oracle.F16, oracle.F32])
+def test_col_major_ue8m0_row_quads(G, in_dtype):
+    # flat, column-major UE8M0 bytes, rows a multiple of 4: the kernel that writes each group's
+    # scale bytes for 4 rows as one word. K = 2560 ends in half a chunk.
+    xb = synth.activations_bf16(32, 44, 2560, outlier_p=0.02)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    x = xb if in_dtype == oracle.BF16 else (xf.astype(np.float16).view(np.uint16) if in_dtype == oracle.F16 else xf)
+    _full_case(x, in_dtype, G, oracle.SCALE_UE8M0, "col")
+    if in_dtype == oracle.BF16:
+        xs = synth.activations_bf16(33, 24, 2 * 1536)
+        _full_case(xs, in_dtype, G, oracle.SCALE_UE8M0, "col", silu=True)
+
+
+def test_col_major_ue8m0_unaligned_scale_columns():
+    # a column stride that is not a multiple of 4 bytes (and rows not a multiple of 4) keeps
+    # the one-byte scale stores; the padding between columns stays untouched
+    f = fq()
+    for M, pad in ((40, 2), (42, 0), (40, 4)):
+        xb = synth.activations_bf16(34, M, 1536)
+        x = torch.from_numpy(xb).cuda().view(torch.bfloat16)
+        q = torch.empty((M, 1536), dtype=torch.uint8, device="cuda")
+        store = torch.full((1536 // 128, M + pad), FILL, dtype=torch.uint8, device="cuda")
+        s = store[:, :M].t()
+        f.fp8q_group_quant(x, q, s, 128)
+        torch.cuda.synchronize()
+        qo, so = _oracle(xb, oracle.BF16, 128, oracle.SCALE_UE8M0, "col")
+        _assert_same(q.cpu().numpy(), qo, f"q M={M} pad={pad}")
+        sn = store.cpu().numpy()
+        _assert_same(np.ascontiguousarray(sn[:, :M]), so, f"scales M={M} pad={pad}")
+        assert np.all(sn[:, M:] == FILL)
+
+
 def test_every_bf16_value_through_unit_scale():
     # each group starts with 448, so its UE8M0 byte is 127 and the multiplier is exactly 1:
     # every finite bf16 value in [-448, 448] reaches the fp8 conversion unchanged
