@@ -1950,6 +1950,7 @@ __global__ __launch_bounds__(256, 1) void gemm_splitk_kernel(GemmParams p, int S
 }
 
 constexpr int kMaxSplit = 16;
+constexpr int kMinRangeBlocks = 4;
 
 // Y[m][n] = bf16( sum over the S ranges, in range order, of part[s][m][n] ); each thread four
 // consecutive columns of one row, all S loads issued before the first add.
@@ -1986,7 +1987,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // The split for a problem on `cus` CUs: sm 16-row slices of A (M <= 64: 4, else 8), the
 // fewest ranges that keep every range within the blocks a workgroup holds, raised (up to
-// kMaxSplit) until the grid fills the chip. Ranges differ by at most one block.
+// kMaxSplit) until the grid fills the chip, but not below kMinRangeBlocks blocks per range
+// unless the register limit needs shorter ones: for a small problem a second launch (the
+// reduction) costs more than the parallelism buys (M=64, N=256, K=512: 7.8 us with 4 ranges,
+// 5.7 us with one). Ranges differ by at most one block.
 struct SplitPlan {
   int sm;      // 4 or 8
   int S;       // K ranges
@@ -2003,7 +2007,8 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t tiles = (N + C - 1) / C;
   const int64_t s_min = (nkb + nbmax - 1) / nbmax;  // ranges short enough for the registers
   const int64_t s_fill = std::max<int64_t>(1, std::min<int64_t>(cus / tiles, kMaxSplit));
-  const int64_t S = std::min<int64_t>(std::max(s_min, s_fill), nkb);
+  const int64_t s_len = std::max<int64_t>(1, nkb / kMinRangeBlocks);  // ranges of >= kMinRangeBlocks blocks
+  const int64_t S = std::max(s_min, std::min<int64_t>(std::min(s_fill, s_len), nkb));
   if (S > kMaxSplit || (nkb + S - 1) / S > nbmax) return pl;
   pl.S = static_cast<int>(S);
   pl.ws = S > 1 ? S * M * N * 4 : 0;

@@ -281,10 +281,11 @@ def _split_ranges(M, N, K):
 
 
 # 16 < M <= 128 with a workspace: the split-K kernel (64-row variant for M <= 64, 128-row
-# above) with K ranges of one block, of uneven length (K / 128 not a multiple of the range
-# count), ragged N and rows past M inside the last 16-row slice, under every scale layout
-@pytest.mark.parametrize("M,N,K", [(17, 300, 1024), (32, 520, 2048), (33, 300, 1024), (64, 1000, 2048),
-                                   (65, 260, 3072), (100, 200, 1536), (128, 130, 896)])
+# above) with short K ranges (the split's minimum of 4 blocks) of uneven length (K / 128 not
+# a multiple of the range count), ragged N and rows past M inside the last 16-row slice,
+# under every scale layout
+@pytest.mark.parametrize("M,N,K", [(17, 300, 1152), (32, 520, 2176), (33, 300, 1152), (64, 1000, 2176),
+                                   (65, 260, 3200), (100, 200, 1664), (128, 130, 1792)])
 @pytest.mark.parametrize("sa_kind", ["f32-row", "ue8m0-col", "packed-col", "ue8m0-row"])
 @pytest.mark.parametrize("sb_kind", ["f32", "ue8m0"])
 def test_split_k_full(M, N, K, sa_kind, sb_kind):
