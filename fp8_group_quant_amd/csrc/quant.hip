@@ -43,6 +43,7 @@ constexpr int kThreads = 64 * kWavesPerBlock;
 constexpr int kPerLane = 16;    // consecutive elements owned by one lane per chunk (32 B of bf16)
 constexpr int kChunk = 64 * kPerLane;  // elements per wave-wide chunk
 constexpr int kMaxChunks = 1;   // chunks per wave item (one: see launch_group_quant)
+constexpr int kTokenRegB = 2;   // chunks per wave of the one-block-per-row per-token kernel
 constexpr float kFmax = 448.0f;
 constexpr float kImax = 127.0f;  // int8 output: largest code used
 constexpr float kEps = 0x1.b7cdfep-34f;  // 1e-10f, the amax floor
@@ -538,12 +539,109 @@ __global__ __launch_bounds__(kThreads) void token_quant_kernel(QuantParams p) {
   }
 }
 
+// Per-token, one block per row: wave w of the block takes chunks w and w + 4 of the row (held
+// in registers), the four waves' maxima meet in LDS, and every wave then quantizes its own
+// chunks. A launch has four times the waves of the one-wave kernel above, so the loads of
+// some rows overlap the stores of others. Rows of at most 4 * kTokenRegB chunks (8192
+// elements); the one-wave kernel takes longer rows. (Sized for more chunks per wave, the
+// kernel would hold their registers for every row and lose occupancy.)
+template <int DT, int FMT, bool SILU, bool I8>
+__global__ __launch_bounds__(kThreads) void token_quant_block_kernel(QuantParams p) {
+  extern __shared__ int32_t lds_pref[];
+  __shared__ float wave_amax[2][kWavesPerBlock];  // by iteration parity
+  constexpr int kRegB = kTokenRegB;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_index();
+  const bool masked = p.masked_m != nullptr;
+  const int64_t total_rows = masked ? masked_prefix(p, lds_pref) : p.E * p.M;
+  const int nc = p.chunks_per_row;
+  int par = 0;
+  for (int64_t row = blockIdx.x; row < total_rows; row += gridDim.x, par ^= 1) {
+    int64_t e, m;
+    row_at(p, lds_pref, masked, row, e, m);
+    const int64_t xrow = e * p.x_se + m * p.x_sm;
+    uint8_t* qrow = p.q + e * p.q_se + m * p.q_sm;
+    Raw16<DT> ra[kRegB];
+    Raw16<DT> rb[SILU ? kRegB : 1];
+#pragma unroll
+    for (int i = 0; i < kRegB; i++) {
+      zero_raw<DT>(ra[i]);
+      if constexpr (SILU) zero_raw<DT>(rb[i]);
+      const int c = wave + kWavesPerBlock * i;
+      const int64_t k = static_cast<int64_t>(c) * kChunk + lane * kPerLane;
+      if (c < nc && k < p.K) {
+        load_raw<DT>(p.x, xrow + k, ra[i]);
+        if constexpr (SILU) load_raw<DT>(p.x, xrow + p.K + k, rb[i]);
+      }
+    }
+    // pass 1: this wave's share of the row amax (lanes past K hold zeros); silu values kept
+    float keep[SILU ? kRegB : 1][16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRegB; i++) {
+      if (wave + kWavesPerBlock * i < nc) {
+        float v[16];
+        widen<DT>(ra[i], v);
+        if constexpr (SILU) {
+          float u[16];
+          widen<DT>(rb[i], u);
+          silu_mul16(v, u);
+#pragma unroll
+          for (int j = 0; j < 16; j++) keep[i][j] = v[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j++) amax = fmaxf(amax, fabsf(v[j]));
+      }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) wave_amax[par][wave] = amax;
+    __syncthreads();  // the other buffer is written next, this one again after the next barrier
+    amax = fmaxf(fmaxf(wave_amax[par][0], wave_amax[par][1]), fmaxf(wave_amax[par][2], wave_amax[par][3]));
+    amax = fmaxf(amax, kEps);
+    uint32_t sbits;
+    const float inv = group_multiplier<FMT, I8>(amax, sbits);
+    if (wave == 0 && lane == 0) {
+      const int64_t sidx = e * p.s_se + m * p.s_sm;
+      if constexpr (FMT == FP8Q_SCALE_UE8M0)
+        static_cast<uint8_t*>(p.s)[sidx] = static_cast<uint8_t>(sbits);
+      else
+        static_cast<uint32_t*>(p.s)[sidx] = sbits;
+    }
+    // pass 2: quantize this wave's chunks
+#pragma unroll
+    for (int i = 0; i < kRegB; i++) {
+      const int c = wave + kWavesPerBlock * i;
+      const int64_t k = static_cast<int64_t>(c) * kChunk + lane * kPerLane;
+      if (c < nc && k < p.K) {
+        float v[16];
+        if constexpr (SILU) {
+#pragma unroll
+          for (int j = 0; j < 16; j++) v[j] = keep[i][j];
+        } else {
+          widen<DT>(ra[i], v);
+        }
+        *reinterpret_cast<u32x4*>(qrow + k) = encode16<I8>(v, inv);
+      }
+    }
+  }
+}
+
+// Whether a per-token row goes to token_quant_block_kernel (one block per row): its chunks
+// fit the four waves' registers.
+constexpr bool token_rows_per_block(int /*dt*/, bool /*silu*/, int chunks_per_row) {
+  return chunks_per_row <= kWavesPerBlock * kTokenRegB;
+}
+
 // Instantiated combinations: e4m3 output with fp32 or UE8M0 scales, with or without silu;
 // int8 output with fp32 scales, without silu. G == 0 selects the per-token kernel.
 template <int DT, int G, int FMT, bool SILU, bool I8>
 void launch_one(const QuantParams& p, int grid, size_t lds, hipStream_t stream) {
-  if constexpr (G == 0)
-    hipLaunchKernelGGL((token_quant_kernel<DT, FMT, SILU, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
+  if constexpr (G == 0) {
+    if (token_rows_per_block(DT, SILU, p.chunks_per_row))  // the grid is then one block per row
+      hipLaunchKernelGGL((token_quant_block_kernel<DT, FMT, SILU, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
+    else
+      hipLaunchKernelGGL((token_quant_kernel<DT, FMT, SILU, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
+  }
   else
     hipLaunchKernelGGL((group_quant_kernel<DT, G, FMT, SILU, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
 }
@@ -599,6 +697,7 @@ int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, b
   p.nseg = per_token ? 1 : chunks;
   const int64_t items = rows_est * p.nseg;
   int64_t grid = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (per_token && token_rows_per_block(in_dtype, silu, chunks)) grid = rows_est;  // one block per row
   // masked launches rebuild the expert prefix sum in every block: cap the grid there so each
   // wave walks several rows instead
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, p.masked_m ? 4096 : 65535));
