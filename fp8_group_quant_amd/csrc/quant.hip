@@ -194,13 +194,18 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -kFmax), kFmax); }
 
-// int8: clamp to +-127, round to nearest even (v_rndne_f32), exact conversion, 4 bytes
-// packed little-endian
-__device__ __forceinline__ uint32_t i8_code(float v) {
-  return static_cast<uint32_t>(static_cast<int>(__builtin_rintf(fminf(fmaxf(v, -kImax), kImax)))) & 0xFFu;
+// int8: clamp to +-127, round to the nearest integer with ties to even, 4 bytes packed
+// little-endian. After the clamp |x| <= 127, so the fp32 sum x + 1.5 * 2^23 lies in [2^23,
+// 2^24), where the spacing is 1: the add rounds x to an integer (ties to even, the same
+// value as rint) and leaves it in the low mantissa bits as 0x400000 + n, whose low byte is n
+// in two's complement. v_perm_b32 then gathers the four low bytes (selector 0x0c: zero).
+__device__ __forceinline__ uint32_t i8_bits(float v) {
+  return __float_as_uint(fminf(fmaxf(v, -kImax), kImax) + 0x1.8p23f);
 }
 __device__ __forceinline__ uint32_t cvt4_i8(float a, float b, float c, float d) {
-  return i8_code(a) | (i8_code(b) << 8) | (i8_code(c) << 16) | (i8_code(d) << 24);
+  const uint32_t lo = __builtin_amdgcn_perm(i8_bits(b), i8_bits(a), 0x0c0c0400u);  // a, b
+  const uint32_t hi = __builtin_amdgcn_perm(i8_bits(d), i8_bits(c), 0x0c0c0400u);  // c, d
+  return lo | (hi << 16);
 }
 
 // 16 values times the multiplier, as 16 output codes (e4m3 after the clamp to +-448, or
