@@ -110,7 +110,7 @@ def _counter_dispatches(run_dir: str, counter: str) -> list:
 CALIBRATION_ELEMS = 1 << 24  # bf16 values the calibration copies move (32 MiB in, 16 MiB out)
 
 # kernels of each source file, by name
-_KERNEL_FILES = {"quant.hip": ("group_quant_kernel", "token_quant_kernel"),
+_KERNEL_FILES = {"quant.hip": ("group_quant_", "token_quant_"),
                  "gemm.hip": ("gemm_", "splitk_reduce_kernel")}
 
 

@@ -85,8 +85,8 @@ def test_record_traffic_scales_by_the_calibration_copy(tmp_path, monkeypatch):
         write += [("copy_hi_bytes(...)", d, "WRITE_SIZE", n / 2048), ("copy_hi_bytes(...)", d, "WRITE_SIZE", n / 2048)]
     for _ in range(3):
         d += 1
-        fetch += [("group_quant_kernel<0, 128>", d, "FETCH_SIZE", 100.0)]
-        write += [("group_quant_kernel<0, 128>", d, "WRITE_SIZE", 50.0)]
+        fetch += [("group_quant_rows4_kernel<0, 128, false>", d, "FETCH_SIZE", 100.0)]
+        write += [("group_quant_rows4_kernel<0, 128, false>", d, "WRITE_SIZE", 50.0)]
         d += 1
         fetch += [("gemm_splitk_kernel<8, 1, 0>", d, "FETCH_SIZE", 1000.0)]
         write += [("gemm_splitk_kernel<8, 1, 0>", d, "WRITE_SIZE", 400.0)]
