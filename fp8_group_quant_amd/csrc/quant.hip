@@ -633,16 +633,14 @@ __global__ __launch_bounds__(kThreads) void token_quant_block_kernel(QuantParams
 
 // Whether a per-token row goes to token_quant_block_kernel (one block per row): its chunks
 // fit the four waves' registers.
-constexpr bool token_rows_per_block(int /*dt*/, bool /*silu*/, int chunks_per_row) {
-  return chunks_per_row <= kWavesPerBlock * kTokenRegB;
-}
+constexpr bool token_rows_per_block(int chunks_per_row) { return chunks_per_row <= kWavesPerBlock * kTokenRegB; }
 
 // Instantiated combinations: e4m3 output with fp32 or UE8M0 scales, with or without silu;
 // int8 output with fp32 scales, without silu. G == 0 selects the per-token kernel.
 template <int DT, int G, int FMT, bool SILU, bool I8>
 void launch_one(const QuantParams& p, int grid, size_t lds, hipStream_t stream) {
   if constexpr (G == 0) {
-    if (token_rows_per_block(DT, SILU, p.chunks_per_row))  // the grid is then one block per row
+    if (token_rows_per_block(p.chunks_per_row))  // the grid is then one block per row
       hipLaunchKernelGGL((token_quant_block_kernel<DT, FMT, SILU, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
     else
       hipLaunchKernelGGL((token_quant_kernel<DT, FMT, SILU, I8>), dim3(grid), dim3(kThreads), lds, stream, p);
@@ -702,7 +700,7 @@ int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, b
   p.nseg = per_token ? 1 : chunks;
   const int64_t items = rows_est * p.nseg;
   int64_t grid = (items + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (per_token && token_rows_per_block(in_dtype, silu, chunks)) grid = rows_est;  // one block per row
+  if (per_token && token_rows_per_block(chunks)) grid = rows_est;  // one block per row
   // masked launches rebuild the expert prefix sum in every block: cap the grid there so each
   // wave walks several rows instead
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, p.masked_m ? 4096 : 65535));
