@@ -11,7 +11,8 @@
 // Two variants share that rule. int8 output (the PR's ref_int8 reference) uses 127 in place
 // of 448: s = amax/127 in fp32, multiplier 1/s, clamp to +-127, nearest integer with ties
 // to even. Per-token quantization (TeleFuser's per-token FP8 example, scale [M, 1]) is the
-// rule with one group per row (G = K), run by a whole-row kernel below.
+// rule with one group per row (G = K), run by the whole-row kernels below (one block per row,
+// or one wave per row for rows past 8192 elements).
 //
 // Mapping to CDNA4:
 //   - one wavefront (64 lanes) streams a segment of one row; each lane owns 16
@@ -25,6 +26,8 @@
 //   - masked (EP-MoE) dispatch: each block turns masked_m into a prefix sum in LDS and
 //     the waves walk the flattened list of valid rows only, so the launch scales with
 //     the number of valid rows, never with the capacity.
+//   - flat problems with column-major UE8M0 scales give the 4 waves of a block 4
+//     consecutive rows of one chunk, so each group's scale bytes go out as one word.
 //
 // Floating point: this file must be compiled without contraction (-ffp-contract=off) and
 // with correctly rounded fp32 division; the arithmetic sequence is part of the contract
@@ -686,8 +689,9 @@ void launch_g(int g, int fmt, bool silu, bool i8, const QuantParams& p, int grid
 // Picks the segment length and the grid, then launches. Measured on MI355X: one chunk per
 // wave item and one wave per item (as many waves as the problem has chunks) streams best;
 // the hardware's own wave scheduling keeps HBM busier than longer per-wave segments.
-// group_size 32/64/128 runs the group kernel; any other value is G = K (per-token), run
-// with one wave per row.
+// group_size 32/64/128 runs the group kernel (or, for flat column-major UE8M0 scales, the
+// row-quad kernel); any other value is G = K (per-token), run with one block per row up to
+// 8192 elements and one wave per row beyond.
 int launch_group_quant(int in_dtype, int scale_fmt, int group_size, bool silu, bool i8, QuantParams p,
                        int64_t expected_m, hipStream_t stream) {
   const bool per_token = group_size != 32 && group_size != 64 && group_size != 128;
