@@ -197,17 +197,11 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -kFmax), kFmax); }
 
-// int8: clamp to +-127, round to the nearest integer with ties to even, 4 bytes packed
-// little-endian. After the clamp |x| <= 127, so the fp32 sum x + 1.5 * 2^23 lies in [2^23,
-// 2^24), where the spacing is 1: the add rounds x to an integer (ties to even, the same
-// value as rint) and leaves it in the low mantissa bits as 0x400000 + n, whose low byte is n
-// in two's complement. v_perm_b32 then gathers the four low bytes (selector 0x0c: zero).
-__device__ __forceinline__ uint32_t i8_bits(float v) {
-  return __float_as_uint(fminf(fmaxf(v, -kImax), kImax) + 0x1.8p23f);
-}
+// int8: four codes (int8_code_bits: clamp to +-127, round with ties to even, code in the low
+// byte), packed little-endian; v_perm_b32 gathers the low bytes (selector 0x0c: zero).
 __device__ __forceinline__ uint32_t cvt4_i8(float a, float b, float c, float d) {
-  const uint32_t lo = __builtin_amdgcn_perm(i8_bits(b), i8_bits(a), 0x0c0c0400u);  // a, b
-  const uint32_t hi = __builtin_amdgcn_perm(i8_bits(d), i8_bits(c), 0x0c0c0400u);  // c, d
+  const uint32_t lo = __builtin_amdgcn_perm(int8_code_bits(b), int8_code_bits(a), 0x0c0c0400u);  // a, b
+  const uint32_t hi = __builtin_amdgcn_perm(int8_code_bits(d), int8_code_bits(c), 0x0c0c0400u);  // c, d
   return lo | (hi << 16);
 }
 

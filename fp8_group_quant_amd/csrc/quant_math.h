@@ -1,8 +1,10 @@
 // quant_math.h — the fp32 arithmetic of the quantization kernels that is more than one
-// instruction: the fixed exp of the fused silu, and correctly rounded division in short forms.
+// instruction: the fixed exp of the fused silu, correctly rounded division in short forms, and
+// the int8 encode.
 //
 // Every function here returns exactly the value its plain definition gives (the fixed exp
-// sequence, or the correctly rounded quotient); the short forms only take fewer instructions.
+// sequence, the correctly rounded quotient, the rounded int8 code); the short forms only take
+// fewer instructions.
 // Each domain stated below was checked on every fp32 input against the compiler's IEEE
 // division by fp8q_check_division in the benchmark library (csrc_bench/division_check.hip).
 //
@@ -66,6 +68,15 @@ __device__ __forceinline__ float div_by_const(float a) {
   const float r = fmaf(-kC, q, a);
   q = fmaf(r, kInv, q);
   return __builtin_amdgcn_div_fixupf(q, kC, a);
+}
+
+// The int8 code of v (clamped to +-127, rounded to the nearest integer with ties to even) in
+// the low byte of the result, in two's complement. After the clamp the fp32 sum
+// v + 1.5 * 2^23 lies in [2^23, 2^24), where the spacing is 1, so the add itself rounds v to an
+// integer n (ties to even, the value rint gives) and the sum's bits are 0x4B400000 + n.
+// Checked on all 2^32 inputs against the clamp followed by rint and a conversion.
+__device__ __forceinline__ uint32_t int8_code_bits(float v) {
+  return __float_as_uint(fminf(fmaxf(v, -127.0f), 127.0f) + 0x1.8p23f);
 }
 
 }  // namespace fp8q

@@ -1,4 +1,5 @@
-// division_check.hip — exhaustive check of the short fp32 forms in csrc/quant_math.h
+// division_check.hip — exhaustive check of the short fp32 forms in csrc/quant_math.h (the
+// divisions, the exp's scaling step and the int8 encode)
 // (libfp8q_bench.so; run by the tests, not part of the fp8q boundary).
 //
 // For every one of the 2^32 fp32 bit patterns x that falls in a form's domain, the short
@@ -10,6 +11,7 @@
 //   which 2  amax / 127     div_by_const<127>(a) vs a / 127, a = |x|;        domain !(a < 1e-10)
 //   which 3  1 / r          div_short(1, r) vs 1 / r, r = |x|;   domain r in [1e-13, 1e37], inf, NaN
 //   which 4  exp_fixed      ldexp form vs p * 2^n with 2^n built from its exponent bits; all x
+//   which 5  int8 code      low byte of int8_code_bits(x) vs (int)rint(clamp(x, +-127)); all x
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,8 +64,11 @@ __global__ __launch_bounds__(256) void check_division(int which, unsigned long l
     } else if (which == 3) {
       in = (a >= 1e-13f && a <= 1e37f) || a == __builtin_inff() || a != a;
       if (in) ok = agree(fp8q::div_short(1.0f, a), 1.0f / a);
-    } else {
+    } else if (which == 4) {
       ok = agree(fp8q::exp_fixed(x), exp_mul_form(x));
+    } else {
+      const uint32_t want = static_cast<uint32_t>(static_cast<int>(rintf(fminf(fmaxf(x, -127.0f), 127.0f)))) & 0xFFu;
+      ok = (fp8q::int8_code_bits(x) & 0xFFu) == want;
     }
     checked += in ? 1 : 0;
     bad += (in && !ok) ? 1 : 0;
@@ -76,10 +81,10 @@ __global__ __launch_bounds__(256) void check_division(int which, unsigned long l
 
 extern "C" {
 
-// which in 0..4 (see above). out: device array of two zeroed unsigned 64-bit counters that
+// which in 0..5 (see above). out: device array of two zeroed unsigned 64-bit counters that
 // receive (mismatches, inputs checked). Returns 0 or a HIP error code.
 int fp8q_check_division(int which, void* out, void* stream) {
-  if (which < 0 || which > 4 || out == nullptr) return static_cast<int>(hipErrorInvalidValue);
+  if (which < 0 || which > 5 || out == nullptr) return static_cast<int>(hipErrorInvalidValue);
   hipLaunchKernelGGL(check_division, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream), which,
                      static_cast<unsigned long long*>(out));
   return static_cast<int>(hipGetLastError());

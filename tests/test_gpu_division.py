@@ -6,7 +6,8 @@ computed in the kernels by shorter instruction sequences than the general IEEE d
 results must be the correctly rounded quotients, bit for bit, or the quantizer would no longer
 match the oracle. The bench library's fp8q_check_division runs each short form and the
 compiler's IEEE operation on all 2^32 bit patterns and counts disagreements; the exp case
-checks that scaling by v_ldexp_f32 equals the multiply by 2^n that the exp sequence states.
+checks that scaling by v_ldexp_f32 equals the multiply by 2^n that the exp sequence states,
+and the int8 case that the one-add encode gives the code of the clamp, rint and conversion.
 """
 import ctypes
 import os
@@ -30,6 +31,7 @@ EXPECTED_CHECKED = {
     2: 2 * ((1 << 31) - _EPS_BITS),
     3: 2 * ((_HI_BITS - _LO_BITS + 1) + 1 + _NAN_PER_SIGN),     # [1e-13, 1e37], inf, NaN
     4: 1 << 32,
+    5: 1 << 32,
 }
 
 
@@ -42,8 +44,9 @@ def _lib():
     return lib
 
 
-@pytest.mark.parametrize("which", [0, 1, 2, 3, 4],
-                         ids=["silu_quotient", "amax_div_448", "amax_div_127", "reciprocal", "exp_ldexp"])
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 4, 5],
+                         ids=["silu_quotient", "amax_div_448", "amax_div_127", "reciprocal", "exp_ldexp",
+                              "int8_code"])
 def test_short_form_matches_ieee_on_every_input(which):
     lib = _lib()
     out = torch.zeros(2, dtype=torch.int64, device="cuda")
@@ -58,5 +61,5 @@ def test_short_form_matches_ieee_on_every_input(which):
 def test_rejects_unknown_check():
     lib = _lib()
     out = torch.zeros(2, dtype=torch.int64, device="cuda")
-    assert lib.fp8q_check_division(5, out.data_ptr(), None) != 0
+    assert lib.fp8q_check_division(6, out.data_ptr(), None) != 0
     assert lib.fp8q_check_division(0, None, None) != 0
