@@ -353,6 +353,11 @@ def test_split_k_workspace_contract():
     assert f.fp8q_gemm_workspace_size(16, N, K, f.GEMM_BLOCK128) == 0
     assert f.fp8q_gemm_workspace_size(4096, N, K, f.GEMM_BLOCK128) == 0
     assert f.fp8q_gemm_workspace_size(M, N, 200, f.GEMM_BLOCK128) == 0
+    # K ranges of at least 4 blocks: the dense M=64 and M=128 splits (S=4 of 14 blocks, S=8 of
+    # 7) keep their workspace; the tiny problem (4 blocks) runs as one range without one
+    assert _split_ranges(64, 4096, 7168) == 4 and _split_ranges(128, 4096, 7168) == 8
+    assert f.fp8q_gemm_workspace_size(64, 256, 512, f.GEMM_BLOCK128) == 0
+    assert _split_ranges(17, 300, 1152) == 2
     w = synth.dense(M)
     a, sa = synth.gemm_activation(w)
     b, sb = synth.weights(w)
