@@ -151,8 +151,8 @@ __device__ __forceinline__ void widen(const Raw16<DT>& r, float (&v)[16]) {
 // fp32 (exp_fixed, then an IEEE add, a correctly rounded division and a multiply). The
 // division takes the short form unless some lane of the wave holds a gate below -87, where
 // 1 + exp(-g) exceeds 2^126 and its reciprocal is subnormal: that wave takes the general
-// division for its 16 values. Both forms give the same correctly rounded quotient.
-// Must be called by the whole wave (wave-uniform control flow).
+// division for its 16 values. The choice is a ballot over the active lanes; both forms give
+// the same correctly rounded quotient, so it never changes a result.
 __device__ __forceinline__ void silu_mul16(float (&v)[16], const float (&u)[16]) {
   float d[16];
   bool low = false;
